@@ -1,0 +1,130 @@
+/*
+ * ssm_scan.h -- C ABI of the MI355X (gfx950) selective state-space (S6) forward scan.
+ *
+ * The operation (per channel d of batch b, state n, time t; all arithmetic fp32):
+ *   delta_t = softplus(delta_raw_t + delta_bias)      (or delta_raw_t + delta_bias when the
+ *                                                      softplus flag is 0)
+ *       -- the step size is an activation of a parameter plus an input-dependent projection
+ *          (page "【論文要約】Mamba: Linear-Time Sequence Modeling with Selective State
+ *          Spaces【自分用メモ】", Algorithm 2 as summarised there; page "NL-345, Mamba: ...",
+ *          §1 "Selection Mechanism").
+ *   dA_tn   = exp(delta_t * A_n),  dB_tn = delta_t * B_tn
+ *       -- the discretisation step (page "NL-345", §2 "Discretization"; A_bar as in the memo
+ *          page's "数式解説" item 3; B_bar = delta * B is the simple rule the pages allow).
+ *   h_tn    = dA_tn * h_(t-1)n + dB_tn * x_t,          h_(-1) = 0
+ *       -- the linear recurrence, eq. (2) (page "NL-345", §2 "Computation"), one diagonal SSM per
+ *          channel (same page, §2 "Structure and Dimensions").
+ *   y_t     = (sum_n C_tn h_tn + D * x_t) * silu(z_t)  (the gate only when z is given)
+ *       -- readout, skip term and the SiLU gate of the Mamba block (memo page, "Mambaアーキテク
+ *          チャ").
+ * The state h is never written to memory (memo page, "ハードウェアを考慮した効率的なアルゴリズム").
+ *
+ * Layouts. Every tensor is indexed with element strides given in the descriptor; the time
+ * (L) stride is always 1:
+ *   x, z, y     (batch, dim, L)                        io dtype
+ *   delta       (batch, dim, L)   A_DIAG mode          io dtype
+ *               (batch, nheads, L) A_HEAD mode (nheads = dim / headdim)
+ *   A           (dim, dstate) fp32 contiguous, A_DIAG mode; (nheads,) fp32 in A_HEAD mode
+ *   B, C        (batch, ngroups, dstate, L)            io dtype; channel d reads group
+ *                                                       d / (dim / ngroups)
+ *   D           (dim,) fp32, nullable (treated as 0)
+ *   delta_bias  (dim,) fp32 in A_DIAG mode, (nheads,) in A_HEAD mode; nullable (treated as 0)
+ *   z           nullable: no gate
+ * Channel d belongs to head d / headdim (A_HEAD mode).
+ *
+ * Ownership and execution: the caller owns every buffer (device memory) and the stream. The
+ * library allocates nothing and keeps no mutable global state; calls are thread-safe. Work is
+ * enqueued asynchronously on `stream` (a hipStream_t, NULL = the default stream). Device faults
+ * surface at the caller's next synchronisation.
+ *
+ * Errors: every entry point returns SSM_OK (0) or a negative ssm_status. Argument checks run on
+ * the host before anything is enqueued; on an error nothing is launched and no buffer is touched.
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_SCAN_ABI_VERSION 1
+
+typedef enum {
+  SSM_OK = 0,
+  SSM_ERR_NULL_ARG = -1,       /* a required pointer (desc, x, delta, A, B, C, y) is NULL */
+  SSM_ERR_BAD_SHAPE = -2,      /* a size < 0, dim/dstate/ngroups/headdim < 1, dim % ngroups,
+                                  dim % headdim, dstate > SSM_MAX_DSTATE (128), or sizes that overflow */
+  SSM_ERR_BAD_DTYPE = -3,      /* io_dtype or a_mode not one of the enums below */
+  SSM_ERR_BAD_STRIDE = -4,     /* a negative stride, or strides that make rows overlap */
+  SSM_ERR_MISALIGNED = -5,     /* a pointer not aligned to its element size */
+  SSM_ERR_ALIAS = -6,          /* y overlaps an input */
+  SSM_ERR_WORKSPACE = -7,      /* workspace NULL or smaller than the size query returns */
+  SSM_ERR_HIP = -8,            /* the HIP runtime reported an error while enqueueing */
+  SSM_ERR_UNSUPPORTED = -9     /* valid arguments outside what this build implements */
+} ssm_status;
+
+typedef enum { SSM_DTYPE_F32 = 0, SSM_DTYPE_BF16 = 1 } ssm_dtype;
+
+typedef enum {
+  SSM_A_DIAG = 0, /* A is (dim, dstate): a diagonal A per channel, delta per channel */
+  SSM_A_HEAD = 1  /* A is one scalar per head; delta and delta_bias per head */
+} ssm_a_mode;
+
+#define SSM_MAX_DSTATE 128
+
+typedef struct ssm_scan_desc {
+  int64_t batch;    /* >= 0 */
+  int64_t dim;      /* channels (d_inner), >= 1 */
+  int64_t seqlen;   /* L, >= 0 */
+  int64_t dstate;   /* N, 1..SSM_MAX_DSTATE (128) */
+  int64_t ngroups;  /* B/C groups, >= 1, divides dim */
+  int64_t headdim;  /* channels per head, >= 1, divides dim; 1 in A_DIAG mode */
+  int32_t io_dtype; /* ssm_dtype of x, delta, B, C, z and y */
+  int32_t a_mode;   /* ssm_a_mode */
+  /* element strides (the L stride is 1) */
+  int64_t x_stride_batch, x_stride_dim;
+  int64_t delta_stride_batch, delta_stride_dim; /* dim index: channel (DIAG) or head (HEAD) */
+  int64_t B_stride_batch, B_stride_group, B_stride_state;
+  int64_t C_stride_batch, C_stride_group, C_stride_state;
+  int64_t z_stride_batch, z_stride_dim;
+  int64_t y_stride_batch, y_stride_dim;
+} ssm_scan_desc;
+
+/* Fills `desc` with the contiguous layout of the given sizes (strides as listed above, L
+ * innermost). Returns SSM_ERR_NULL_ARG for a NULL desc, else SSM_OK; sizes are checked by the
+ * calls that use the descriptor. */
+int ssm_scan_desc_init_contiguous(ssm_scan_desc* desc, int64_t batch, int64_t dim, int64_t seqlen,
+                                  int64_t dstate, int64_t ngroups, int64_t headdim,
+                                  int32_t io_dtype, int32_t a_mode);
+
+/* Bytes of device workspace that ssm_selective_scan_fwd needs for `desc` (0 when the sequence
+ * is processed in one segment). The value depends only on the descriptor. */
+int ssm_selective_scan_workspace_size(const ssm_scan_desc* desc, size_t* bytes);
+
+/* The selective-scan forward pass described at the top of this header.
+ *   x, delta, B, C, z, y : device pointers of the io dtype (z may be NULL)
+ *   A, D, delta_bias     : device pointers, fp32 (D and delta_bias may be NULL)
+ *   delta_softplus       : nonzero applies softplus to delta_raw + delta_bias
+ *   workspace            : device scratch of at least the queried size (may be NULL when the
+ *                          query returns 0); its contents on entry do not matter
+ *   stream               : hipStream_t to enqueue on
+ * y must not overlap any input. */
+int ssm_selective_scan_fwd(const ssm_scan_desc* desc, const void* x, const void* delta,
+                           const float* A, const void* B, const void* C, const float* D,
+                           const void* z, const float* delta_bias, int32_t delta_softplus,
+                           void* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* ssm_status_string(int status);
+
+/* SSM_SCAN_ABI_VERSION of the built library. */
+int ssm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_SCAN_H */

@@ -1,0 +1,205 @@
+"""Python binding of the MI355X selective-scan library (``lib/libssm_scan.so``).
+
+Argument marshalling only: every step of the scan runs in the library's HIP kernels. PyTorch
+provides device memory and the current stream. There is no fallback: if the library is not
+built, every entry point raises.
+
+The C ABI is declared in ``include/ssm_scan.h``; the names here mirror it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libssm_scan.so")
+
+SSM_OK = 0
+SSM_DTYPE_F32, SSM_DTYPE_BF16 = 0, 1
+SSM_A_DIAG, SSM_A_HEAD = 0, 1
+SSM_MAX_DSTATE = 128
+
+STATUS_NAMES = {
+    0: "SSM_OK", -1: "SSM_ERR_NULL_ARG", -2: "SSM_ERR_BAD_SHAPE", -3: "SSM_ERR_BAD_DTYPE",
+    -4: "SSM_ERR_BAD_STRIDE", -5: "SSM_ERR_MISALIGNED", -6: "SSM_ERR_ALIAS",
+    -7: "SSM_ERR_WORKSPACE", -8: "SSM_ERR_HIP", -9: "SSM_ERR_UNSUPPORTED",
+}
+
+
+class ScanDesc(ctypes.Structure):
+    """Mirror of ``ssm_scan_desc``."""
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("dim", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+        ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64), ("headdim", ctypes.c_int64),
+        ("io_dtype", ctypes.c_int32), ("a_mode", ctypes.c_int32),
+        ("x_stride_batch", ctypes.c_int64), ("x_stride_dim", ctypes.c_int64),
+        ("delta_stride_batch", ctypes.c_int64), ("delta_stride_dim", ctypes.c_int64),
+        ("B_stride_batch", ctypes.c_int64), ("B_stride_group", ctypes.c_int64),
+        ("B_stride_state", ctypes.c_int64),
+        ("C_stride_batch", ctypes.c_int64), ("C_stride_group", ctypes.c_int64),
+        ("C_stride_state", ctypes.c_int64),
+        ("z_stride_batch", ctypes.c_int64), ("z_stride_dim", ctypes.c_int64),
+        ("y_stride_batch", ctypes.c_int64), ("y_stride_dim", ctypes.c_int64),
+    ]
+
+
+class ScanError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS_NAMES.get(status, status)} ({status_string(status)})")
+
+
+_lib = None
+
+
+def lib():
+    """ctypes handle of the built library (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        h = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        dp = ctypes.POINTER(ScanDesc)
+        h.ssm_scan_desc_init_contiguous.argtypes = [dp, i64, i64, i64, i64, i64, i64, i32, i32]
+        h.ssm_scan_desc_init_contiguous.restype = ctypes.c_int
+        h.ssm_selective_scan_workspace_size.argtypes = [dp, ctypes.POINTER(sz)]
+        h.ssm_selective_scan_workspace_size.restype = ctypes.c_int
+        h.ssm_selective_scan_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
+        h.ssm_selective_scan_fwd.restype = ctypes.c_int
+        h.ssm_status_string.argtypes = [ctypes.c_int]
+        h.ssm_status_string.restype = ctypes.c_char_p
+        h.ssm_abi_version.argtypes = []
+        h.ssm_abi_version.restype = ctypes.c_int
+        _lib = h
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().ssm_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(lib().ssm_abi_version())
+
+
+def desc_contiguous(batch, dim, seqlen, dstate, ngroups=1, headdim=1, io_dtype=SSM_DTYPE_BF16,
+                    a_mode=SSM_A_DIAG) -> ScanDesc:
+    d = ScanDesc()
+    rc = lib().ssm_scan_desc_init_contiguous(ctypes.byref(d), batch, dim, seqlen, dstate, ngroups,
+                                             headdim, io_dtype, a_mode)
+    if rc != SSM_OK:
+        raise ScanError(rc, "ssm_scan_desc_init_contiguous")
+    return d
+
+
+def workspace_size(desc: ScanDesc) -> int:
+    out = ctypes.c_size_t(0)
+    rc = lib().ssm_selective_scan_workspace_size(ctypes.byref(desc), ctypes.byref(out))
+    if rc != SSM_OK:
+        raise ScanError(rc, "ssm_selective_scan_workspace_size")
+    return int(out.value)
+
+
+def fwd_raw(desc: ScanDesc, x, delta, A, B, C, D, z, delta_bias, delta_softplus: bool, y,
+            workspace, workspace_bytes: int, stream) -> int:
+    """Direct call of ``ssm_selective_scan_fwd`` with integer device addresses (or None).
+    Returns the status code without raising."""
+    return int(lib().ssm_selective_scan_fwd(ctypes.byref(desc), x, delta, A, B, C, D, z,
+                                            delta_bias, int(bool(delta_softplus)), y, workspace,
+                                            int(workspace_bytes), stream))
+
+
+# ---------------------------------------------------------------------------------------------
+# torch front end (device memory and streams only)
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def describe(x, delta, A, B, C, z=None, y=None) -> ScanDesc:
+    """Descriptor of torch tensors: x (batch, dim, L), delta (batch, dim | nheads, L),
+    A (dim, N) or (nheads,), B/C (batch, ngroups, N, L), z and y like x."""
+    import torch
+    if x.dtype == torch.bfloat16:
+        io = SSM_DTYPE_BF16
+    elif x.dtype == torch.float32:
+        io = SSM_DTYPE_F32
+    else:
+        raise TypeError(f"x must be bfloat16 or float32, got {x.dtype}")
+    for name, t in (("delta", delta), ("B", B), ("C", C), ("z", z), ("y", y)):
+        if t is not None and t.dtype != x.dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {x.dtype}")
+    if A.dtype != torch.float32:
+        raise TypeError("A must be float32")
+    if x.dim() != 3 or delta.dim() != 3 or B.dim() != 4 or C.dim() != 4:
+        raise ValueError("expected x/delta (batch, rows, L) and B/C (batch, groups, N, L)")
+    batch, dim, L = x.shape
+    ngroups, N = B.shape[1], B.shape[2]
+    if A.dim() == 1:
+        a_mode = SSM_A_HEAD
+        nheads = A.shape[0]
+        if nheads == 0 or dim % nheads:
+            raise ValueError("A (nheads,) must divide dim")
+        headdim = dim // nheads
+    elif A.dim() == 2:
+        a_mode, headdim = SSM_A_DIAG, 1
+        if tuple(A.shape) != (dim, N):
+            raise ValueError(f"A must be (dim, N) = {(dim, N)}, got {tuple(A.shape)}")
+    else:
+        raise ValueError("A must be (dim, N) or (nheads,)")
+    rows = dim // headdim
+    if tuple(delta.shape) != (batch, rows, L):
+        raise ValueError(f"delta must be {(batch, rows, L)}, got {tuple(delta.shape)}")
+    if tuple(B.shape) != (batch, ngroups, N, L) or tuple(C.shape) != (batch, ngroups, N, L):
+        raise ValueError("B and C must both be (batch, ngroups, N, L)")
+    for name, t in (("x", x), ("delta", delta), ("B", B), ("C", C), ("z", z), ("y", y)):
+        if t is not None and t.shape[-1] > 1 and t.stride(-1) != 1:
+            raise ValueError(f"{name} must have unit stride along L")
+    if not A.is_contiguous():
+        raise ValueError("A must be contiguous")
+    d = ScanDesc()
+    d.batch, d.dim, d.seqlen, d.dstate, d.ngroups, d.headdim = batch, dim, L, N, ngroups, headdim
+    d.io_dtype, d.a_mode = io, a_mode
+    d.x_stride_batch, d.x_stride_dim = x.stride(0), x.stride(1)
+    d.delta_stride_batch, d.delta_stride_dim = delta.stride(0), delta.stride(1)
+    d.B_stride_batch, d.B_stride_group, d.B_stride_state = B.stride(0), B.stride(1), B.stride(2)
+    d.C_stride_batch, d.C_stride_group, d.C_stride_state = C.stride(0), C.stride(1), C.stride(2)
+    if z is not None:
+        if tuple(z.shape) != (batch, dim, L):
+            raise ValueError("z must be shaped like x")
+        d.z_stride_batch, d.z_stride_dim = z.stride(0), z.stride(1)
+    if y is not None:
+        if tuple(y.shape) != (batch, dim, L):
+            raise ValueError("y must be shaped like x")
+        d.y_stride_batch, d.y_stride_dim = y.stride(0), y.stride(1)
+    return d
+
+
+def selective_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                       *, out=None, workspace=None, stream=None):
+    """y = selective scan of torch device tensors (see ``include/ssm_scan.h``).
+
+    ``out`` receives y if given (shape and dtype of x). ``workspace`` may be a uint8 device
+    tensor of at least ``workspace_size`` bytes; otherwise one is allocated. ``stream`` defaults
+    to the current torch stream. Raises ScanError with the library's status on failure.
+    """
+    import torch
+    y = out if out is not None else torch.empty_like(x, memory_format=torch.contiguous_format)
+    desc = describe(x, delta, A, B, C, z, y)
+    for name, t in (("D", D), ("delta_bias", delta_bias)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise TypeError(f"{name} must be a contiguous float32 tensor")
+    need = workspace_size(desc)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    sp = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    rc = fwd_raw(desc, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                 _ptr(delta_bias), delta_softplus, _ptr(y), _ptr(workspace) if need else None,
+                 need, sp)
+    if rc != SSM_OK:
+        raise ScanError(rc, "ssm_selective_scan_fwd")
+    return y

@@ -1,0 +1,258 @@
+// C ABI of the selective-scan library: argument validation, segment planning and dispatch.
+// Every check runs on the host before anything is enqueued; a failing call launches nothing.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "scan_internal.h"
+#include "ssm_scan.h"
+
+namespace ssm {
+hipError_t launch_scan_fwd(const ScanParams& p, bool bf16, bool head, hipStream_t stream);
+int time_tile();
+}  // namespace ssm
+
+namespace {
+
+constexpr int64_t kTargetWorkgroups = 512;    // about two resident workgroups per CU (256 CUs)
+constexpr int64_t kMinSegmentTiles = 8;       // shortest segment worth a summary pass, in tiles
+constexpr int64_t kMaxSegments = 65535;       // grid.y limit
+
+struct Plan {
+  int64_t nseg;
+  int64_t seg_len;
+};
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+// Largest element offset + 1 of a (n0, n1, L) tensor with strides (s0, s1, 1); -1 on overflow.
+int64_t extent3(int64_t n0, int64_t n1, int64_t L, int64_t s0, int64_t s1) {
+  if (n0 == 0 || n1 == 0 || L == 0) return 0;
+  int64_t a, b2;
+  if (!mul_ok(n0 - 1, s0, &a) || !mul_ok(n1 - 1, s1, &b2)) return -1;
+  int64_t e;
+  if (__builtin_add_overflow(a, b2, &e) || __builtin_add_overflow(e, L, &e)) return -1;
+  return e;
+}
+
+int64_t extent4(int64_t n0, int64_t n1, int64_t n2, int64_t L, int64_t s0, int64_t s1, int64_t s2) {
+  if (n0 == 0 || n1 == 0 || n2 == 0 || L == 0) return 0;
+  int64_t a, b2, c;
+  if (!mul_ok(n0 - 1, s0, &a) || !mul_ok(n1 - 1, s1, &b2) || !mul_ok(n2 - 1, s2, &c)) return -1;
+  int64_t e;
+  if (__builtin_add_overflow(a, b2, &e) || __builtin_add_overflow(e, c, &e) ||
+      __builtin_add_overflow(e, L, &e))
+    return -1;
+  return e;
+}
+
+int check_desc(const ssm_scan_desc* d) {
+  if (!d) return SSM_ERR_NULL_ARG;
+  if (d->io_dtype != SSM_DTYPE_F32 && d->io_dtype != SSM_DTYPE_BF16) return SSM_ERR_BAD_DTYPE;
+  if (d->a_mode != SSM_A_DIAG && d->a_mode != SSM_A_HEAD) return SSM_ERR_BAD_DTYPE;
+  if (d->batch < 0 || d->seqlen < 0 || d->dim < 1 || d->dstate < 1 || d->dstate > SSM_MAX_DSTATE ||
+      d->ngroups < 1 || d->headdim < 1)
+    return SSM_ERR_BAD_SHAPE;
+  if (d->dim % d->ngroups || d->dim % d->headdim) return SSM_ERR_BAD_SHAPE;
+  if (d->a_mode == SSM_A_DIAG && d->headdim != 1) return SSM_ERR_BAD_SHAPE;
+  int64_t t;
+  if (!mul_ok(d->batch, d->dim, &t) || !mul_ok(t, d->seqlen, &t) || !mul_ok(t, d->dstate, &t))
+    return SSM_ERR_BAD_SHAPE;
+  const int64_t strides[] = {d->x_stride_batch, d->x_stride_dim, d->delta_stride_batch,
+                             d->delta_stride_dim, d->B_stride_batch, d->B_stride_group,
+                             d->B_stride_state, d->C_stride_batch, d->C_stride_group,
+                             d->C_stride_state, d->z_stride_batch, d->z_stride_dim,
+                             d->y_stride_batch, d->y_stride_dim};
+  for (int64_t s : strides)
+    if (s < 0) return SSM_ERR_BAD_STRIDE;
+  // y rows must be disjoint (they are written)
+  if (d->dim > 1 && d->seqlen > 0 && d->y_stride_dim < d->seqlen) return SSM_ERR_BAD_STRIDE;
+  if (d->batch > 1 && d->seqlen > 0) {
+    int64_t last;
+    if (!mul_ok(d->dim - 1, d->y_stride_dim, &last) || __builtin_add_overflow(last, d->seqlen, &last))
+      return SSM_ERR_BAD_STRIDE;
+    if (d->y_stride_batch < last) return SSM_ERR_BAD_STRIDE;
+  }
+  const int64_t drows = d->a_mode == SSM_A_HEAD ? d->dim / d->headdim : d->dim;
+  if (extent3(d->batch, d->dim, d->seqlen, d->x_stride_batch, d->x_stride_dim) < 0 ||
+      extent3(d->batch, drows, d->seqlen, d->delta_stride_batch, d->delta_stride_dim) < 0 ||
+      extent3(d->batch, d->dim, d->seqlen, d->z_stride_batch, d->z_stride_dim) < 0 ||
+      extent3(d->batch, d->dim, d->seqlen, d->y_stride_batch, d->y_stride_dim) < 0 ||
+      extent4(d->batch, d->ngroups, d->dstate, d->seqlen, d->B_stride_batch, d->B_stride_group,
+              d->B_stride_state) < 0 ||
+      extent4(d->batch, d->ngroups, d->dstate, d->seqlen, d->C_stride_batch, d->C_stride_group,
+              d->C_stride_state) < 0)
+    return SSM_ERR_BAD_SHAPE;
+  return SSM_OK;
+}
+
+Plan plan_segments(const ssm_scan_desc* d) {
+  const int64_t tile = ssm::time_tile();
+  const int64_t groups = d->batch * ((d->dim + ssm::kChannelsPerGroup - 1) / ssm::kChannelsPerGroup);
+  Plan p{1, d->seqlen > 0 ? d->seqlen : 1};
+  if (groups == 0 || d->seqlen == 0) return p;
+  if (groups * 4 >= kTargetWorkgroups * 3) return p;  // enough channel groups: one pass
+  int64_t want = (kTargetWorkgroups + groups - 1) / groups;
+  const int64_t tiles = (d->seqlen + tile - 1) / tile;
+  const int64_t max_by_len = tiles / kMinSegmentTiles;
+  if (want > max_by_len) want = max_by_len;
+  if (want > kMaxSegments) want = kMaxSegments;
+  if (want <= 1) return p;
+  const int64_t seg_tiles = (tiles + want - 1) / want;
+  p.seg_len = seg_tiles * tile;
+  p.nseg = (d->seqlen + p.seg_len - 1) / p.seg_len;
+  if (p.nseg <= 1) p = Plan{1, d->seqlen};
+  return p;
+}
+
+size_t workspace_bytes_for(const ssm_scan_desc* d, const Plan& p) {
+  if (p.nseg <= 1) return 0;
+  // hend (batch, dim, nseg, N) fp32, then dsum (batch, dim, nseg) fp32
+  return (size_t)d->batch * (size_t)d->dim * (size_t)p.nseg * (size_t)(d->dstate + 1) * sizeof(float);
+}
+
+bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
+  if (!a || !b || abytes == 0 || bbytes == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + bbytes && b0 < a0 + abytes;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int ssm_abi_version(void) { return SSM_SCAN_ABI_VERSION; }
+
+const char* ssm_status_string(int status) {
+  switch (status) {
+    case SSM_OK: return "ok";
+    case SSM_ERR_NULL_ARG: return "a required pointer argument is NULL";
+    case SSM_ERR_BAD_SHAPE: return "invalid sizes (negative, zero where >= 1 is needed, indivisible dim, dstate > 128, or overflow)";
+    case SSM_ERR_BAD_DTYPE: return "unknown io dtype or A mode";
+    case SSM_ERR_BAD_STRIDE: return "invalid strides (negative, or overlapping output rows)";
+    case SSM_ERR_MISALIGNED: return "a pointer is not aligned to its element size";
+    case SSM_ERR_ALIAS: return "the output overlaps an input";
+    case SSM_ERR_WORKSPACE: return "workspace missing or smaller than the queried size";
+    case SSM_ERR_HIP: return "the HIP runtime reported an error";
+    case SSM_ERR_UNSUPPORTED: return "valid arguments outside what this build implements";
+    default: return "unknown status";
+  }
+}
+
+int ssm_scan_desc_init_contiguous(ssm_scan_desc* d, int64_t batch, int64_t dim, int64_t seqlen,
+                                  int64_t dstate, int64_t ngroups, int64_t headdim,
+                                  int32_t io_dtype, int32_t a_mode) {
+  if (!d) return SSM_ERR_NULL_ARG;
+  memset(d, 0, sizeof(*d));
+  d->batch = batch; d->dim = dim; d->seqlen = seqlen; d->dstate = dstate;
+  d->ngroups = ngroups; d->headdim = headdim; d->io_dtype = io_dtype; d->a_mode = a_mode;
+  const int64_t rows = (a_mode == SSM_A_HEAD && headdim > 0) ? dim / headdim : dim;
+  d->x_stride_dim = seqlen; d->x_stride_batch = dim * seqlen;
+  d->delta_stride_dim = seqlen; d->delta_stride_batch = rows * seqlen;
+  d->B_stride_state = seqlen; d->B_stride_group = dstate * seqlen; d->B_stride_batch = ngroups * dstate * seqlen;
+  d->C_stride_state = d->B_stride_state; d->C_stride_group = d->B_stride_group; d->C_stride_batch = d->B_stride_batch;
+  d->z_stride_dim = seqlen; d->z_stride_batch = dim * seqlen;
+  d->y_stride_dim = seqlen; d->y_stride_batch = dim * seqlen;
+  return SSM_OK;
+}
+
+int ssm_selective_scan_workspace_size(const ssm_scan_desc* desc, size_t* bytes) {
+  if (!bytes) return SSM_ERR_NULL_ARG;
+  const int rc = check_desc(desc);
+  if (rc != SSM_OK) return rc;
+  *bytes = workspace_bytes_for(desc, plan_segments(desc));
+  return SSM_OK;
+}
+
+int ssm_selective_scan_fwd(const ssm_scan_desc* desc, const void* x, const void* delta,
+                           const float* A, const void* B, const void* C, const float* D,
+                           const void* z, const float* delta_bias, int32_t delta_softplus,
+                           void* y, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_desc(desc);
+  if (rc != SSM_OK) return rc;
+  const ssm_scan_desc& d = *desc;
+  if (d.batch == 0 || d.seqlen == 0) return SSM_OK;  // nothing to compute or write
+  if (!x || !delta || !A || !B || !C || !y) return SSM_ERR_NULL_ARG;
+
+  const bool bf16 = d.io_dtype == SSM_DTYPE_BF16;
+  const bool head = d.a_mode == SSM_A_HEAD;
+  const size_t es = bf16 ? 2 : 4;
+  const int64_t nheads = d.dim / d.headdim;
+  const int64_t drows = head ? nheads : d.dim;
+  const void* io_ptrs[] = {x, delta, B, C, z, y};
+  for (const void* p : io_ptrs)
+    if (p && !aligned(p, es)) return SSM_ERR_MISALIGNED;
+  const void* f32_ptrs[] = {A, D, delta_bias, workspace};
+  for (const void* p : f32_ptrs)
+    if (p && !aligned(p, 4)) return SSM_ERR_MISALIGNED;
+
+  // y must not overlap any input
+  const size_t y_bytes = (size_t)extent3(d.batch, d.dim, d.seqlen, d.y_stride_batch, d.y_stride_dim) * es;
+  const size_t in_bytes[] = {
+      (size_t)extent3(d.batch, d.dim, d.seqlen, d.x_stride_batch, d.x_stride_dim) * es,
+      (size_t)extent3(d.batch, drows, d.seqlen, d.delta_stride_batch, d.delta_stride_dim) * es,
+      (size_t)extent4(d.batch, d.ngroups, d.dstate, d.seqlen, d.B_stride_batch, d.B_stride_group, d.B_stride_state) * es,
+      (size_t)extent4(d.batch, d.ngroups, d.dstate, d.seqlen, d.C_stride_batch, d.C_stride_group, d.C_stride_state) * es,
+      z ? (size_t)extent3(d.batch, d.dim, d.seqlen, d.z_stride_batch, d.z_stride_dim) * es : 0,
+      (size_t)(head ? nheads : d.dim * d.dstate) * 4,
+      D ? (size_t)d.dim * 4 : 0,
+      delta_bias ? (size_t)drows * 4 : 0};
+  const void* in_ptrs[] = {x, delta, B, C, z, A, D, delta_bias};
+  for (int i = 0; i < 8; ++i)
+    if (overlaps(y, y_bytes, in_ptrs[i], in_bytes[i])) return SSM_ERR_ALIAS;
+
+  // B and C must be uniform over each 64-channel workgroup
+  const int64_t ch_per_group = d.dim / d.ngroups;
+  if (d.ngroups > 1 && ch_per_group % ssm::kChannelsPerGroup != 0) return SSM_ERR_UNSUPPORTED;
+
+  const Plan plan = plan_segments(desc);
+  const size_t need = workspace_bytes_for(desc, plan);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SSM_ERR_WORKSPACE;
+  if (need > 0 && overlaps(workspace, need, y, y_bytes)) return SSM_ERR_ALIAS;
+
+  ssm::ScanParams p;
+  memset(&p, 0, sizeof(p));
+  p.x = x; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.delta_bias = delta_bias;
+  p.y = y;
+  p.batch = d.batch; p.dim = d.dim; p.L = d.seqlen; p.N = d.dstate; p.ngroups = d.ngroups;
+  p.headdim = d.headdim;
+  p.x_sb = d.x_stride_batch; p.x_sd = d.x_stride_dim;
+  p.dl_sb = d.delta_stride_batch; p.dl_sd = d.delta_stride_dim;
+  p.B_sb = d.B_stride_batch; p.B_sg = d.B_stride_group; p.B_sn = d.B_stride_state;
+  p.C_sb = d.C_stride_batch; p.C_sg = d.C_stride_group; p.C_sn = d.C_stride_state;
+  p.z_sb = d.z_stride_batch; p.z_sd = d.z_stride_dim;
+  p.y_sb = d.y_stride_batch; p.y_sd = d.y_stride_dim;
+  p.groups_per_batch = (d.dim + ssm::kChannelsPerGroup - 1) / ssm::kChannelsPerGroup;
+  p.seg_len = plan.seg_len;
+  p.nseg = (int32_t)plan.nseg;
+  p.softplus = delta_softplus ? 1 : 0;
+  if (plan.nseg > 1) {
+    p.hend = static_cast<float*>(workspace);
+    p.dsum = p.hend + (size_t)d.batch * d.dim * plan.nseg * d.dstate;
+  }
+  // 16-byte vector access of x/delta/z/y rows: 16-byte aligned bases, strides multiple of 16 B
+  const int64_t vec = 16 / (int64_t)es;
+  bool vec_ok = true;
+  const void* vptrs[] = {x, delta, z, y};
+  for (const void* q : vptrs)
+    if (q && !aligned(q, 16)) vec_ok = false;
+  const int64_t vstrides[] = {d.x_stride_batch, d.x_stride_dim, d.delta_stride_batch,
+                              d.delta_stride_dim, z ? d.z_stride_batch : 0, z ? d.z_stride_dim : 0,
+                              d.y_stride_batch, d.y_stride_dim};
+  for (int64_t s : vstrides)
+    if (s % vec) vec_ok = false;
+  p.vec_io = vec_ok ? 1 : 0;
+  bool bc_vec = aligned(B, 16) && aligned(C, 16);
+  const int64_t bstrides[] = {d.B_stride_batch, d.B_stride_group, d.B_stride_state,
+                              d.C_stride_batch, d.C_stride_group, d.C_stride_state};
+  for (int64_t s : bstrides)
+    if (s % vec) bc_vec = false;
+  p.bc_vec = bc_vec ? 1 : 0;
+
+  const hipError_t e = ssm::launch_scan_fwd(p, bf16, head, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+"""Shared helpers of the GPU tests: generated inputs to device tensors, HIP-path calls, and the
+oracle on the same inputs."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import ssmgen
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def to_torch(arr: np.ndarray, io_bits: bool, device):
+    """numpy input (bf16 bit patterns as uint16) -> torch tensor on device, same bits."""
+    import torch
+    if arr.dtype == np.uint16:
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr))
+    return t.to(device)
+
+
+def device_inputs(inputs: dict, device="cuda"):
+    return {k: to_torch(v, v.dtype == np.uint16, device) for k, v in inputs.items()}
+
+
+def run_hip(dev: dict, softplus=True, out=None):
+    import selective_state_space_24_amd as ssm
+    return ssm.selective_scan_fwd(dev["x"], dev["delta"], dev["A"], dev["B"], dev["C"],
+                                  dev.get("D"), dev.get("z"), dev.get("delta_bias"), softplus,
+                                  out=out)
+
+
+def y_to_f64(y) -> np.ndarray:
+    import torch
+    return y.float().cpu().numpy().astype(np.float64) if y.dtype == torch.bfloat16 else \
+        y.cpu().numpy().astype(np.float64)
+
+
+def oracle_of(cfg: ssmgen.ScanConfig, inputs: dict) -> np.ndarray:
+    return oracle.scan_inputs(inputs, cfg)
+
+
+def channel_oracle(cfg: ssmgen.ScanConfig, b: int, d: int) -> np.ndarray:
+    """fp64 oracle of one channel (b, d), inputs regenerated from the streams."""
+    ch = ssmgen.make_channel(cfg, b, d)
+    head = cfg.a_mode == "head"
+    return oracle.selective_scan(ch["x"], ch["delta"], ch["A"], ch["B"], ch["C"], ch.get("D"),
+                                 ch.get("z"), ch.get("delta_bias"), cfg.softplus, headdim=1,
+                                 head_mode=head, nthreads=1)[0, 0]
+
+
+def sample_channels(cfg: ssmgen.ScanConfig, count: int, seed: int = 0):
+    """Channels spread over the tensor, always including the first and the last."""
+    rng = np.random.default_rng(seed)
+    picks = {(0, 0), (cfg.batch - 1, cfg.dim - 1)}
+    while len(picks) < min(count, cfg.batch * cfg.dim):
+        picks.add((int(rng.integers(cfg.batch)), int(rng.integers(cfg.dim))))
+    return sorted(picks)

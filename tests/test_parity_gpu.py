@@ -1,0 +1,191 @@
+"""HIP path vs the fp64 oracle on the same seeded inputs (needs an MI355X).
+
+Tolerance: max_i |y_i - yref_i| / max(|yref_i|, rms(yref)) <= 1e-4 with fp32 I/O and <= 2e-2
+with bf16 I/O (fp32 state and arithmetic in both cases).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import ssmgen
+from scan_cases import (TOL, channel_oracle, device_inputs, oracle_of, run_hip, sample_channels,
+                        y_to_f64)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import selective_state_space_24_amd as ssm
+    ssm.lib()  # fails loudly if the HIP library is not built
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _check(cfg, inputs, y, tol=None):
+    yref = oracle_of(cfg, inputs)
+    err = oracle.rel_err(y_to_f64(y), yref)
+    assert np.isfinite(y_to_f64(y)).all()
+    assert err <= (tol or TOL[cfg.io]), f"{cfg.name}: rel err {err:.3e}"
+    return err
+
+
+@pytest.mark.parametrize("ci", [0, 1])
+def test_config_full_parity(ci):
+    cfg = ssmgen.CONFIGS[ci]
+    _say(f"[parity] config {ci} {cfg.name} (full oracle)")
+    inputs = ssmgen.make_inputs(cfg)
+    y = run_hip(device_inputs(inputs))
+    torch.cuda.synchronize()
+    err = _check(cfg, inputs, y)
+    _say(f"[parity] config {ci} rel err {err:.3e}")
+
+
+@pytest.mark.parametrize("ci,nsamp", [(2, 24), (4, 12), (3, 6)])
+def test_config_sampled_parity(ci, nsamp):
+    """Full-size run in the bench's launch configuration; sampled channels against the oracle
+    computed channel by channel from regenerated inputs."""
+    cfg = ssmgen.CONFIGS[ci]
+    _say(f"[parity] config {ci} {cfg.name}: generating inputs")
+    dev = {}
+    for name in cfg.shapes():
+        dev.update(device_inputs({name: ssmgen.make_tensor(cfg, name)}))
+    _say(f"[parity] config {ci}: running")
+    y = run_hip(dev)
+    torch.cuda.synchronize()
+    del dev
+    worst = 0.0
+    for b, d in sample_channels(cfg, nsamp, seed=ci):
+        yref = channel_oracle(cfg, b, d)
+        yg = y[b, d].float().cpu().numpy().astype(np.float64)
+        err = oracle.rel_err(yg, yref)
+        worst = max(worst, err)
+        assert np.isfinite(yg).all()
+        assert err <= TOL[cfg.io], f"config {ci} channel ({b},{d}): rel err {err:.3e}"
+    _say(f"[parity] config {ci}: worst sampled rel err {worst:.3e}")
+    del y
+    torch.cuda.empty_cache()
+
+
+EDGE = [
+    # batch, dim, L, N, headdim, a_mode, io, gate, softplus, D, bias, ngroups
+    (1, 1, 1, 1, 1, "diag", "f32", False, True, True, True, 1),
+    (2, 3, 7, 3, 1, "diag", "f32", True, True, True, True, 1),
+    (1, 64, 33, 16, 1, "diag", "f32", False, True, False, False, 1),
+    (3, 65, 65, 5, 1, "diag", "bf16", True, False, True, True, 1),
+    (2, 130, 63, 16, 1, "diag", "bf16", True, True, True, True, 1),
+    (1, 70, 1000, 17, 1, "diag", "f32", True, True, True, True, 1),       # segments, ragged N
+    (1, 16, 4100, 16, 1, "diag", "bf16", True, True, True, True, 1),      # segments, ragged L
+    (2, 128, 257, 64, 1, "diag", "f32", True, True, True, True, 2),       # two B/C groups
+    (1, 128, 96, 128, 1, "diag", "bf16", False, True, True, True, 1),
+    (2, 256, 77, 128, 64, "head", "bf16", True, True, True, True, 1),
+    (1, 192, 300, 32, 2, "head", "f32", True, True, True, True, 1),
+    (1, 128, 2100, 8, 128, "head", "f32", False, True, False, True, 1),   # segments, head mode
+    (2, 128, 40, 4, 64, "head", "bf16", True, True, True, False, 2),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=lambda c: "-".join(map(str, c)))
+def test_edge_shapes(case):
+    batch, dim, L, N, headdim, a_mode, io, gate, sp, hasD, bias, G = case
+    # without softplus the step size is raw + bias itself, so it is drawn positive
+    dists = {} if sp else {"delta": ssmgen.Dist(ssmgen.UNIFORM, 0.0, 0.2),
+                           "delta_bias": ssmgen.Dist(ssmgen.UNIFORM, 0.001, 0.01)}
+    cfg = ssmgen.ScanConfig(name="edge", batch=batch, dim=dim, L=L, N=N, ngroups=G,
+                            headdim=headdim, a_mode=a_mode, io=io, gate=gate, softplus=sp,
+                            has_D=hasD, has_bias=bias, seed=12345 + L + 7 * dim, dists=dists)
+    _say(f"[edge] {case}")
+    inputs = ssmgen.make_inputs(cfg)
+    y = run_hip(device_inputs(inputs), softplus=sp)
+    torch.cuda.synchronize()
+    _check(cfg, inputs, y)
+
+
+def test_empty_inputs_are_noops():
+    import selective_state_space_24_amd as ssm
+    for (b, d, L) in [(0, 8, 16), (2, 8, 0)]:
+        x = torch.zeros(b, d, L, dtype=torch.bfloat16, device="cuda")
+        B = torch.zeros(b, 1, 4, L, dtype=torch.bfloat16, device="cuda")
+        A = torch.zeros(d, 4, device="cuda")
+        y = ssm.selective_scan_fwd(x, x.clone(), A, B, B.clone())
+        assert y.shape == x.shape
+
+
+def test_strided_views_match_contiguous():
+    """Inputs that are views into larger buffers (batch and channel strides > packed)."""
+    cfg = ssmgen.ScanConfig(name="strided", batch=2, dim=96, L=200, N=16, seed=99)
+    inputs = ssmgen.make_inputs(cfg)
+    dev = device_inputs(inputs)
+    big = {}
+    for k in ("x", "delta", "z"):
+        t = dev[k]
+        buf = torch.zeros(t.shape[0], t.shape[1] + 3, t.shape[2] + 24, dtype=t.dtype, device="cuda")
+        buf[:, 1:1 + t.shape[1], 8:8 + t.shape[2]] = t
+        big[k] = buf[:, 1:1 + t.shape[1], 8:8 + t.shape[2]]
+    for k in ("B", "C"):
+        t = dev[k]
+        buf = torch.zeros(t.shape[0], t.shape[1], t.shape[2] + 2, t.shape[3] + 8, dtype=t.dtype, device="cuda")
+        buf[:, :, 2:, :t.shape[3]] = t
+        big[k] = buf[:, :, 2:, :t.shape[3]]
+    for k in ("A", "D", "delta_bias"):
+        big[k] = dev[k]
+    y_ref = run_hip(dev)
+    y_big = torch.zeros(2, 100, 240, dtype=torch.bfloat16, device="cuda")
+    y_view = y_big[:, 2:98, 16:216]
+    run_hip(big, out=y_view)
+    torch.cuda.synchronize()
+    assert torch.equal(y_ref, y_view)
+    _check(cfg, inputs, y_view)
+    # the padding around the output view is untouched
+    assert float(y_big[:, :2].abs().sum()) == 0.0 and float(y_big[:, :, :16].abs().sum()) == 0.0
+
+
+def test_run_to_run_bitwise_determinism():
+    cfg = ssmgen.CONFIGS[1]
+    dev = device_inputs(ssmgen.make_inputs(cfg))
+    y1 = run_hip(dev)
+    y2 = run_hip(dev)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+def test_causality_on_gpu():
+    cfg = ssmgen.ScanConfig(name="causal", batch=1, dim=64, L=3000, N=16, seed=5)
+    inputs = ssmgen.make_inputs(cfg)
+    dev = device_inputs(inputs)
+    y1 = run_hip(dev)
+    t0 = 1234
+    dev2 = {k: v.clone() for k, v in dev.items()}
+    dev2["x"][..., t0:] += 1.0
+    dev2["B"][..., t0:] *= -1.0
+    y2 = run_hip(dev2)
+    torch.cuda.synchronize()
+    assert torch.equal(y1[..., :t0], y2[..., :t0])
+    assert not torch.equal(y1[..., t0:], y2[..., t0:])
+
+
+def test_head_mode_equals_broadcast_channel_mode():
+    """Head mode against per-channel mode with A, delta and bias repeated over each head; the
+    same arithmetic per element except the exp, so the results agree to fp32 rounding."""
+    cfg = ssmgen.ScanConfig(name="heads", batch=2, dim=256, L=500, N=16, headdim=64,
+                            a_mode="head", io="f32", seed=7)
+    inputs = ssmgen.make_inputs(cfg)
+    dev = device_inputs(inputs)
+    yh = run_hip(dev)
+    rep = dict(dev)
+    rep["A"] = dev["A"].repeat_interleave(64)[:, None].expand(256, 16).contiguous()
+    rep["delta"] = dev["delta"].repeat_interleave(64, dim=1).contiguous()
+    rep["delta_bias"] = dev["delta_bias"].repeat_interleave(64).contiguous()
+    yc = run_hip(rep)
+    torch.cuda.synchronize()
+    err = oracle.rel_err(yh.cpu().numpy(), yc.cpu().numpy().astype(np.float64))
+    assert err < 1e-5
