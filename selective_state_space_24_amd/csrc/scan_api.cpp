@@ -10,11 +10,12 @@
 namespace ssm {
 hipError_t launch_scan_fwd(const ScanParams& p, bool bf16, bool head, hipStream_t stream);
 int time_tile();
+int channels_per_group(int64_t N);
 }  // namespace ssm
 
 namespace {
 
-constexpr int64_t kTargetWorkgroups = 512;    // about two resident workgroups per CU (256 CUs)
+constexpr int64_t kTargetWaves = 2048;        // about two resident wavefronts per SIMD (256 CUs)
 constexpr int64_t kMinSegmentTiles = 8;       // shortest segment worth a summary pass, in tiles
 constexpr int64_t kMaxSegments = 65535;       // grid.y limit
 
@@ -86,13 +87,22 @@ int check_desc(const ssm_scan_desc* d) {
   return SSM_OK;
 }
 
+// Wavefronts per channel group of the kernel chosen for dstate N (16 channels x 4 rows per
+// wavefront up to N = 32, else 64 channels with one wavefront per slice of states).
+int64_t waves_per_group(int64_t N) {
+  if (N <= 32) return 1;
+  return N <= 64 ? 4 : 8;
+}
+
 Plan plan_segments(const ssm_scan_desc* d) {
   const int64_t tile = ssm::time_tile();
-  const int64_t groups = d->batch * ((d->dim + ssm::kChannelsPerGroup - 1) / ssm::kChannelsPerGroup);
+  const int64_t cpg = ssm::channels_per_group(d->dstate);
+  const int64_t groups = d->batch * ((d->dim + cpg - 1) / cpg);
+  const int64_t waves = groups * waves_per_group(d->dstate);
   Plan p{1, d->seqlen > 0 ? d->seqlen : 1};
   if (groups == 0 || d->seqlen == 0) return p;
-  if (groups * 4 >= kTargetWorkgroups * 3) return p;  // enough channel groups: one pass
-  int64_t want = (kTargetWorkgroups + groups - 1) / groups;
+  if (waves * 4 >= kTargetWaves * 3) return p;  // enough channel groups: one pass
+  int64_t want = (kTargetWaves + waves - 1) / waves;
   const int64_t tiles = (d->seqlen + tile - 1) / tile;
   const int64_t max_by_len = tiles / kMinSegmentTiles;
   if (want > max_by_len) want = max_by_len;
@@ -203,9 +213,9 @@ int ssm_selective_scan_fwd(const ssm_scan_desc* desc, const void* x, const void*
   for (int i = 0; i < 8; ++i)
     if (overlaps(y, y_bytes, in_ptrs[i], in_bytes[i])) return SSM_ERR_ALIAS;
 
-  // B and C must be uniform over each 64-channel workgroup
+  // B and C must be uniform over each workgroup's channels
   const int64_t ch_per_group = d.dim / d.ngroups;
-  if (d.ngroups > 1 && ch_per_group % ssm::kChannelsPerGroup != 0) return SSM_ERR_UNSUPPORTED;
+  if (d.ngroups > 1 && ch_per_group % ssm::channels_per_group(d.dstate) != 0) return SSM_ERR_UNSUPPORTED;
 
   const Plan plan = plan_segments(desc);
   const size_t need = workspace_bytes_for(desc, plan);

@@ -97,6 +97,22 @@ __device__ __forceinline__ void load_chunk(const IO* __restrict__ row, int64_t t
   }
 }
 
+// The kVec io values of a 16-byte word as fp32.
+template <typename IO>
+__device__ __forceinline__ void unpack16(const u32x4 w, float (&out)[IoTraits<IO>::kVec]) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  if constexpr (IoTraits<IO>::kVec == 8) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      out[2 * k] = __uint_as_float(ws[k] << 16);
+      out[2 * k + 1] = __uint_as_float(ws[k] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) out[k] = __uint_as_float(ws[k]);
+  }
+}
+
 template <typename IO>
 __device__ __forceinline__ void store_chunk(IO* __restrict__ row, int64_t t, int cnt, bool vec_ok,
                                             const float (&v)[IoTraits<IO>::kVec]) {
@@ -397,6 +413,354 @@ __global__ void __launch_bounds__(64 * NW)
   }
 }
 
+// Sum of v over the four 16-lane rows, transposed over four steps: on return, row r of the
+// result holds the row-sum of p[r] (per lane position within the row). gfx950's
+// v_permlane32_swap exchanges the upper half of its first operand with the lower half of its
+// second; v_permlane16_swap exchanges the odd rows of the first with the even rows of the second.
+__device__ __forceinline__ float rows_transpose_sum4(float p0, float p1, float p2, float p3) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p2), false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(p1), __float_as_uint(p3), false, false);
+  const float s02 = __uint_as_float(a[0]) + __uint_as_float(a[1]);  // rows: p0(0+2) p0(1+3) p2(0+2) p2(1+3)
+  const float s13 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// One wavefront per workgroup: 16 channels x 4 rows. Lane (row, ci) owns channel d0 + ci and the
+// states [row*NS, row*NS + NS); the readout over the four rows is summed with cross-row lane
+// swaps, so wavefronts never wait for each other. Global loads of the next tile are issued as
+// soon as the current tile's raw registers have been consumed, and complete while the
+// recurrence runs.
+template <typename IO, int NS, bool HEAD, bool SUMMARY>
+__global__ void __launch_bounds__(64)
+    scan_rows_kernel(const IO* __restrict__ X, const IO* __restrict__ DL, const IO* __restrict__ Bm,
+                     const IO* __restrict__ Cm, const IO* __restrict__ Z, IO* __restrict__ Y,
+                     const float* __restrict__ Am, const float* __restrict__ Dm,
+                     const float* __restrict__ bias_p, float* __restrict__ hend,
+                     float* __restrict__ dsum, const ScanParams p) {
+  static_assert(NS % 4 == 0, "states are swept in chunks of four");
+  constexpr int CH = 16;       // channels per wavefront
+  constexpr int NP = 4 * NS;   // padded state count
+  constexpr int V = IoTraits<IO>::kVec;
+  constexpr int CPR = kTB / V;  // 16-byte chunks per row of a tile
+  constexpr int IPT = CH * CPR / 64;
+  constexpr int BPT = NP * CPR / 64;
+  static_assert(IPT >= 1 && BPT >= 1 && CH * CPR % 64 == 0 && NP * CPR % 64 == 0, "tile shape");
+  __shared__ __align__(16) float s_du[CH * kDuStride];
+  __shared__ __align__(16) float s_B[NP * kBcStride];
+  __shared__ __align__(16) float s_C[SUMMARY ? 4 : NP * kBcStride];
+  __shared__ __align__(16) float s_y[SUMMARY ? 4 : CH * kPartStride];
+
+  const int lane = threadIdx.x;
+  const int row = lane >> 4;
+  const int ci = lane & 15;
+  const int64_t gpb = (p.dim + CH - 1) / CH;
+  const int64_t b = blockIdx.x / gpb;
+  const int64_t d0 = (blockIdx.x % gpb) * CH;
+  const int seg = blockIdx.y;
+  const int64_t t_begin = (int64_t)seg * p.seg_len;
+  const int64_t t_end = min(p.L, t_begin + p.seg_len);
+  const bool fast_ok = p.vec_io != 0 && p.bc_vec != 0;
+  const bool has_z = !SUMMARY && Z != nullptr;
+  const bool softplus = p.softplus != 0;
+  const int64_t grp = d0 / (p.dim / p.ngroups);
+  const IO* __restrict__ Bg = Bm + b * p.B_sb + grp * p.B_sg;
+  const IO* __restrict__ Cg = Cm + b * p.C_sb + grp * p.C_sg;
+  const int n0 = row * NS;
+
+  // ---- per-lane constants of channel d = d0 + ci, states n0 .. n0 + NS - 1
+  const int64_t d = d0 + ci;
+  const bool live = d < p.dim;
+  float ap[HEAD ? 1 : NS];
+  if constexpr (HEAD) {
+    ap[0] = live ? Am[d / p.headdim] * kLog2e : 0.0f;
+  } else {
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+      ap[j] = (live && n0 + j < p.N) ? Am[d * p.N + n0 + j] * kLog2e : 0.0f;
+  }
+  float h[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) h[j] = 0.0f;
+  if (!SUMMARY && seg > 0 && live) {
+    const int64_t base = (b * p.dim + d) * p.nseg;
+    for (int s = 0; s < seg; ++s) {
+      const float ds = dsum[base + s];
+      const float* he = hend + (base + s) * p.N;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        float a;
+        if constexpr (HEAD) a = ap[0]; else a = ap[j];
+        if (n0 + j < p.N) h[j] = __builtin_amdgcn_exp2f(a * ds) * h[j] + he[n0 + j];
+      }
+    }
+  }
+  double dsum_total = 0.0;
+
+  // ---- this lane's prologue/epilogue items, fixed for the whole segment: io item it covers
+  // channel row ir[it], steps itl[it] .. +V of each tile; B/C item it covers state bn[it]
+  const IO* xrow[IPT];
+  const IO* drow_p[IPT];
+  const IO* zrow[IPT];
+  IO* yrow[IPT];
+  float ibias[IPT], iD[IPT];
+  int ir[IPT], itl[IPT];
+  bool ilive[IPT];
+#pragma unroll
+  for (int it = 0; it < IPT; ++it) {
+    const int item = lane + it * 64;
+    ir[it] = item / CPR;
+    itl[it] = (item % CPR) * V;
+    const int64_t dd = d0 + ir[it];
+    ilive[it] = dd < p.dim;
+    const int64_t dv = min(dd, p.dim - 1);  // rows past dim read a valid row (never stored)
+    const int64_t dr = HEAD ? dv / p.headdim : dv;
+    xrow[it] = X + b * p.x_sb + dv * p.x_sd;
+    drow_p[it] = DL + b * p.dl_sb + dr * p.dl_sd;
+    zrow[it] = has_z ? Z + b * p.z_sb + dv * p.z_sd : nullptr;
+    yrow[it] = SUMMARY ? nullptr : Y + b * p.y_sb + dv * p.y_sd;
+    ibias[it] = bias_p ? bias_p[dr] : 0.0f;
+    iD[it] = (!SUMMARY && Dm) ? Dm[dv] : 0.0f;
+  }
+  const IO* brow[BPT];
+  const IO* crow[BPT];
+  int bn[BPT], btl[BPT];
+#pragma unroll
+  for (int it = 0; it < BPT; ++it) {
+    const int item = lane + it * 64;
+    bn[it] = item / CPR;
+    btl[it] = (item % CPR) * V;
+    const int64_t nn = min<int64_t>(bn[it], p.N - 1);
+    brow[it] = Bg + nn * p.B_sn;
+    crow[it] = SUMMARY ? nullptr : Cg + nn * p.C_sn;
+  }
+
+  // raw 16-byte words of the next full tile
+  u32x4 rx[IPT], rd[IPT], rz[IPT], rb[BPT], rc[BPT];
+  auto fetch = [&](int64_t t0) {
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+      rx[it] = load16<true>(xrow[it] + t0 + itl[it]);
+      rd[it] = load16<true>(drow_p[it] + t0 + itl[it]);
+      if (has_z) rz[it] = load16<true>(zrow[it] + t0 + itl[it]);
+    }
+#pragma unroll
+    for (int it = 0; it < BPT; ++it) {
+      rb[it] = load16<false>(brow[it] + t0 + btl[it]);
+      if (!SUMMARY) rc[it] = load16<false>(crow[it] + t0 + btl[it]);
+    }
+  };
+  if (fast_ok && t_end - t_begin >= kTB) fetch(t_begin);
+
+  float xkeep[IPT][V];
+  u32x4 zkeep[IPT];
+
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += kTB) {
+    const int tb_len = (int)min<int64_t>(kTB, t_end - t0);
+    const bool full = fast_ok && tb_len == kTB;
+
+    // ---- prologue: delta, u = delta * x into LDS; B, C tiles into LDS (fp32)
+    if (full) {
+#pragma unroll
+      for (int it = 0; it < IPT; ++it) {
+        float dv[V];
+        unpack16<IO>(rx[it], xkeep[it]);
+        unpack16<IO>(rd[it], dv);
+        zkeep[it] = rz[it];
+        float du[2 * V];
+        if (softplus) {
+#pragma unroll
+          for (int e = 0; e < V; ++e) {
+            const float dl = softplus_f32(dv[e] + ibias[it]);
+            du[2 * e] = dl;
+            du[2 * e + 1] = dl * xkeep[it][e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < V; ++e) {
+            const float dl = dv[e] + ibias[it];
+            du[2 * e] = dl;
+            du[2 * e + 1] = dl * xkeep[it][e];
+          }
+        }
+        float4* dst = reinterpret_cast<float4*>(&s_du[ir[it] * kDuStride + 2 * itl[it]]);
+#pragma unroll
+        for (int k = 0; k < V / 2; ++k)
+          dst[k] = make_float4(du[4 * k], du[4 * k + 1], du[4 * k + 2], du[4 * k + 3]);
+      }
+#pragma unroll
+      for (int it = 0; it < BPT; ++it) {
+        float bv[V], cv[V];
+        unpack16<IO>(rb[it], bv);
+        if constexpr (!SUMMARY) unpack16<IO>(rc[it], cv);
+        if (bn[it] >= p.N) {
+#pragma unroll
+          for (int e = 0; e < V; ++e) { bv[e] = 0.0f; cv[e] = 0.0f; }
+        }
+        float4* db = reinterpret_cast<float4*>(&s_B[bn[it] * kBcStride + btl[it]]);
+#pragma unroll
+        for (int k = 0; k < V / 4; ++k)
+          db[k] = make_float4(bv[4 * k], bv[4 * k + 1], bv[4 * k + 2], bv[4 * k + 3]);
+        if constexpr (!SUMMARY) {
+          float4* dc = reinterpret_cast<float4*>(&s_C[bn[it] * kBcStride + btl[it]]);
+#pragma unroll
+          for (int k = 0; k < V / 4; ++k)
+            dc[k] = make_float4(cv[4 * k], cv[4 * k + 1], cv[4 * k + 2], cv[4 * k + 3]);
+        }
+      }
+      // the raw registers are free: start loading the next tile
+      if (t_end - (t0 + kTB) >= kTB) fetch(t0 + kTB);
+    } else {
+      // partial tile or unaligned rows: guarded element loads; padding steps and channels get
+      // delta = u = 0 (dA = 1, dB x = 0) and B = C = 0
+#pragma unroll
+      for (int it = 0; it < IPT; ++it) {
+        const int cnt = max(0, min(V, tb_len - itl[it]));
+        const int c2 = ilive[it] ? cnt : 0;
+        float dv[V], zv[V];
+        load_chunk<IO, true>(xrow[it], t0 + itl[it], c2, false, xkeep[it]);
+        load_chunk<IO, true>(drow_p[it], t0 + itl[it], c2, false, dv);
+        if (has_z) load_chunk<IO, true>(zrow[it], t0 + itl[it], c2, false, zv);
+        else {
+#pragma unroll
+          for (int e = 0; e < V; ++e) zv[e] = 0.0f;
+        }
+        uint32_t zw[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if constexpr (V == 8) zw[k] = pack_bf16x2(zv[2 * k], zv[2 * k + 1]);
+          else zw[k] = __float_as_uint(zv[k]);
+        }
+        zkeep[it] = u32x4{zw[0], zw[1], zw[2], zw[3]};
+        float du[2 * V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const float v = dv[e] + ibias[it];
+          float dl = softplus ? softplus_f32(v) : v;
+          if (e >= c2) dl = 0.0f;
+          du[2 * e] = dl;
+          du[2 * e + 1] = dl * xkeep[it][e];
+        }
+        float4* dst = reinterpret_cast<float4*>(&s_du[ir[it] * kDuStride + 2 * itl[it]]);
+#pragma unroll
+        for (int k = 0; k < V / 2; ++k)
+          dst[k] = make_float4(du[4 * k], du[4 * k + 1], du[4 * k + 2], du[4 * k + 3]);
+      }
+#pragma unroll
+      for (int it = 0; it < BPT; ++it) {
+        const int cnt = bn[it] < p.N ? max(0, min(V, tb_len - btl[it])) : 0;
+        float bv[V], cv[V];
+        load_chunk<IO, false>(brow[it], t0 + btl[it], cnt, false, bv);
+        if constexpr (!SUMMARY) load_chunk<IO, false>(crow[it], t0 + btl[it], cnt, false, cv);
+        float4* db = reinterpret_cast<float4*>(&s_B[bn[it] * kBcStride + btl[it]]);
+#pragma unroll
+        for (int k = 0; k < V / 4; ++k)
+          db[k] = make_float4(bv[4 * k], bv[4 * k + 1], bv[4 * k + 2], bv[4 * k + 3]);
+        if constexpr (!SUMMARY) {
+          float4* dc = reinterpret_cast<float4*>(&s_C[bn[it] * kBcStride + btl[it]]);
+#pragma unroll
+          for (int k = 0; k < V / 4; ++k)
+            dc[k] = make_float4(cv[4 * k], cv[4 * k + 1], cv[4 * k + 2], cv[4 * k + 3]);
+        }
+      }
+      if (fast_ok && t0 + kTB < t_end && t_end - (t0 + kTB) >= kTB) fetch(t0 + kTB);
+    }
+    __syncthreads();
+
+    // ---- recurrence over the tile
+    for (int tt = 0; tt < tb_len; tt += 8) {
+      float dl[8], u[8];
+      const float4* src = reinterpret_cast<const float4*>(&s_du[ci * kDuStride + 2 * tt]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float4 q = src[k];
+        dl[2 * k] = q.x; u[2 * k] = q.y; dl[2 * k + 1] = q.z; u[2 * k + 1] = q.w;
+      }
+      float acc[8];
+      float dA_head[HEAD ? 8 : 1];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        acc[k] = 0.0f;
+        if constexpr (HEAD) dA_head[k] = __builtin_amdgcn_exp2f(dl[k] * ap[0]);
+      }
+      if constexpr (SUMMARY) {
+        float s8 = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) s8 += dl[k];
+        dsum_total += (double)s8;
+      }
+#pragma unroll
+      for (int jc = 0; jc < NS; jc += 4) {
+        // 16 (state, step) values per register and row: states n0+jc .. +3, steps tt .. tt+3
+        // (lo) and tt+4 .. tt+7 (hi)
+        const int bc_off = (n0 + jc + (ci >> 2)) * kBcStride + tt + (ci & 3);
+        const float b_lo = s_B[bc_off], b_hi = s_B[bc_off + 4];
+        float c_lo = 0.0f, c_hi = 0.0f;
+        if constexpr (!SUMMARY) { c_lo = s_C[bc_off]; c_hi = s_C[bc_off + 4]; }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int slot = j * 4 + (k & 3);
+            float dA;
+            if constexpr (HEAD) dA = dA_head[k]; else dA = __builtin_amdgcn_exp2f(dl[k] * ap[jc + j]);
+            const float bb = row_bcast_k(k < 4 ? b_lo : b_hi, slot);
+            h[jc + j] = fmaf(dA, h[jc + j], u[k] * bb);
+            if constexpr (!SUMMARY) {
+              const float cc2 = row_bcast_k(k < 4 ? c_lo : c_hi, slot);
+              acc[k] = fmaf(cc2, h[jc + j], acc[k]);
+            }
+          }
+        }
+      }
+      if constexpr (!SUMMARY) {
+        const float y_lo = rows_transpose_sum4(acc[0], acc[1], acc[2], acc[3]);
+        const float y_hi = rows_transpose_sum4(acc[4], acc[5], acc[6], acc[7]);
+        s_y[ci * kPartStride + tt + row] = y_lo;
+        s_y[ci * kPartStride + tt + 4 + row] = y_hi;
+      }
+    }
+    __syncthreads();
+
+    // ---- epilogue: y = (readout + D x) * silu(z), 16-byte stores
+    if constexpr (!SUMMARY) {
+#pragma unroll
+      for (int it = 0; it < IPT; ++it) {
+        float yv[V];
+#pragma unroll
+        for (int e4 = 0; e4 < V; e4 += 4) {
+          const float4 s4 = *reinterpret_cast<const float4*>(&s_y[ir[it] * kPartStride + itl[it] + e4]);
+          yv[e4] = s4.x; yv[e4 + 1] = s4.y; yv[e4 + 2] = s4.z; yv[e4 + 3] = s4.w;
+        }
+        float zv[V];
+        unpack16<IO>(zkeep[it], zv);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          float yy = fmaf(iD[it], xkeep[it][e], yv[e]);
+          if (has_z) yy *= silu_f32(zv[e]);
+          yv[e] = yy;
+        }
+        if (full) {
+          if (ilive[it]) store_chunk<IO>(yrow[it], t0 + itl[it], V, true, yv);
+        } else {
+          const int cnt = max(0, min(V, tb_len - itl[it]));
+          if (ilive[it] && cnt > 0) store_chunk<IO>(yrow[it], t0 + itl[it], cnt, false, yv);
+        }
+      }
+    }
+  }
+
+  if constexpr (SUMMARY) {
+    if (live) {
+      const int64_t base = (b * p.dim + d) * p.nseg + seg;
+#pragma unroll
+      for (int j = 0; j < NS; ++j)
+        if (n0 + j < p.N) hend[base * p.N + n0 + j] = h[j];
+      if (row == 0) dsum[base] = (float)dsum_total;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // host-side launch
 
@@ -422,13 +786,28 @@ static hipError_t launch_cfg(const ScanParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <typename IO, int NS, bool HEAD>
+static hipError_t launch_rows(const ScanParams& p, hipStream_t stream) {
+  const dim3 block(64);
+  const int64_t groups = p.batch * ((p.dim + 15) / 16);
+  if (p.nseg > 1) {
+    const dim3 grid_sum((unsigned)groups, (unsigned)(p.nseg - 1));
+    hipLaunchKernelGGL((scan_rows_kernel<IO, NS, HEAD, true>), grid_sum, block, 0, stream,
+                       SCAN_ARGS(p));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid((unsigned)groups, (unsigned)p.nseg);
+  hipLaunchKernelGGL((scan_rows_kernel<IO, NS, HEAD, false>), grid, block, 0, stream,
+                     SCAN_ARGS(p));
+  return hipGetLastError();
+}
+
 template <typename IO, bool HEAD>
 static hipError_t launch_n(const ScanParams& p, hipStream_t stream) {
   const int64_t N = p.N;
-  if (N <= 4) return launch_cfg<IO, 4, 1, HEAD>(p, stream);
-  if (N <= 8) return launch_cfg<IO, 4, 2, HEAD>(p, stream);
-  if (N <= 16) return launch_cfg<IO, 4, 4, HEAD>(p, stream);
-  if (N <= 32) return launch_cfg<IO, 8, 4, HEAD>(p, stream);
+  if (N <= 16) return launch_rows<IO, 4, HEAD>(p, stream);
+  if (N <= 32) return launch_rows<IO, 8, HEAD>(p, stream);
   if (N <= 64) return launch_cfg<IO, 16, 4, HEAD>(p, stream);
   return launch_cfg<IO, 16, 8, HEAD>(p, stream);  // N <= 128 (checked by the caller)
 }
@@ -439,5 +818,8 @@ hipError_t launch_scan_fwd(const ScanParams& p, bool bf16, bool head, hipStream_
 }
 
 int time_tile() { return kTB; }
+
+// Channels per workgroup of the kernel that launch_scan_fwd picks for dstate N.
+int channels_per_group(int64_t N) { return N <= 32 ? 16 : kChannelsPerGroup; }
 
 }  // namespace ssm

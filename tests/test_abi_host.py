@@ -97,7 +97,7 @@ def test_validation_errors_are_reported_before_launch():
     assert need > 0
     assert _fwd(big) == -7
     assert _fwd(big, ws=FAKE + (20 << 30), wsb=need - 4) == -7
-    g = ssm.desc_contiguous(1, 64, 128, 16, ngroups=2)     # B/C group smaller than 64 channels
+    g = ssm.desc_contiguous(1, 64, 128, 16, ngroups=8)     # B/C group of 8 channels: unsupported
     assert _fwd(g) == -9
 
 
