@@ -11,6 +11,7 @@ namespace ssm {
 hipError_t launch_scan_fwd(const ScanParams& p, bool bf16, bool head, hipStream_t stream);
 int time_tile();
 int channels_per_group(int64_t N);
+int waves_per_group(int64_t N);
 }  // namespace ssm
 
 namespace {
@@ -87,18 +88,11 @@ int check_desc(const ssm_scan_desc* d) {
   return SSM_OK;
 }
 
-// Wavefronts per channel group of the kernel chosen for dstate N (16 channels x 4 rows per
-// wavefront up to N = 32, else 64 channels with one wavefront per slice of states).
-int64_t waves_per_group(int64_t N) {
-  if (N <= 32) return 1;
-  return N <= 64 ? 4 : 8;
-}
-
 Plan plan_segments(const ssm_scan_desc* d) {
   const int64_t tile = ssm::time_tile();
   const int64_t cpg = ssm::channels_per_group(d->dstate);
   const int64_t groups = d->batch * ((d->dim + cpg - 1) / cpg);
-  const int64_t waves = groups * waves_per_group(d->dstate);
+  const int64_t waves = groups * ssm::waves_per_group(d->dstate);
   Plan p{1, d->seqlen > 0 ? d->seqlen : 1};
   if (groups == 0 || d->seqlen == 0) return p;
   if (waves * 4 >= kTargetWaves * 3) return p;  // enough channel groups: one pass

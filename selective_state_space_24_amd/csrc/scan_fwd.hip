@@ -1,19 +1,19 @@
 // gfx950 kernels of the selective-scan forward pass.
 //
-// Work decomposition (one workgroup = 64 channels of one batch entry x one segment of L):
+// Work decomposition: one workgroup = 64 channels of one batch entry x one segment of L, in NW
+// wavefronts.
 //   * lane l of every wavefront owns channel d0 + l; wavefront w owns states [w*NS, (w+1)*NS).
 //     The state h (NS fp32 values per lane) lives in VGPRs for the whole segment and is never
 //     written to memory (the pages' hardware-aware scan keeps the expanded state on chip).
-//   * time advances in tiles of kTB steps. Per tile, a prologue (all threads) loads x, delta and
-//     z with row-contiguous 16-byte loads, computes the step size delta = softplus(raw + bias)
-//     and u = delta * x once per (channel, t), and stages those plus the tile of B and C
-//     (shared by all channels of the group) in LDS as fp32.
-//   * the recurrence sweeps the tile per lane. B_tn and C_tn are the same for every lane, so a
-//     wavefront fetches 16 (state, step) values per VGPR (one per lane of a 16-lane row,
-//     replicated over the four rows) and broadcasts each one with the DPP row_newbcast operand
-//     modifier, which folds into the multiply that consumes it.
-//   * each wavefront's partial readout sum_n C h over its states goes to LDS; an epilogue adds
-//     the partials, the D skip and the silu(z) gate and stores y with 16-byte stores.
+//   * time advances in load tiles of 64 steps. A prologue (all threads) reads x, delta, z and
+//     the B, C rows with 16-byte loads, 128 contiguous bytes per row, computes the step size
+//     delta = softplus(raw + bias) and u = delta * x once per (channel, t), and stages them and
+//     the B, C tile in LDS as fp32. Loads of the next tile are issued before the current one is
+//     processed.
+//   * the recurrence runs per 32-step half. B_tn and C_tn are the same in every lane of a
+//     wavefront, so they are read with wave-uniform LDS addresses and enter the multiply-adds
+//     as plain operands; each wavefront's partial readout sum_n C h over its states goes to LDS
+//     and an epilogue adds the partials, the D skip and the silu(z) gate and stores y.
 //   * a sequence split into segments along L (too few channels to fill the chip) first runs a
 //     summary pass per segment: the final state from a zero start and the segment's sum of
 //     delta, whose exp(A * sum) is the segment's decay. The output pass of segment s composes the
@@ -30,10 +30,15 @@ namespace ssm {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kTB = 32;                 // time steps per tile
-constexpr int kDuStride = 2 * kTB + 4;  // floats per channel row of (delta, u) in LDS
-constexpr int kPartStride = kTB + 4;    // floats per channel row of partial readouts
-constexpr int kBcStride = kTB + 4;      // floats per state row of the B / C tile
+constexpr int kTB = 32;                 // time steps per compute tile
+constexpr int kLT = 2 * kTB;            // time steps per load tile (128 bytes of bf16 per row)
+constexpr int kDuStrideL = 2 * kLT + 4;  // floats per channel row of (delta, u) in LDS
+constexpr int kBcStrideL = kLT + 4;      // floats per state row of the B / C tile
+constexpr int kPartStride = kTB + 4;     // floats per channel row of partial readouts
+#ifndef SSM_PREFETCH_TILES
+#define SSM_PREFETCH_TILES 1
+#endif
+constexpr int kPrefetch = SSM_PREFETCH_TILES;  // load tiles fetched ahead per workgroup
 
 typedef uint16_t bf16_bits;
 typedef float float2v __attribute__((ext_vector_type(2)));
@@ -151,44 +156,40 @@ __device__ __forceinline__ float silu_f32(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
 }
 
-// Lane (16 * row + I)'s value of v, given to every lane of the row (DPP row_newbcast:I).
-template <int I>
-__device__ __forceinline__ float row_bcast(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + I, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float row_bcast_k(float v, int i) {
-  switch (i) {
-    case 0: return row_bcast<0>(v);   case 1: return row_bcast<1>(v);
-    case 2: return row_bcast<2>(v);   case 3: return row_bcast<3>(v);
-    case 4: return row_bcast<4>(v);   case 5: return row_bcast<5>(v);
-    case 6: return row_bcast<6>(v);   case 7: return row_bcast<7>(v);
-    case 8: return row_bcast<8>(v);   case 9: return row_bcast<9>(v);
-    case 10: return row_bcast<10>(v); case 11: return row_bcast<11>(v);
-    case 12: return row_bcast<12>(v); case 13: return row_bcast<13>(v);
-    case 14: return row_bcast<14>(v); default: return row_bcast<15>(v);
-  }
-}
-
-// NS states per wavefront, NW wavefronts (N <= NS*NW); HEAD: one A and one delta per head;
-// SUMMARY: the segment summary pass (no readout, no y).
-template <typename IO, int NS, int NW, bool HEAD, bool SUMMARY>
+// One workgroup = NW wavefronts x 64 channels. Lane l owns channel d0 + l in every wavefront;
+// wavefront w owns states [w*NS, (w+1)*NS), so the B and C values a wavefront needs at a step
+// are the same for all of its lanes: they are read from the LDS tile with wave-uniform
+// addresses and enter the multiply-adds as plain operands. Each wavefront writes its partial
+// readout sum over its states to LDS; the epilogue adds the NW partials.
+//
+// Time advances in load tiles of kLT steps: every row is read 128 contiguous bytes (bf16) at a
+// time, which keeps DRAM pages open; the recurrence and the epilogue run per kTB-step half.
+// Full load tiles take a path whose only global loads are the prefetch ring (so the compiler's
+// wait counts track exactly those loads and the epilogue never waits on the next tile's data);
+// a final partial tile, or rows that do not allow 16-byte access, take a guarded path.
+//
+// HEAD: one A and one delta per head; SUMMARY: the segment summary pass (no readout, no y);
+// GATE: y is multiplied by silu(z).
+template <typename IO, int NS, int NW, bool HEAD, bool SUMMARY, bool GATE>
 __global__ void __launch_bounds__(64 * NW)
     scan_fwd_kernel(const IO* __restrict__ X, const IO* __restrict__ DL, const IO* __restrict__ Bm,
                     const IO* __restrict__ Cm, const IO* __restrict__ Z, IO* __restrict__ Y,
                     const float* __restrict__ Am, const float* __restrict__ Dm,
                     const float* __restrict__ bias_p, float* __restrict__ hend,
                     float* __restrict__ dsum, const ScanParams p) {
-  static_assert(NS % 4 == 0, "states are swept in chunks of four");
+  constexpr int PF = kPrefetch;
   constexpr int NT = 64 * NW;
   constexpr int NP = NS * NW;  // padded state count
   constexpr int V = IoTraits<IO>::kVec;
-  constexpr int CPR = kTB / V;  // 16-byte chunks per row of a tile
+  constexpr int CPR = kTB / V;  // 16-byte chunks per row of a kTB half
   constexpr int ITEMS = kChannelsPerGroup * CPR;
   constexpr int IPT = (ITEMS + NT - 1) / NT;
   constexpr int BC_ITEMS = NP * CPR;
-  __shared__ __align__(16) float s_du[kChannelsPerGroup * kDuStride];
-  __shared__ __align__(16) float s_B[NP * kBcStride];
-  __shared__ __align__(16) float s_C[SUMMARY ? 4 : NP * kBcStride];
+  constexpr int BPT = (BC_ITEMS + NT - 1) / NT;
+  static_assert(!(SUMMARY && GATE), "the summary pass has no gate");
+  __shared__ __align__(16) float s_du[kChannelsPerGroup * kDuStrideL];
+  __shared__ __align__(16) float s_B[NP * kBcStrideL];
+  __shared__ __align__(16) float s_C[SUMMARY ? 4 : NP * kBcStrideL];
   __shared__ __align__(16) float s_part[SUMMARY ? 4 : NW * kChannelsPerGroup * kPartStride];
 
   const int tid = threadIdx.x;
@@ -199,17 +200,14 @@ __global__ void __launch_bounds__(64 * NW)
   const int seg = blockIdx.y;
   const int64_t t_begin = (int64_t)seg * p.seg_len;
   const int64_t t_end = min(p.L, t_begin + p.seg_len);
-  const bool vec_ok = p.vec_io != 0;
-  const bool bc_vec = p.bc_vec != 0;
-  const bool has_z = !SUMMARY && Z != nullptr;
-
-  // B/C group of this workgroup's channels (the host guarantees one group per workgroup)
+  const bool fast_ok = p.vec_io != 0 && p.bc_vec != 0;
+  const bool softplus = p.softplus != 0;
   const int64_t grp = d0 / (p.dim / p.ngroups);
   const IO* __restrict__ Bg = Bm + b * p.B_sb + grp * p.B_sg;
   const IO* __restrict__ Cg = Cm + b * p.C_sb + grp * p.C_sg;
   const int n0 = w * NS;
 
-  // ---- per-lane constants of channel d = d0 + lane
+  // ---- per-lane constants of channel d = d0 + lane, states n0 .. n0 + NS - 1
   const int64_t d = d0 + lane;
   const bool live = d < p.dim;
   float ap[HEAD ? 1 : NS];
@@ -220,7 +218,6 @@ __global__ void __launch_bounds__(64 * NW)
     for (int j = 0; j < NS; ++j)
       ap[j] = (live && n0 + j < p.N) ? Am[d * p.N + n0 + j] * kLog2e : 0.0f;
   }
-
   float h[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) h[j] = 0.0f;
@@ -240,81 +237,194 @@ __global__ void __launch_bounds__(64 * NW)
   }
   double dsum_total = 0.0;
 
-  float xkeep[IPT][V];
-  float zkeep[IPT][V];
+  // ---- this thread's prologue/epilogue items, fixed for the whole segment: io item it covers
+  // channel row ir[it], steps itl[it] .. +V of each half; B/C item it covers state bn[it]
+  const IO* xrow[IPT];
+  const IO* drow_p[IPT];
+  const IO* zrow[IPT];
+  IO* yrow[IPT];
+  float ibias[IPT], iD[IPT];
+  int ir[IPT], itl[IPT];
+  bool ilive[IPT], iown[IPT];
+#pragma unroll
+  for (int it = 0; it < IPT; ++it) {
+    const int item = tid + it * NT;
+    iown[it] = ITEMS % NT == 0 || item < ITEMS;
+    const int itc = iown[it] ? item : 0;
+    ir[it] = itc / CPR;
+    itl[it] = (itc % CPR) * V;
+    const int64_t dd = d0 + ir[it];
+    ilive[it] = iown[it] && dd < p.dim;
+    const int64_t dv = min(dd, p.dim - 1);  // rows past dim read a valid row (never stored)
+    const int64_t dr = HEAD ? dv / p.headdim : dv;
+    xrow[it] = X + b * p.x_sb + dv * p.x_sd;
+    drow_p[it] = DL + b * p.dl_sb + dr * p.dl_sd;
+    zrow[it] = GATE ? Z + b * p.z_sb + dv * p.z_sd : nullptr;
+    yrow[it] = SUMMARY ? nullptr : Y + b * p.y_sb + dv * p.y_sd;
+    ibias[it] = bias_p ? bias_p[dr] : 0.0f;
+    iD[it] = (!SUMMARY && Dm) ? Dm[dv] : 0.0f;
+  }
+  const IO* brow[BPT];
+  const IO* crow[BPT];
+  int bn[BPT], btl[BPT];
+  bool bown[BPT];
+#pragma unroll
+  for (int it = 0; it < BPT; ++it) {
+    const int item = tid + it * NT;
+    bown[it] = BC_ITEMS % NT == 0 || item < BC_ITEMS;
+    const int itc = bown[it] ? item : 0;
+    bn[it] = itc / CPR;
+    btl[it] = (itc % CPR) * V;
+    const int64_t nn = min<int64_t>(bn[it], p.N - 1);
+    brow[it] = Bg + nn * p.B_sn;
+    crow[it] = SUMMARY ? nullptr : Cg + nn * p.C_sn;
+  }
 
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += kTB) {
-    const int tb_len = (int)min<int64_t>(kTB, t_end - t0);
-
-    // ---- prologue 1: delta and u = delta * x of the tile, into LDS. Steps past the end of the
-    // sequence get delta = u = 0, which leaves h unchanged (dA = 1, dB x = 0).
+  // raw 16-byte words of a full load tile: each item's two halves are fetched back to back
+  struct Raw {
+    u32x4 x[2][IPT], d[2][IPT], z[2][IPT], b[2][BPT], c[2][BPT];
+  };
+  auto fetch = [&](Raw& r, int64_t t0) {
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
-      const int item = tid + it * NT;
-      if (ITEMS % NT == 0 || item < ITEMS) {
-        const int r = item / CPR;
-        const int tl = (item % CPR) * V;
-        const int64_t dd = d0 + r;
-        const int cnt = max(0, min(V, tb_len - tl));
-        float xv[V], dv[V], zv[V];
-        float bias = 0.0f;
-        if (dd < p.dim && cnt > 0) {
-          const int64_t drow = HEAD ? dd / p.headdim : dd;
-          load_chunk<IO, true>(X + b * p.x_sb + dd * p.x_sd, t0 + tl, cnt, vec_ok, xv);
-          load_chunk<IO, true>(DL + b * p.dl_sb + drow * p.dl_sd, t0 + tl, cnt, vec_ok, dv);
-          if (has_z) load_chunk<IO, true>(Z + b * p.z_sb + dd * p.z_sd, t0 + tl, cnt, vec_ok, zv);
-          if (bias_p) bias = bias_p[drow];
-        } else {
+      if (!iown[it]) continue;
 #pragma unroll
-          for (int e = 0; e < V; ++e) { xv[e] = 0.0f; dv[e] = 0.0f; zv[e] = 0.0f; }
-        }
-        float du[2 * V];
-#pragma unroll
-        for (int e = 0; e < V; ++e) {
-          const float v = dv[e] + bias;
-          const float dl = (e < cnt) ? (p.softplus ? softplus_f32(v) : v) : 0.0f;
-          du[2 * e] = dl;
-          du[2 * e + 1] = dl * xv[e];
-          xkeep[it][e] = xv[e];
-          zkeep[it][e] = has_z ? zv[e] : 0.0f;
-        }
-        float4* dst = reinterpret_cast<float4*>(&s_du[r * kDuStride + 2 * tl]);
-#pragma unroll
-        for (int k = 0; k < V / 2; ++k)
-          dst[k] = make_float4(du[4 * k], du[4 * k + 1], du[4 * k + 2], du[4 * k + 3]);
+      for (int hf = 0; hf < 2; ++hf) {
+        r.x[hf][it] = load16<true>(xrow[it] + t0 + hf * kTB + itl[it]);
+        r.d[hf][it] = load16<true>(drow_p[it] + t0 + hf * kTB + itl[it]);
+        if constexpr (GATE) r.z[hf][it] = load16<true>(zrow[it] + t0 + hf * kTB + itl[it]);
       }
     }
-    // ---- prologue 2: the B (and C) tile as fp32; padded states and steps are zero
-    for (int item = tid; item < BC_ITEMS; item += NT) {
-      const int n = item / CPR;
-      const int tl = (item % CPR) * V;
-      const int cnt = max(0, min(V, tb_len - tl));
-      float bv[V], cv[V];
-      if (n < p.N && cnt > 0) {
-        load_chunk<IO, false>(Bg + (int64_t)n * p.B_sn, t0 + tl, cnt, bc_vec, bv);
-        if (!SUMMARY) load_chunk<IO, false>(Cg + (int64_t)n * p.C_sn, t0 + tl, cnt, bc_vec, cv);
-      } else {
 #pragma unroll
-        for (int e = 0; e < V; ++e) { bv[e] = 0.0f; cv[e] = 0.0f; }
+    for (int it = 0; it < BPT; ++it) {
+      if (!bown[it]) continue;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        r.b[hf][it] = load16<false>(brow[it] + t0 + hf * kTB + btl[it]);
+        if constexpr (!SUMMARY) r.c[hf][it] = load16<false>(crow[it] + t0 + hf * kTB + btl[it]);
       }
-      float4* db = reinterpret_cast<float4*>(&s_B[n * kBcStride + tl]);
+    }
+  };
+
+  float xkeep[2][IPT][V];
+  u32x4 zkeep[2][IPT];
+
+  // delta and u = delta * x of item it, half hf, into LDS
+  auto put_du = [&](int hf, int it, float (&dv)[V]) {
+    float du[2 * V];
+    if (softplus) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const float dl = softplus_f32(dv[e] + ibias[it]);
+        du[2 * e] = dl;
+        du[2 * e + 1] = dl * xkeep[hf][it][e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const float dl = dv[e] + ibias[it];
+        du[2 * e] = dl;
+        du[2 * e + 1] = dl * xkeep[hf][it][e];
+      }
+    }
+    float4* dst = reinterpret_cast<float4*>(&s_du[ir[it] * kDuStrideL + 2 * (hf * kTB + itl[it])]);
+#pragma unroll
+    for (int k = 0; k < V / 2; ++k)
+      dst[k] = make_float4(du[4 * k], du[4 * k + 1], du[4 * k + 2], du[4 * k + 3]);
+  };
+  auto put_bc = [&](int hf, int it, const float (&bv)[V], const float (&cv)[V]) {
+    float4* db = reinterpret_cast<float4*>(&s_B[bn[it] * kBcStrideL + hf * kTB + btl[it]]);
+#pragma unroll
+    for (int k = 0; k < V / 4; ++k)
+      db[k] = make_float4(bv[4 * k], bv[4 * k + 1], bv[4 * k + 2], bv[4 * k + 3]);
+    if constexpr (!SUMMARY) {
+      float4* dc = reinterpret_cast<float4*>(&s_C[bn[it] * kBcStrideL + hf * kTB + btl[it]]);
 #pragma unroll
       for (int k = 0; k < V / 4; ++k)
-        db[k] = make_float4(bv[4 * k], bv[4 * k + 1], bv[4 * k + 2], bv[4 * k + 3]);
-      if constexpr (!SUMMARY) {
-        float4* dc = reinterpret_cast<float4*>(&s_C[n * kBcStride + tl]);
+        dc[k] = make_float4(cv[4 * k], cv[4 * k + 1], cv[4 * k + 2], cv[4 * k + 3]);
+    }
+  };
+
+  // prologue of a full load tile from the raw registers
+  auto prologue_full = [&](const Raw& rw) {
 #pragma unroll
-        for (int k = 0; k < V / 4; ++k)
-          dc[k] = make_float4(cv[4 * k], cv[4 * k + 1], cv[4 * k + 2], cv[4 * k + 3]);
+    for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+      for (int it = 0; it < IPT; ++it) {
+        if (!iown[it]) continue;
+        float dv[V];
+        unpack16<IO>(rw.x[hf][it], xkeep[hf][it]);
+        unpack16<IO>(rw.d[hf][it], dv);
+        if constexpr (GATE) zkeep[hf][it] = rw.z[hf][it];
+        put_du(hf, it, dv);
+      }
+#pragma unroll
+      for (int it = 0; it < BPT; ++it) {
+        if (!bown[it]) continue;
+        float bv[V], cv[V];
+        unpack16<IO>(rw.b[hf][it], bv);
+        if constexpr (!SUMMARY) unpack16<IO>(rw.c[hf][it], cv);
+        if (bn[it] >= p.N) {
+#pragma unroll
+          for (int e = 0; e < V; ++e) { bv[e] = 0.0f; cv[e] = 0.0f; }
+        }
+        put_bc(hf, it, bv, cv);
       }
     }
-    __syncthreads();
+  };
 
-    // ---- recurrence over the tile: lane = channel, this wavefront's NS states
-    const int ri = lane & 15;  // slot in a 16-lane row: state ri / 4, step ri % 4
+  // prologue of a partial load tile (or unaligned rows) with guarded element loads; padding
+  // steps get delta = u = 0 (dA = 1, dB x = 0) and padding states B = C = 0
+  auto prologue_partial = [&](int64_t t0, int lt_len) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int tb_len = max(0, min(kTB, lt_len - hf * kTB));
+#pragma unroll
+      for (int it = 0; it < IPT; ++it) {
+        if (!iown[it]) continue;
+        const int cnt = ilive[it] ? max(0, min(V, tb_len - itl[it])) : 0;
+        float dv[V], zv[V];
+        load_chunk<IO, true>(xrow[it], t0 + hf * kTB + itl[it], cnt, false, xkeep[hf][it]);
+        load_chunk<IO, true>(drow_p[it], t0 + hf * kTB + itl[it], cnt, false, dv);
+        if constexpr (GATE) {
+          load_chunk<IO, true>(zrow[it], t0 + hf * kTB + itl[it], cnt, false, zv);
+          uint32_t zw[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            if constexpr (V == 8) zw[k] = pack_bf16x2(zv[2 * k], zv[2 * k + 1]);
+            else zw[k] = __float_as_uint(zv[k]);
+          }
+          zkeep[hf][it] = u32x4{zw[0], zw[1], zw[2], zw[3]};
+        }
+        put_du(hf, it, dv);
+        if (cnt < V) {
+          // padding steps: delta = u = 0 (written over what put_du stored)
+          float* row = &s_du[ir[it] * kDuStrideL + 2 * (hf * kTB + itl[it])];
+          for (int e = cnt; e < V; ++e) { row[2 * e] = 0.0f; row[2 * e + 1] = 0.0f; }
+        }
+      }
+#pragma unroll
+      for (int it = 0; it < BPT; ++it) {
+        if (!bown[it]) continue;
+        const int cnt = bn[it] < p.N ? max(0, min(V, tb_len - btl[it])) : 0;
+        float bv[V], cv[V];
+        load_chunk<IO, false>(brow[it], t0 + hf * kTB + btl[it], cnt, false, bv);
+        if constexpr (!SUMMARY) {
+          load_chunk<IO, false>(crow[it], t0 + hf * kTB + btl[it], cnt, false, cv);
+        } else {
+#pragma unroll
+          for (int e = 0; e < V; ++e) cv[e] = 0.0f;
+        }
+        put_bc(hf, it, bv, cv);
+      }
+    }
+  };
+
+  // the recurrence over steps [h0, h0 + tb_len) of the load tile: lane = channel
+  auto recurrence = [&](int h0, int tb_len) {
     for (int tt = 0; tt < tb_len; tt += 8) {
       float dl[8], u[8];
-      const float4* src = reinterpret_cast<const float4*>(&s_du[lane * kDuStride + 2 * tt]);
+      const float4* src = reinterpret_cast<const float4*>(&s_du[lane * kDuStrideL + 2 * (h0 + tt)]);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const float4 q = src[k];
@@ -322,10 +432,9 @@ __global__ void __launch_bounds__(64 * NW)
       }
       float acc[8];
       float dA_head[HEAD ? 8 : 1];
+      if constexpr (HEAD) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        acc[k] = 0.0f;
-        if constexpr (HEAD) dA_head[k] = __builtin_amdgcn_exp2f(dl[k] * ap[0]);
+        for (int k = 0; k < 8; ++k) dA_head[k] = __builtin_amdgcn_exp2f(dl[k] * ap[0]);
       }
       if constexpr (SUMMARY) {
         float s8 = 0.0f;
@@ -334,27 +443,28 @@ __global__ void __launch_bounds__(64 * NW)
         dsum_total += (double)s8;
       }
 #pragma unroll
-      for (int jc = 0; jc < NS; jc += 4) {
-        // 16 (state, step) values per register: states n0+jc .. +3 and steps tt .. tt+3 (lo),
-        // tt+4 .. tt+7 (hi)
-        const int bc_off = (n0 + jc + (ri >> 2)) * kBcStride + tt + (ri & 3);
-        const float b_lo = s_B[bc_off], b_hi = s_B[bc_off + 4];
-        float c_lo = 0.0f, c_hi = 0.0f;
-        if constexpr (!SUMMARY) { c_lo = s_C[bc_off]; c_hi = s_C[bc_off + 4]; }
+      for (int j = 0; j < NS; ++j) {
+        // B and C of state n0 + j at steps tt .. tt+7: the same address in every lane
+        const float4* bq = reinterpret_cast<const float4*>(&s_B[(n0 + j) * kBcStrideL + h0 + tt]);
+        const float4 b0 = bq[0], b1 = bq[1];
+        const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        float cv[8];
+        if constexpr (!SUMMARY) {
+          const float4* cq = reinterpret_cast<const float4*>(&s_C[(n0 + j) * kBcStrideL + h0 + tt]);
+          const float4 c0 = cq[0], c1 = cq[1];
+          cv[0] = c0.x; cv[1] = c0.y; cv[2] = c0.z; cv[3] = c0.w;
+          cv[4] = c1.x; cv[5] = c1.y; cv[6] = c1.z; cv[7] = c1.w;
+        }
+        float dA[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
+          if constexpr (HEAD) dA[k] = dA_head[k];
+          else dA[k] = __builtin_amdgcn_exp2f(dl[k] * ap[j]);
+        }
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int slot = j * 4 + (k & 3);
-            float dA;
-            if constexpr (HEAD) dA = dA_head[k]; else dA = __builtin_amdgcn_exp2f(dl[k] * ap[jc + j]);
-            const float bb = row_bcast_k(k < 4 ? b_lo : b_hi, slot);
-            h[jc + j] = fmaf(dA, h[jc + j], u[k] * bb);
-            if constexpr (!SUMMARY) {
-              const float cc = row_bcast_k(k < 4 ? c_lo : c_hi, slot);
-              acc[k] = fmaf(cc, h[jc + j], acc[k]);
-            }
-          }
+        for (int k = 0; k < 8; ++k) {
+          h[j] = fmaf(dA[k], h[j], u[k] * bv[k]);
+          if constexpr (!SUMMARY) acc[k] = (j == 0) ? cv[k] * h[j] : fmaf(cv[k], h[j], acc[k]);
         }
       }
       if constexpr (!SUMMARY) {
@@ -363,43 +473,83 @@ __global__ void __launch_bounds__(64 * NW)
         dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
       }
     }
-    __syncthreads();
+  };
 
-    // ---- epilogue: y = (sum of partial readouts + D x) * silu(z)
-    if constexpr (!SUMMARY) {
+  // y = (sum of the partial readouts + D x) * silu(z) for half hf
+  auto epilogue = [&](int hf, int64_t t0, int tb_len, bool full) {
 #pragma unroll
-      for (int it = 0; it < IPT; ++it) {
-        const int item = tid + it * NT;
-        if (ITEMS % NT == 0 || item < ITEMS) {
-          const int r = item / CPR;
-          const int tl = (item % CPR) * V;
-          const int64_t dd = d0 + r;
-          const int cnt = max(0, min(V, tb_len - tl));
-          if (dd < p.dim && cnt > 0) {
-            const float Dd = Dm ? Dm[dd] : 0.0f;
-            float yv[V];
+    for (int it = 0; it < IPT; ++it) {
+      if (!ilive[it]) continue;
+      float yv[V];
 #pragma unroll
-            for (int e4 = 0; e4 < V; e4 += 4) {
-              float4 s4 = *reinterpret_cast<const float4*>(&s_part[r * kPartStride + tl + e4]);
+      for (int e4 = 0; e4 < V; e4 += 4) {
+        float4 s4 = *reinterpret_cast<const float4*>(&s_part[ir[it] * kPartStride + itl[it] + e4]);
 #pragma unroll
-              for (int ww = 1; ww < NW; ++ww) {
-                const float4 q = *reinterpret_cast<const float4*>(
-                    &s_part[(ww * kChannelsPerGroup + r) * kPartStride + tl + e4]);
-                s4.x += q.x; s4.y += q.y; s4.z += q.z; s4.w += q.w;
-              }
-              yv[e4] = s4.x; yv[e4 + 1] = s4.y; yv[e4 + 2] = s4.z; yv[e4 + 3] = s4.w;
-            }
-#pragma unroll
-            for (int e = 0; e < V; ++e) {
-              float yy = fmaf(Dd, xkeep[it][e], yv[e]);
-              if (has_z) yy *= silu_f32(zkeep[it][e]);
-              yv[e] = yy;
-            }
-            store_chunk<IO>(Y + b * p.y_sb + dd * p.y_sd, t0 + tl, cnt, vec_ok, yv);
-          }
+        for (int ww = 1; ww < NW; ++ww) {
+          const float4 q = *reinterpret_cast<const float4*>(
+              &s_part[(ww * kChannelsPerGroup + ir[it]) * kPartStride + itl[it] + e4]);
+          s4.x += q.x; s4.y += q.y; s4.z += q.z; s4.w += q.w;
         }
+        yv[e4] = s4.x; yv[e4 + 1] = s4.y; yv[e4 + 2] = s4.z; yv[e4 + 3] = s4.w;
+      }
+      float zv[V];
+      if constexpr (GATE) unpack16<IO>(zkeep[hf][it], zv);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        float yy = fmaf(iD[it], xkeep[hf][it][e], yv[e]);
+        if constexpr (GATE) yy *= silu_f32(zv[e]);
+        yv[e] = yy;
+      }
+      if (full) {
+        store_chunk<IO>(yrow[it], t0 + hf * kTB + itl[it], V, true, yv);
+      } else {
+        const int cnt = max(0, min(V, tb_len - itl[it]));
+        if (cnt > 0) store_chunk<IO>(yrow[it], t0 + hf * kTB + itl[it], cnt, false, yv);
       }
     }
+  };
+
+  // the two halves of a load tile whose prologue is in LDS
+  auto halves = [&](int64_t t0, int lt_len, bool full) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int h0 = hf * kTB;
+      if (h0 >= lt_len) break;
+      const int tb_len = min(kTB, lt_len - h0);
+      recurrence(h0, tb_len);
+      if constexpr (!SUMMARY) {
+        __syncthreads();  // partial readouts complete
+        epilogue(hf, t0, tb_len, full);
+        if (hf == 0 && kTB < lt_len) __syncthreads();  // the next half overwrites them
+      }
+    }
+  };
+
+  // ---- full load tiles, with the prefetch ring
+  const int64_t n_full = fast_ok ? (t_end - t_begin) / kLT : 0;
+  Raw raw[PF];
+#pragma unroll
+  for (int q = 0; q < PF; ++q)
+    if (q < n_full) fetch(raw[q], t_begin + q * kLT);
+  for (int64_t i = 0; i < n_full; i += PF) {
+#pragma unroll
+    for (int q = 0; q < PF; ++q) {
+      if (i + q >= n_full) break;
+      const int64_t t0 = t_begin + (i + q) * kLT;
+      prologue_full(raw[q]);
+      if (i + q + PF < n_full) fetch(raw[q], t0 + PF * kLT);
+      __syncthreads();
+      halves(t0, kLT, true);
+      __syncthreads();  // LDS tiles free for the next prologue
+    }
+  }
+  // ---- the rest: one partial tile, or every tile when rows do not allow 16-byte access
+  for (int64_t t0 = t_begin + n_full * kLT; t0 < t_end; t0 += kLT) {
+    const int lt_len = (int)min<int64_t>(kLT, t_end - t0);
+    prologue_partial(t0, lt_len);
+    __syncthreads();
+    halves(t0, lt_len, false);
+    __syncthreads();
   }
 
   if constexpr (SUMMARY) {
@@ -409,354 +559,6 @@ __global__ void __launch_bounds__(64 * NW)
       for (int j = 0; j < NS; ++j)
         if (n0 + j < p.N) hend[base * p.N + n0 + j] = h[j];
       if (w == 0) dsum[base] = (float)dsum_total;
-    }
-  }
-}
-
-// Sum of v over the four 16-lane rows, transposed over four steps: on return, row r of the
-// result holds the row-sum of p[r] (per lane position within the row). gfx950's
-// v_permlane32_swap exchanges the upper half of its first operand with the lower half of its
-// second; v_permlane16_swap exchanges the odd rows of the first with the even rows of the second.
-__device__ __forceinline__ float rows_transpose_sum4(float p0, float p1, float p2, float p3) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p2), false, false);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(p1), __float_as_uint(p3), false, false);
-  const float s02 = __uint_as_float(a[0]) + __uint_as_float(a[1]);  // rows: p0(0+2) p0(1+3) p2(0+2) p2(1+3)
-  const float s13 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
-  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
-  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
-}
-
-// One wavefront per workgroup: 16 channels x 4 rows. Lane (row, ci) owns channel d0 + ci and the
-// states [row*NS, row*NS + NS); the readout over the four rows is summed with cross-row lane
-// swaps, so wavefronts never wait for each other. Global loads of the next tile are issued as
-// soon as the current tile's raw registers have been consumed, and complete while the
-// recurrence runs.
-template <typename IO, int NS, bool HEAD, bool SUMMARY>
-__global__ void __launch_bounds__(64)
-    scan_rows_kernel(const IO* __restrict__ X, const IO* __restrict__ DL, const IO* __restrict__ Bm,
-                     const IO* __restrict__ Cm, const IO* __restrict__ Z, IO* __restrict__ Y,
-                     const float* __restrict__ Am, const float* __restrict__ Dm,
-                     const float* __restrict__ bias_p, float* __restrict__ hend,
-                     float* __restrict__ dsum, const ScanParams p) {
-  static_assert(NS % 4 == 0, "states are swept in chunks of four");
-  constexpr int CH = 16;       // channels per wavefront
-  constexpr int NP = 4 * NS;   // padded state count
-  constexpr int V = IoTraits<IO>::kVec;
-  constexpr int CPR = kTB / V;  // 16-byte chunks per row of a tile
-  constexpr int IPT = CH * CPR / 64;
-  constexpr int BPT = NP * CPR / 64;
-  static_assert(IPT >= 1 && BPT >= 1 && CH * CPR % 64 == 0 && NP * CPR % 64 == 0, "tile shape");
-  __shared__ __align__(16) float s_du[CH * kDuStride];
-  __shared__ __align__(16) float s_B[NP * kBcStride];
-  __shared__ __align__(16) float s_C[SUMMARY ? 4 : NP * kBcStride];
-  __shared__ __align__(16) float s_y[SUMMARY ? 4 : CH * kPartStride];
-
-  const int lane = threadIdx.x;
-  const int row = lane >> 4;
-  const int ci = lane & 15;
-  const int64_t gpb = (p.dim + CH - 1) / CH;
-  const int64_t b = blockIdx.x / gpb;
-  const int64_t d0 = (blockIdx.x % gpb) * CH;
-  const int seg = blockIdx.y;
-  const int64_t t_begin = (int64_t)seg * p.seg_len;
-  const int64_t t_end = min(p.L, t_begin + p.seg_len);
-  const bool fast_ok = p.vec_io != 0 && p.bc_vec != 0;
-  const bool has_z = !SUMMARY && Z != nullptr;
-  const bool softplus = p.softplus != 0;
-  const int64_t grp = d0 / (p.dim / p.ngroups);
-  const IO* __restrict__ Bg = Bm + b * p.B_sb + grp * p.B_sg;
-  const IO* __restrict__ Cg = Cm + b * p.C_sb + grp * p.C_sg;
-  const int n0 = row * NS;
-
-  // ---- per-lane constants of channel d = d0 + ci, states n0 .. n0 + NS - 1
-  const int64_t d = d0 + ci;
-  const bool live = d < p.dim;
-  float ap[HEAD ? 1 : NS];
-  if constexpr (HEAD) {
-    ap[0] = live ? Am[d / p.headdim] * kLog2e : 0.0f;
-  } else {
-#pragma unroll
-    for (int j = 0; j < NS; ++j)
-      ap[j] = (live && n0 + j < p.N) ? Am[d * p.N + n0 + j] * kLog2e : 0.0f;
-  }
-  float h[NS];
-#pragma unroll
-  for (int j = 0; j < NS; ++j) h[j] = 0.0f;
-  if (!SUMMARY && seg > 0 && live) {
-    const int64_t base = (b * p.dim + d) * p.nseg;
-    for (int s = 0; s < seg; ++s) {
-      const float ds = dsum[base + s];
-      const float* he = hend + (base + s) * p.N;
-#pragma unroll
-      for (int j = 0; j < NS; ++j) {
-        float a;
-        if constexpr (HEAD) a = ap[0]; else a = ap[j];
-        if (n0 + j < p.N) h[j] = __builtin_amdgcn_exp2f(a * ds) * h[j] + he[n0 + j];
-      }
-    }
-  }
-  double dsum_total = 0.0;
-
-  // ---- this lane's prologue/epilogue items, fixed for the whole segment: io item it covers
-  // channel row ir[it], steps itl[it] .. +V of each tile; B/C item it covers state bn[it]
-  const IO* xrow[IPT];
-  const IO* drow_p[IPT];
-  const IO* zrow[IPT];
-  IO* yrow[IPT];
-  float ibias[IPT], iD[IPT];
-  int ir[IPT], itl[IPT];
-  bool ilive[IPT];
-#pragma unroll
-  for (int it = 0; it < IPT; ++it) {
-    const int item = lane + it * 64;
-    ir[it] = item / CPR;
-    itl[it] = (item % CPR) * V;
-    const int64_t dd = d0 + ir[it];
-    ilive[it] = dd < p.dim;
-    const int64_t dv = min(dd, p.dim - 1);  // rows past dim read a valid row (never stored)
-    const int64_t dr = HEAD ? dv / p.headdim : dv;
-    xrow[it] = X + b * p.x_sb + dv * p.x_sd;
-    drow_p[it] = DL + b * p.dl_sb + dr * p.dl_sd;
-    zrow[it] = has_z ? Z + b * p.z_sb + dv * p.z_sd : nullptr;
-    yrow[it] = SUMMARY ? nullptr : Y + b * p.y_sb + dv * p.y_sd;
-    ibias[it] = bias_p ? bias_p[dr] : 0.0f;
-    iD[it] = (!SUMMARY && Dm) ? Dm[dv] : 0.0f;
-  }
-  const IO* brow[BPT];
-  const IO* crow[BPT];
-  int bn[BPT], btl[BPT];
-#pragma unroll
-  for (int it = 0; it < BPT; ++it) {
-    const int item = lane + it * 64;
-    bn[it] = item / CPR;
-    btl[it] = (item % CPR) * V;
-    const int64_t nn = min<int64_t>(bn[it], p.N - 1);
-    brow[it] = Bg + nn * p.B_sn;
-    crow[it] = SUMMARY ? nullptr : Cg + nn * p.C_sn;
-  }
-
-  // raw 16-byte words of the next full tile
-  u32x4 rx[IPT], rd[IPT], rz[IPT], rb[BPT], rc[BPT];
-  auto fetch = [&](int64_t t0) {
-#pragma unroll
-    for (int it = 0; it < IPT; ++it) {
-      rx[it] = load16<true>(xrow[it] + t0 + itl[it]);
-      rd[it] = load16<true>(drow_p[it] + t0 + itl[it]);
-      if (has_z) rz[it] = load16<true>(zrow[it] + t0 + itl[it]);
-    }
-#pragma unroll
-    for (int it = 0; it < BPT; ++it) {
-      rb[it] = load16<false>(brow[it] + t0 + btl[it]);
-      if (!SUMMARY) rc[it] = load16<false>(crow[it] + t0 + btl[it]);
-    }
-  };
-  if (fast_ok && t_end - t_begin >= kTB) fetch(t_begin);
-
-  float xkeep[IPT][V];
-  u32x4 zkeep[IPT];
-
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += kTB) {
-    const int tb_len = (int)min<int64_t>(kTB, t_end - t0);
-    const bool full = fast_ok && tb_len == kTB;
-
-    // ---- prologue: delta, u = delta * x into LDS; B, C tiles into LDS (fp32)
-    if (full) {
-#pragma unroll
-      for (int it = 0; it < IPT; ++it) {
-        float dv[V];
-        unpack16<IO>(rx[it], xkeep[it]);
-        unpack16<IO>(rd[it], dv);
-        zkeep[it] = rz[it];
-        float du[2 * V];
-        if (softplus) {
-#pragma unroll
-          for (int e = 0; e < V; ++e) {
-            const float dl = softplus_f32(dv[e] + ibias[it]);
-            du[2 * e] = dl;
-            du[2 * e + 1] = dl * xkeep[it][e];
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < V; ++e) {
-            const float dl = dv[e] + ibias[it];
-            du[2 * e] = dl;
-            du[2 * e + 1] = dl * xkeep[it][e];
-          }
-        }
-        float4* dst = reinterpret_cast<float4*>(&s_du[ir[it] * kDuStride + 2 * itl[it]]);
-#pragma unroll
-        for (int k = 0; k < V / 2; ++k)
-          dst[k] = make_float4(du[4 * k], du[4 * k + 1], du[4 * k + 2], du[4 * k + 3]);
-      }
-#pragma unroll
-      for (int it = 0; it < BPT; ++it) {
-        float bv[V], cv[V];
-        unpack16<IO>(rb[it], bv);
-        if constexpr (!SUMMARY) unpack16<IO>(rc[it], cv);
-        if (bn[it] >= p.N) {
-#pragma unroll
-          for (int e = 0; e < V; ++e) { bv[e] = 0.0f; cv[e] = 0.0f; }
-        }
-        float4* db = reinterpret_cast<float4*>(&s_B[bn[it] * kBcStride + btl[it]]);
-#pragma unroll
-        for (int k = 0; k < V / 4; ++k)
-          db[k] = make_float4(bv[4 * k], bv[4 * k + 1], bv[4 * k + 2], bv[4 * k + 3]);
-        if constexpr (!SUMMARY) {
-          float4* dc = reinterpret_cast<float4*>(&s_C[bn[it] * kBcStride + btl[it]]);
-#pragma unroll
-          for (int k = 0; k < V / 4; ++k)
-            dc[k] = make_float4(cv[4 * k], cv[4 * k + 1], cv[4 * k + 2], cv[4 * k + 3]);
-        }
-      }
-      // the raw registers are free: start loading the next tile
-      if (t_end - (t0 + kTB) >= kTB) fetch(t0 + kTB);
-    } else {
-      // partial tile or unaligned rows: guarded element loads; padding steps and channels get
-      // delta = u = 0 (dA = 1, dB x = 0) and B = C = 0
-#pragma unroll
-      for (int it = 0; it < IPT; ++it) {
-        const int cnt = max(0, min(V, tb_len - itl[it]));
-        const int c2 = ilive[it] ? cnt : 0;
-        float dv[V], zv[V];
-        load_chunk<IO, true>(xrow[it], t0 + itl[it], c2, false, xkeep[it]);
-        load_chunk<IO, true>(drow_p[it], t0 + itl[it], c2, false, dv);
-        if (has_z) load_chunk<IO, true>(zrow[it], t0 + itl[it], c2, false, zv);
-        else {
-#pragma unroll
-          for (int e = 0; e < V; ++e) zv[e] = 0.0f;
-        }
-        uint32_t zw[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          if constexpr (V == 8) zw[k] = pack_bf16x2(zv[2 * k], zv[2 * k + 1]);
-          else zw[k] = __float_as_uint(zv[k]);
-        }
-        zkeep[it] = u32x4{zw[0], zw[1], zw[2], zw[3]};
-        float du[2 * V];
-#pragma unroll
-        for (int e = 0; e < V; ++e) {
-          const float v = dv[e] + ibias[it];
-          float dl = softplus ? softplus_f32(v) : v;
-          if (e >= c2) dl = 0.0f;
-          du[2 * e] = dl;
-          du[2 * e + 1] = dl * xkeep[it][e];
-        }
-        float4* dst = reinterpret_cast<float4*>(&s_du[ir[it] * kDuStride + 2 * itl[it]]);
-#pragma unroll
-        for (int k = 0; k < V / 2; ++k)
-          dst[k] = make_float4(du[4 * k], du[4 * k + 1], du[4 * k + 2], du[4 * k + 3]);
-      }
-#pragma unroll
-      for (int it = 0; it < BPT; ++it) {
-        const int cnt = bn[it] < p.N ? max(0, min(V, tb_len - btl[it])) : 0;
-        float bv[V], cv[V];
-        load_chunk<IO, false>(brow[it], t0 + btl[it], cnt, false, bv);
-        if constexpr (!SUMMARY) load_chunk<IO, false>(crow[it], t0 + btl[it], cnt, false, cv);
-        float4* db = reinterpret_cast<float4*>(&s_B[bn[it] * kBcStride + btl[it]]);
-#pragma unroll
-        for (int k = 0; k < V / 4; ++k)
-          db[k] = make_float4(bv[4 * k], bv[4 * k + 1], bv[4 * k + 2], bv[4 * k + 3]);
-        if constexpr (!SUMMARY) {
-          float4* dc = reinterpret_cast<float4*>(&s_C[bn[it] * kBcStride + btl[it]]);
-#pragma unroll
-          for (int k = 0; k < V / 4; ++k)
-            dc[k] = make_float4(cv[4 * k], cv[4 * k + 1], cv[4 * k + 2], cv[4 * k + 3]);
-        }
-      }
-      if (fast_ok && t0 + kTB < t_end && t_end - (t0 + kTB) >= kTB) fetch(t0 + kTB);
-    }
-    __syncthreads();
-
-    // ---- recurrence over the tile
-    for (int tt = 0; tt < tb_len; tt += 8) {
-      float dl[8], u[8];
-      const float4* src = reinterpret_cast<const float4*>(&s_du[ci * kDuStride + 2 * tt]);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float4 q = src[k];
-        dl[2 * k] = q.x; u[2 * k] = q.y; dl[2 * k + 1] = q.z; u[2 * k + 1] = q.w;
-      }
-      float acc[8];
-      float dA_head[HEAD ? 8 : 1];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        acc[k] = 0.0f;
-        if constexpr (HEAD) dA_head[k] = __builtin_amdgcn_exp2f(dl[k] * ap[0]);
-      }
-      if constexpr (SUMMARY) {
-        float s8 = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) s8 += dl[k];
-        dsum_total += (double)s8;
-      }
-#pragma unroll
-      for (int jc = 0; jc < NS; jc += 4) {
-        // 16 (state, step) values per register and row: states n0+jc .. +3, steps tt .. tt+3
-        // (lo) and tt+4 .. tt+7 (hi)
-        const int bc_off = (n0 + jc + (ci >> 2)) * kBcStride + tt + (ci & 3);
-        const float b_lo = s_B[bc_off], b_hi = s_B[bc_off + 4];
-        float c_lo = 0.0f, c_hi = 0.0f;
-        if constexpr (!SUMMARY) { c_lo = s_C[bc_off]; c_hi = s_C[bc_off + 4]; }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int slot = j * 4 + (k & 3);
-            float dA;
-            if constexpr (HEAD) dA = dA_head[k]; else dA = __builtin_amdgcn_exp2f(dl[k] * ap[jc + j]);
-            const float bb = row_bcast_k(k < 4 ? b_lo : b_hi, slot);
-            h[jc + j] = fmaf(dA, h[jc + j], u[k] * bb);
-            if constexpr (!SUMMARY) {
-              const float cc2 = row_bcast_k(k < 4 ? c_lo : c_hi, slot);
-              acc[k] = fmaf(cc2, h[jc + j], acc[k]);
-            }
-          }
-        }
-      }
-      if constexpr (!SUMMARY) {
-        const float y_lo = rows_transpose_sum4(acc[0], acc[1], acc[2], acc[3]);
-        const float y_hi = rows_transpose_sum4(acc[4], acc[5], acc[6], acc[7]);
-        s_y[ci * kPartStride + tt + row] = y_lo;
-        s_y[ci * kPartStride + tt + 4 + row] = y_hi;
-      }
-    }
-    __syncthreads();
-
-    // ---- epilogue: y = (readout + D x) * silu(z), 16-byte stores
-    if constexpr (!SUMMARY) {
-#pragma unroll
-      for (int it = 0; it < IPT; ++it) {
-        float yv[V];
-#pragma unroll
-        for (int e4 = 0; e4 < V; e4 += 4) {
-          const float4 s4 = *reinterpret_cast<const float4*>(&s_y[ir[it] * kPartStride + itl[it] + e4]);
-          yv[e4] = s4.x; yv[e4 + 1] = s4.y; yv[e4 + 2] = s4.z; yv[e4 + 3] = s4.w;
-        }
-        float zv[V];
-        unpack16<IO>(zkeep[it], zv);
-#pragma unroll
-        for (int e = 0; e < V; ++e) {
-          float yy = fmaf(iD[it], xkeep[it][e], yv[e]);
-          if (has_z) yy *= silu_f32(zv[e]);
-          yv[e] = yy;
-        }
-        if (full) {
-          if (ilive[it]) store_chunk<IO>(yrow[it], t0 + itl[it], V, true, yv);
-        } else {
-          const int cnt = max(0, min(V, tb_len - itl[it]));
-          if (ilive[it] && cnt > 0) store_chunk<IO>(yrow[it], t0 + itl[it], cnt, false, yv);
-        }
-      }
-    }
-  }
-
-  if constexpr (SUMMARY) {
-    if (live) {
-      const int64_t base = (b * p.dim + d) * p.nseg + seg;
-#pragma unroll
-      for (int j = 0; j < NS; ++j)
-        if (n0 + j < p.N) hend[base * p.N + n0 + j] = h[j];
-      if (row == 0) dsum[base] = (float)dsum_total;
     }
   }
 }
@@ -775,41 +577,30 @@ static hipError_t launch_cfg(const ScanParams& p, hipStream_t stream) {
   const int64_t groups = p.batch * p.groups_per_batch;
   if (p.nseg > 1) {
     const dim3 grid_sum((unsigned)groups, (unsigned)(p.nseg - 1));
-    hipLaunchKernelGGL((scan_fwd_kernel<IO, NS, NW, HEAD, true>), grid_sum, block, 0, stream,
-                       SCAN_ARGS(p));
+    hipLaunchKernelGGL((scan_fwd_kernel<IO, NS, NW, HEAD, true, false>), grid_sum, block, 0,
+                       stream, SCAN_ARGS(p));
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const dim3 grid((unsigned)groups, (unsigned)p.nseg);
-  hipLaunchKernelGGL((scan_fwd_kernel<IO, NS, NW, HEAD, false>), grid, block, 0, stream,
-                     SCAN_ARGS(p));
-  return hipGetLastError();
-}
-
-template <typename IO, int NS, bool HEAD>
-static hipError_t launch_rows(const ScanParams& p, hipStream_t stream) {
-  const dim3 block(64);
-  const int64_t groups = p.batch * ((p.dim + 15) / 16);
-  if (p.nseg > 1) {
-    const dim3 grid_sum((unsigned)groups, (unsigned)(p.nseg - 1));
-    hipLaunchKernelGGL((scan_rows_kernel<IO, NS, HEAD, true>), grid_sum, block, 0, stream,
+  if (p.z)
+    hipLaunchKernelGGL((scan_fwd_kernel<IO, NS, NW, HEAD, false, true>), grid, block, 0, stream,
                        SCAN_ARGS(p));
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  const dim3 grid((unsigned)groups, (unsigned)p.nseg);
-  hipLaunchKernelGGL((scan_rows_kernel<IO, NS, HEAD, false>), grid, block, 0, stream,
-                     SCAN_ARGS(p));
+  else
+    hipLaunchKernelGGL((scan_fwd_kernel<IO, NS, NW, HEAD, false, false>), grid, block, 0, stream,
+                       SCAN_ARGS(p));
   return hipGetLastError();
 }
 
 template <typename IO, bool HEAD>
 static hipError_t launch_n(const ScanParams& p, hipStream_t stream) {
   const int64_t N = p.N;
-  if (N <= 16) return launch_rows<IO, 4, HEAD>(p, stream);
-  if (N <= 32) return launch_rows<IO, 8, HEAD>(p, stream);
+  if (N <= 4) return launch_cfg<IO, 1, 4, HEAD>(p, stream);
+  if (N <= 8) return launch_cfg<IO, 2, 4, HEAD>(p, stream);
+  if (N <= 16) return launch_cfg<IO, 4, 4, HEAD>(p, stream);
+  if (N <= 32) return launch_cfg<IO, 8, 4, HEAD>(p, stream);
   if (N <= 64) return launch_cfg<IO, 16, 4, HEAD>(p, stream);
-  return launch_cfg<IO, 16, 8, HEAD>(p, stream);  // N <= 128 (checked by the caller)
+  return launch_cfg<IO, 32, 4, HEAD>(p, stream);  // N <= 128 (checked by the caller)
 }
 
 hipError_t launch_scan_fwd(const ScanParams& p, bool bf16, bool head, hipStream_t stream) {
@@ -817,9 +608,11 @@ hipError_t launch_scan_fwd(const ScanParams& p, bool bf16, bool head, hipStream_
   return head ? launch_n<float, true>(p, stream) : launch_n<float, false>(p, stream);
 }
 
-int time_tile() { return kTB; }
+// Segments along L start at multiples of this many steps.
+int time_tile() { return kLT; }
 
 // Channels per workgroup of the kernel that launch_scan_fwd picks for dstate N.
-int channels_per_group(int64_t N) { return N <= 32 ? 16 : kChannelsPerGroup; }
+int channels_per_group(int64_t) { return kChannelsPerGroup; }
+int waves_per_group(int64_t) { return 4; }
 
 }  // namespace ssm
