@@ -7,9 +7,12 @@ every stage of the scan runs inside it. Inputs are generated once, copied to HBM
 resident; the timed region covers exactly ``--steps`` calls between two device
 synchronisations, timed with HIP events on the stream the kernels are launched on.
 
-Prints one JSON line: throughput in Gtoken*channel/s, the roofline of the dominant kernel
-(algorithmic bytes per launch / average launch time, against the 8 TB/s HBM peak), and the fp64
-CPU oracle timed on a bounded sample of the same workload on the host cores.
+Prints one JSON line: throughput in Gtoken*channel/s; the roofline of the scan kernel, which is
+bound by fp32 VALU and transcendental issue, not by HBM (algorithmic flops per launch / average
+launch time, against the peak of the same instruction mix at full issue, see ``alu_model``); the
+HBM figures beside it (algorithmic bytes and, when a counter profile of the current kernel source
+is committed, counted bytes, against the 8 TB/s peak); and the fp64 CPU oracle timed on the host
+cores over whole batch entries of the same workload.
 
 ``--copy-calibration`` runs only a plain device copy of a known size (for scaling the
 FETCH_SIZE / WRITE_SIZE counters of a profiler run).
@@ -68,45 +71,83 @@ def device_inputs(cfg, torch):
     return dev
 
 
+def alu_model(cfg):
+    """Minimal fp32 instruction stream of the method per token*channel: (flops, SIMD cycles).
+
+    A wavefront-wide (64-lane) fp32 add/mul/fma/max issues every 2 cycles on a SIMD (the
+    157.3 TFLOP/s vector rate: 256 CUs x 4 SIMDs x 64 lanes x 2 flops / 2 cycles x 2.4 GHz);
+    exp2, log2 and rcp issue at quarter rate, every 8 cycles. Flops count an fma as 2 and every
+    other operation, transcendentals included, as 1.
+      per state update (t, channel, n): delta*a, exp2, u*B, h fma, readout fma -> 7 flops, 16 cyc
+        (head mode: delta*a and exp2 once per (t, head) instead)
+      per (t, channel): bias add (1, 2), softplus (10, 30: |v|*log2e, exp2, 1+e, log2, two
+        subtractions of the log1p correction, fma, max, add), u = delta*x (1, 2), D skip fma
+        (2, 2), silu gate (6, 24: z*log2e, exp2, 1+e, rcp, z*r, y*g)
+    Unpacking and packing of bf16 are not counted (they are not arithmetic of the method).
+    """
+    valu, trans = 2, 8
+    head = cfg.a_mode == "head"
+    rows_per_ch = 1.0 / cfg.headdim if head else 1.0
+    fl = cy = 0.0
+    if head:
+        fl += cfg.N * 5 + 2 * rows_per_ch
+        cy += cfg.N * 3 * valu + (valu + trans) * rows_per_ch
+    else:
+        fl += cfg.N * 7
+        cy += cfg.N * (4 * valu + trans)
+    if cfg.has_bias:
+        fl += 1 * rows_per_ch
+        cy += valu * rows_per_ch
+    if cfg.softplus:
+        fl += 10 * rows_per_ch
+        cy += (7 * valu + 2 * trans) * rows_per_ch
+    fl += 1
+    cy += valu
+    if cfg.has_D:
+        fl += 2
+        cy += valu
+    if cfg.gate:
+        fl += 6
+        cy += 4 * valu + 2 * trans
+    return fl, cy
+
+
+SIMDS = 256 * 4
+CLOCK_HZ = 2.4e9
+
+
+def alu_peak_tflops(cfg) -> float:
+    fl, cy = alu_model(cfg)
+    return fl * 64 / cy * SIMDS * CLOCK_HZ / 1e12
+
+
 def cpu_baseline(cfg, budget_s: float):
-    """The fp64 oracle, as it stands, on a sample of whole channels of the workload (batch 0,
-    channels 0..S-1, all L steps), S grown until the run takes about ``budget_s`` seconds."""
-    import numpy as np
+    """The fp64 oracle, as it stands, over whole batch entries of the workload (inputs of one
+    entry generated untimed, then the oracle timed on them), until every entry is done or the
+    time budget is spent."""
     import oracle
     import ssmgen
     threads = oracle.cpu_threads()
-    L = cfg.L
-
-    def run(nch):
-        sub = ssmgen.with_shape(cfg, batch=1, dim=nch)
-        inputs = {}
-        for name in sub.shapes():
-            # channels 0..nch-1 of batch 0 are the first rows of every per-channel tensor
-            full_shape = sub.shapes()[name]
-            d = sub.dist_of(name)
-            count = int(np.prod(full_shape))
-            inputs[name] = ssmgen.fill(cfg.seed, ssmgen.TENSOR_IDS[name], d.kind, d.p0, d.p1,
-                                       count, sub.dtype_of(name)).reshape(full_shape)
+    spent, done = 0.0, 0
+    for b in range(cfg.batch):
+        inputs = ssmgen.make_batch_entry(cfg, b)
+        one = ssmgen.with_shape(cfg, batch=1)
         t0 = time.perf_counter()
-        oracle.scan_inputs(inputs, sub, nthreads=threads)
-        return time.perf_counter() - t0
-
-    nch = max(threads, 16)
-    dt = run(nch)
-    while dt < budget_s / 4 and nch < cfg.dim:
-        nch = min(cfg.dim, nch * 4)
-        dt = run(nch)
-    if dt < budget_s / 2 and nch < cfg.dim:
-        nch = min(cfg.dim, int(nch * budget_s / max(dt, 1e-3)))
-        dt = run(nch)
+        oracle.scan_inputs(inputs, one, nthreads=threads)
+        spent += time.perf_counter() - t0
+        done += 1
+        del inputs
+        if spent >= budget_s:
+            break
+    tokch = done * cfg.dim * cfg.L
     return {
-        "value": round(nch * L / dt / 1e9, 6),
+        "value": round(tokch / spent / 1e9, 6),
         "unit": "Gtoken\u00b7channel/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{nch} of {cfg.batch * cfg.dim} channels (batch 0, channels 0..{nch - 1}, "
-                  f"all {L} steps): {nch * L * cfg.N / 1e9:.3f} G fp64 state updates in "
-                  f"{dt:.2f} s",
+        "sample": (f"batch entries 0..{done - 1} of {cfg.batch} ({done * cfg.dim} channels x "
+                   f"{cfg.L} steps, {tokch * cfg.N / 1e9:.2f} G fp64 state updates) in "
+                   f"{spent:.2f} s; input generation untimed"),
     }
 
 
@@ -118,7 +159,6 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 skips it)")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--check", action="store_true", help="compare sampled channels with the oracle")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -171,29 +211,29 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
-    for _ in range(args.steps):
+    for s_ev, e_ev in ev:
+        s_ev.record(stream)
         step()
+        e_ev.record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
+    per = sorted(s_ev.elapsed_time(e_ev) for s_ev, e_ev in ev)
+    pct = lambda q: per[min(len(per) - 1, int(q * (len(per) - 1) + 0.5))]
 
-    check = None
-    if args.check:
-        import numpy as np
-        import oracle
-        sys.path.insert(0, os.path.join(ROOT, "tests"))
-        from scan_cases import channel_oracle, sample_channels
-        worst = 0.0
-        for b, d in sample_channels(cfg, 8):
-            yg = y[b, d].float().cpu().numpy().astype(np.float64)
-            worst = max(worst, oracle.rel_err(yg, channel_oracle(cfg, b, d)))
-        check = worst
-
+    # one launch per step when the sequence is not split along L (no workspace needed)
+    launches = 1 if ws_bytes == 0 else 2
     tokch = cfg.tokch
     alg_bytes = cfg.algorithmic_bytes()
-    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    fl, _ = alu_model(cfg)
+    alg_flops = fl * tokch
+    peak = alu_peak_tflops(cfg)
+    launch_ms = ms if launches == 1 else None
+    achieved = alg_flops / (launch_ms * 1e-3) / 1e12 if launch_ms else None
     traffic = traffic_from_profile("mamba14b_layer")
     out = {
         "metric": "selective-scan Gtoken\u00b7channel/s and achieved HBM GB/s vs peak, 1 MI355X",
@@ -215,18 +255,26 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "bound": "alu",
+            "achieved": round(achieved, 2) if achieved else None,
+            "peak": round(peak, 2),
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4) if achieved else None,
             "traffic": traffic,
         },
-        "algorithmic_bytes_per_step": alg_bytes,
+        "hbm": {
+            "algorithmic_bytes": alg_bytes,
+            "algorithmic_GBs": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
+            "peak_GBs": HBM_PEAK_GBS,
+            "frac_of_peak": round(alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "counter_GBs": round(traffic / (launch_ms * 1e-3) / 1e9, 1)
+            if (traffic and launch_ms) else None,
+        },
+        "step_ms": {"p10": round(pct(0.1), 5), "median": round(pct(0.5), 5),
+                    "p90": round(pct(0.9), 5)},
+        "launches_per_step": launches,
         "kernel_source": kernel_source_hash(),
     }
-    if check is not None:
-        out["sampled_max_rel_err"] = check
     if args.cpu_budget > 0:
         del dev, y
         torch.cuda.empty_cache()

@@ -238,6 +238,21 @@ def make_channel(cfg: ScanConfig, b: int, d: int) -> Dict[str, np.ndarray]:
     return out
 
 
+def make_batch_entry(cfg: ScanConfig, b: int, nthreads: Optional[int] = None
+                     ) -> Dict[str, np.ndarray]:
+    """Inputs of batch entry ``b`` alone (shapes of the batch-1 problem), regenerated from the
+    streams at their offsets; per-channel parameters (A, D, delta_bias) are whole."""
+    out = {}
+    one = with_shape(cfg, batch=1)
+    for name, shp in one.shapes().items():
+        d = cfg.dist_of(name)
+        count = int(np.prod(shp))
+        start = b * count if name in ("x", "delta", "B", "C", "z") else 0
+        out[name] = fill(cfg.seed, TENSOR_IDS[name], d.kind, d.p0, d.p1, count,
+                         cfg.dtype_of(name), start, nthreads).reshape(shp)
+    return out
+
+
 def with_shape(cfg: ScanConfig, **kw) -> ScanConfig:
     """A copy of ``cfg`` with some fields replaced (same recipe, different sizes)."""
     return replace(cfg, **kw)

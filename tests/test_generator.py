@@ -97,3 +97,16 @@ def test_channel_slice_matches_full_tensors():
     assert np.array_equal(ch["B"][0, 0], full["B"][b, 0])
     assert ch["A"][0] == full["A"][d // 64] and ch["D"][0] == full["D"][d]
     assert ch["delta_bias"][0] == full["delta_bias"][d // 64]
+
+
+def test_batch_entry_is_a_slice_of_the_whole_tensors():
+    cfg = ssmgen.with_shape(ssmgen.CONFIGS[1], batch=3, dim=16, L=40)
+    whole = ssmgen.make_inputs(cfg)
+    for b in range(cfg.batch):
+        one = ssmgen.make_batch_entry(cfg, b)
+        assert set(one) == set(whole)
+        for name, arr in one.items():
+            if name in ("x", "delta", "B", "C", "z"):
+                assert np.array_equal(arr[0], whole[name][b]), name
+            else:
+                assert np.array_equal(arr, whole[name]), name
