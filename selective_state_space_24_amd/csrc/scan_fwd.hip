@@ -39,6 +39,7 @@ constexpr int kPartStride = kTB + 4;     // floats per channel row of partial re
 #define SSM_PREFETCH_TILES 1
 #endif
 constexpr int kPrefetch = SSM_PREFETCH_TILES;  // load tiles fetched ahead per workgroup
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 typedef uint16_t bf16_bits;
 typedef float float2v __attribute__((ext_vector_type(2)));
@@ -171,7 +172,9 @@ __device__ __forceinline__ float silu_f32(float z) {
 // HEAD: one A and one delta per head; SUMMARY: the segment summary pass (no readout, no y);
 // GATE: y is multiplied by silu(z).
 template <typename IO, int NS, int NW, bool HEAD, bool SUMMARY, bool GATE>
-__global__ void __launch_bounds__(64 * NW)
+// Two workgroups fit a CU's LDS, so each SIMD holds at most two of these wavefronts: the second
+// launch bound lets the compiler use the registers that this occupancy leaves.
+__global__ void __launch_bounds__(64 * NW, 2)
     scan_fwd_kernel(const IO* __restrict__ X, const IO* __restrict__ DL, const IO* __restrict__ Bm,
                     const IO* __restrict__ Cm, const IO* __restrict__ Z, IO* __restrict__ Y,
                     const float* __restrict__ Am, const float* __restrict__ Dm,
@@ -188,8 +191,9 @@ __global__ void __launch_bounds__(64 * NW)
   constexpr int BPT = (BC_ITEMS + NT - 1) / NT;
   static_assert(!(SUMMARY && GATE), "the summary pass has no gate");
   __shared__ __align__(16) float s_du[kChannelsPerGroup * kDuStrideL];
-  __shared__ __align__(16) float s_B[NP * kBcStrideL];
-  __shared__ __align__(16) float s_C[SUMMARY ? 4 : NP * kBcStrideL];
+  __shared__ __align__(16) float s_bc[(SUMMARY ? 1 : 2) * NP * kBcStrideL];
+  float* const s_B = s_bc;
+  float* const s_C = s_bc + (SUMMARY ? 0 : NP * kBcStrideL);
   __shared__ __align__(16) float s_part[SUMMARY ? 4 : NW * kChannelsPerGroup * kPartStride];
 
   const int tid = threadIdx.x;
@@ -284,7 +288,7 @@ __global__ void __launch_bounds__(64 * NW)
   struct Raw {
     u32x4 x[2][IPT], d[2][IPT], z[2][IPT], b[2][BPT], c[2][BPT];
   };
-  auto fetch = [&](Raw& r, int64_t t0) {
+  auto fetch = [&](Raw& r, int64_t t0) __attribute__((always_inline)) {
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
       if (!iown[it]) continue;
@@ -346,7 +350,7 @@ __global__ void __launch_bounds__(64 * NW)
   };
 
   // prologue of a full load tile from the raw registers
-  auto prologue_full = [&](const Raw& rw) {
+  auto prologue_full = [&](const Raw& rw) __attribute__((always_inline)) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
@@ -375,7 +379,7 @@ __global__ void __launch_bounds__(64 * NW)
 
   // prologue of a partial load tile (or unaligned rows) with guarded element loads; padding
   // steps get delta = u = 0 (dA = 1, dB x = 0) and padding states B = C = 0
-  auto prologue_partial = [&](int64_t t0, int lt_len) {
+  auto prologue_partial = [&](int64_t t0, int lt_len) __attribute__((always_inline)) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const int tb_len = max(0, min(kTB, lt_len - hf * kTB));
@@ -420,63 +424,151 @@ __global__ void __launch_bounds__(64 * NW)
     }
   };
 
-  // the recurrence over steps [h0, h0 + tb_len) of the load tile: lane = channel
-  auto recurrence = [&](int h0, int tb_len) {
-    for (int tt = 0; tt < tb_len; tt += 8) {
-      float dl[8], u[8];
-      const float4* src = reinterpret_cast<const float4*>(&s_du[lane * kDuStrideL + 2 * (h0 + tt)]);
+  // the recurrence over steps [h0, h0 + tb_len) of the load tile: lane = channel.
+  // A block is 8 steps: this lane's (delta, u) pairs and, for each of the wavefront's states,
+  // B and C at those steps (the same values in every lane, read with wave-uniform addresses).
+  struct Blk {
+    f32x4 du[4];
+    f32x4 bc[NS][SUMMARY ? 2 : 4];
+  };
+  auto load_blk = [&](Blk& k, int h0, int tt) __attribute__((always_inline)) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(&s_du[lane * kDuStrideL + 2 * (h0 + tt)]);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float4 q = src[k];
-        dl[2 * k] = q.x; u[2 * k] = q.y; dl[2 * k + 1] = q.z; u[2 * k + 1] = q.w;
-      }
-      float acc[8];
-      float dA_head[HEAD ? 8 : 1];
-      if constexpr (HEAD) {
+    for (int q = 0; q < 4; ++q) k.du[q] = src[q];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) dA_head[k] = __builtin_amdgcn_exp2f(dl[k] * ap[0]);
-      }
-      if constexpr (SUMMARY) {
-        float s8 = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) s8 += dl[k];
-        dsum_total += (double)s8;
-      }
-#pragma unroll
-      for (int j = 0; j < NS; ++j) {
-        // B and C of state n0 + j at steps tt .. tt+7: the same address in every lane
-        const float4* bq = reinterpret_cast<const float4*>(&s_B[(n0 + j) * kBcStrideL + h0 + tt]);
-        const float4 b0 = bq[0], b1 = bq[1];
-        const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-        float cv[8];
-        if constexpr (!SUMMARY) {
-          const float4* cq = reinterpret_cast<const float4*>(&s_C[(n0 + j) * kBcStrideL + h0 + tt]);
-          const float4 c0 = cq[0], c1 = cq[1];
-          cv[0] = c0.x; cv[1] = c0.y; cv[2] = c0.z; cv[3] = c0.w;
-          cv[4] = c1.x; cv[5] = c1.y; cv[6] = c1.z; cv[7] = c1.w;
-        }
-        float dA[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          if constexpr (HEAD) dA[k] = dA_head[k];
-          else dA[k] = __builtin_amdgcn_exp2f(dl[k] * ap[j]);
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          h[j] = fmaf(dA[k], h[j], u[k] * bv[k]);
-          if constexpr (!SUMMARY) acc[k] = (j == 0) ? cv[k] * h[j] : fmaf(cv[k], h[j], acc[k]);
-        }
-      }
+    for (int j = 0; j < NS; ++j) {
+      const f32x4* bq = reinterpret_cast<const f32x4*>(&s_B[(n0 + j) * kBcStrideL + h0 + tt]);
+      k.bc[j][0] = bq[0];
+      k.bc[j][1] = bq[1];
       if constexpr (!SUMMARY) {
-        float4* dst = reinterpret_cast<float4*>(&s_part[(w * kChannelsPerGroup + lane) * kPartStride + tt]);
-        dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        const f32x4* cq = reinterpret_cast<const f32x4*>(&s_C[(n0 + j) * kBcStrideL + h0 + tt]);
+        k.bc[j][2] = cq[0];
+        k.bc[j][3] = cq[1];
       }
+    }
+  };
+  auto comp_blk = [&](const Blk& k, int tt) __attribute__((always_inline)) {
+    float dl[8], u[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      dl[2 * q] = k.du[q].x; u[2 * q] = k.du[q].y;
+      dl[2 * q + 1] = k.du[q].z; u[2 * q + 1] = k.du[q].w;
+    }
+    float acc[8];
+    float dA_head[HEAD ? 8 : 1];
+    if constexpr (HEAD) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) dA_head[q] = __builtin_amdgcn_exp2f(dl[q] * ap[0]);
+    }
+    if constexpr (SUMMARY) {
+      float s8 = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s8 += dl[q];
+      dsum_total += (double)s8;
+    }
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const float bv[8] = {k.bc[j][0].x, k.bc[j][0].y, k.bc[j][0].z, k.bc[j][0].w,
+                           k.bc[j][1].x, k.bc[j][1].y, k.bc[j][1].z, k.bc[j][1].w};
+      float cv[8];
+      if constexpr (!SUMMARY) {
+        cv[0] = k.bc[j][2].x; cv[1] = k.bc[j][2].y; cv[2] = k.bc[j][2].z; cv[3] = k.bc[j][2].w;
+        cv[4] = k.bc[j][3].x; cv[5] = k.bc[j][3].y; cv[6] = k.bc[j][3].z; cv[7] = k.bc[j][3].w;
+      }
+      float dA[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if constexpr (HEAD) dA[q] = dA_head[q];
+        else dA[q] = __builtin_amdgcn_exp2f(dl[q] * ap[j]);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        h[j] = fmaf(dA[q], h[j], u[q] * bv[q]);
+        if constexpr (!SUMMARY) acc[q] = (j == 0) ? cv[q] * h[j] : fmaf(cv[q], h[j], acc[q]);
+      }
+    }
+    if constexpr (!SUMMARY) {
+      float4* dst = reinterpret_cast<float4*>(&s_part[(w * kChannelsPerGroup + lane) * kPartStride + tt]);
+      dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+  };
+  // 4-step blocks for the software-pipelined full half
+  struct Blk4 {
+    f32x4 du[2];
+    f32x4 bc[NS][SUMMARY ? 1 : 2];
+  };
+  auto load4 = [&](Blk4& k, int h0, int tt) __attribute__((always_inline)) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(&s_du[lane * kDuStrideL + 2 * (h0 + tt)]);
+    k.du[0] = src[0];
+    k.du[1] = src[1];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      k.bc[j][0] = *reinterpret_cast<const f32x4*>(&s_B[(n0 + j) * kBcStrideL + h0 + tt]);
+      if constexpr (!SUMMARY)
+        k.bc[j][1] = *reinterpret_cast<const f32x4*>(&s_C[(n0 + j) * kBcStrideL + h0 + tt]);
+    }
+  };
+  auto comp4 = [&](const Blk4& k, int tt) __attribute__((always_inline)) {
+    const float dl[4] = {k.du[0].x, k.du[0].z, k.du[1].x, k.du[1].z};
+    const float u[4] = {k.du[0].y, k.du[0].w, k.du[1].y, k.du[1].w};
+    float acc[4];
+    float dA_head[HEAD ? 4 : 1];
+    if constexpr (HEAD) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dA_head[q] = __builtin_amdgcn_exp2f(dl[q] * ap[0]);
+    }
+    if constexpr (SUMMARY) dsum_total += (double)((dl[0] + dl[1]) + (dl[2] + dl[3]));
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const float bv[4] = {k.bc[j][0].x, k.bc[j][0].y, k.bc[j][0].z, k.bc[j][0].w};
+      float cv[4];
+      if constexpr (!SUMMARY) {
+        cv[0] = k.bc[j][1].x; cv[1] = k.bc[j][1].y; cv[2] = k.bc[j][1].z; cv[3] = k.bc[j][1].w;
+      }
+      float dA[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (HEAD) dA[q] = dA_head[q];
+        else dA[q] = __builtin_amdgcn_exp2f(dl[q] * ap[j]);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        h[j] = fmaf(dA[q], h[j], u[q] * bv[q]);
+        if constexpr (!SUMMARY) acc[q] = (j == 0) ? cv[q] * h[j] : fmaf(cv[q], h[j], acc[q]);
+      }
+    }
+    if constexpr (!SUMMARY) {
+      float4* dst = reinterpret_cast<float4*>(&s_part[(w * kChannelsPerGroup + lane) * kPartStride + tt]);
+      dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+  };
+  auto recurrence = [&](int h0, int tb_len) __attribute__((always_inline)) {
+    if constexpr (NS <= 4) {
+      if (tb_len == kTB) {
+        // a full half in 4-step blocks, software-pipelined: block i + 1 is read from LDS before
+        // block i is computed, so the reads of one block overlap the arithmetic of the previous
+        Blk4 cur, nxt;
+        load4(cur, h0, 0);
+#pragma unroll
+        for (int tt = 0; tt < kTB; tt += 4) {
+          if (tt + 4 < kTB) load4(nxt, h0, tt + 4);
+          __builtin_amdgcn_sched_barrier(0);  // the compiler would otherwise sink the reads
+          comp4(cur, tt);
+          if (tt + 4 < kTB) cur = nxt;
+        }
+        return;
+      }
+    }
+    for (int tt = 0; tt < tb_len; tt += 8) {
+      Blk k;
+      load_blk(k, h0, tt);
+      comp_blk(k, tt);
     }
   };
 
   // y = (sum of the partial readouts + D x) * silu(z) for half hf
-  auto epilogue = [&](int hf, int64_t t0, int tb_len, bool full) {
+  auto epilogue = [&](int hf, int64_t t0, int tb_len, bool full) __attribute__((always_inline)) {
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
       if (!ilive[it]) continue;
@@ -510,7 +602,7 @@ __global__ void __launch_bounds__(64 * NW)
   };
 
   // the two halves of a load tile whose prologue is in LDS
-  auto halves = [&](int64_t t0, int lt_len, bool full) {
+  auto halves = [&](int64_t t0, int lt_len, bool full) __attribute__((always_inline)) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const int h0 = hf * kTB;
