@@ -50,17 +50,19 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_ABI_VERSION 1
+#define SSM_SCAN_ABI_VERSION 2
 
 typedef enum {
   SSM_OK = 0,
   SSM_ERR_NULL_ARG = -1,       /* a required pointer (desc, x, delta, A, B, C, y) is NULL */
   SSM_ERR_BAD_SHAPE = -2,      /* a size < 0, dim/dstate/ngroups/headdim < 1, dim % ngroups,
                                   dim % headdim, dstate > SSM_MAX_DSTATE (128), or sizes that overflow */
-  SSM_ERR_BAD_DTYPE = -3,      /* io_dtype or a_mode not one of the enums below */
+  SSM_ERR_BAD_DTYPE = -3,      /* io_dtype, a_mode or discretization not one of the enums below,
+                                  or a nonzero reserved field */
   SSM_ERR_BAD_STRIDE = -4,     /* a negative stride, or strides that make rows overlap */
   SSM_ERR_MISALIGNED = -5,     /* a pointer not aligned to its element size */
-  SSM_ERR_ALIAS = -6,          /* y overlaps an input */
+  SSM_ERR_ALIAS = -6,          /* an output (y, h_final, workspace) overlaps an input or another
+                                  output */
   SSM_ERR_WORKSPACE = -7,      /* workspace NULL or smaller than the size query returns */
   SSM_ERR_HIP = -8,            /* the HIP runtime reported an error while enqueueing */
   SSM_ERR_UNSUPPORTED = -9     /* valid arguments outside what this build implements */
@@ -108,8 +110,9 @@ int ssm_selective_scan_workspace_size(const ssm_scan_desc* desc, size_t* bytes);
  *   x, delta, B, C, z, y : device pointers of the io dtype (z may be NULL)
  *   A, D, delta_bias     : device pointers, fp32 (D and delta_bias may be NULL)
  *   delta_softplus       : nonzero applies softplus to delta_raw + delta_bias
- *   workspace            : device scratch of at least the queried size (may be NULL when the
- *                          query returns 0); its contents on entry do not matter
+ *   workspace            : device scratch of at least the queried size, 4-byte aligned (may be
+ *                          NULL when the query returns 0); its contents on entry do not matter
+ *                          and it must not overlap any other argument
  *   stream               : hipStream_t to enqueue on
  * y must not overlap any input. */
 int ssm_selective_scan_fwd(const ssm_scan_desc* desc, const void* x, const void* delta,
@@ -119,6 +122,34 @@ int ssm_selective_scan_fwd(const ssm_scan_desc* desc, const void* x, const void*
 
 /* Static, NUL-terminated description of a status code. */
 const char* ssm_status_string(int status);
+
+/* Discretisation of B (the pages' f_B).
+ *   SSM_DISC_DELTA_B: B_bar = delta * B (the default).
+ *   SSM_DISC_ZOH:     B_bar = (exp(delta A) - 1) / A * B, the zero-order hold; it tends to
+ *                     delta * B as delta A -> 0 and equals it where A == 0. (Page "NL-345",
+ *                     §2 "Discretization", eq. (4); memo page, "数式解説".) */
+typedef enum { SSM_DISC_DELTA_B = 0, SSM_DISC_ZOH = 1 } ssm_discretization;
+
+/* Options of ssm_selective_scan_fwd_ext. A zero-filled struct gives ssm_selective_scan_fwd.
+ * The state carried between calls lets a long sequence be scanned in pieces (the recurrence is
+ * the same across a call boundary: page "NL-345", §2 "Computation", recurrent mode). */
+typedef struct ssm_scan_ext {
+  int32_t discretization; /* ssm_discretization */
+  int32_t reserved;       /* must be 0 */
+  const float* h0;        /* nullable: initial state (batch, dim, dstate) fp32, contiguous, read
+                             before the first step; NULL starts from zeros */
+  float* h_final;         /* nullable: receives the state after the last step, (batch, dim,
+                             dstate) fp32 contiguous; must not overlap h0, y or any input (use
+                             two buffers to carry the state across calls) */
+} ssm_scan_ext;
+
+/* ssm_selective_scan_fwd with the options above (`ext` may be NULL). With seqlen == 0, y is not
+ * touched and h_final receives h0 (or zeros). The workspace size does not depend on `ext`. */
+int ssm_selective_scan_fwd_ext(const ssm_scan_desc* desc, const void* x, const void* delta,
+                               const float* A, const void* B, const void* C, const float* D,
+                               const void* z, const float* delta_bias, int32_t delta_softplus,
+                               void* y, const ssm_scan_ext* ext, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /* SSM_SCAN_ABI_VERSION of the built library. */
 int ssm_abi_version(void);

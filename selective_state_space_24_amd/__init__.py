@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_PKG, "lib", "libssm_scan.so")
 SSM_OK = 0
 SSM_DTYPE_F32, SSM_DTYPE_BF16 = 0, 1
 SSM_A_DIAG, SSM_A_HEAD = 0, 1
+SSM_DISC_DELTA_B, SSM_DISC_ZOH = 0, 1
 SSM_MAX_DSTATE = 128
 
 STATUS_NAMES = {
@@ -44,6 +45,12 @@ class ScanDesc(ctypes.Structure):
     ]
 
 
+class ScanExt(ctypes.Structure):
+    """Mirror of ``ssm_scan_ext``."""
+    _fields_ = [("discretization", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("h0", ctypes.c_void_p), ("h_final", ctypes.c_void_p)]
+
+
 class ScanError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -68,6 +75,9 @@ def lib():
         h.ssm_selective_scan_workspace_size.restype = ctypes.c_int
         h.ssm_selective_scan_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
         h.ssm_selective_scan_fwd.restype = ctypes.c_int
+        h.ssm_selective_scan_fwd_ext.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
+                                                 ctypes.POINTER(ScanExt), vp, sz, vp]
+        h.ssm_selective_scan_fwd_ext.restype = ctypes.c_int
         h.ssm_status_string.argtypes = [ctypes.c_int]
         h.ssm_status_string.restype = ctypes.c_char_p
         h.ssm_abi_version.argtypes = []
@@ -109,6 +119,14 @@ def fwd_raw(desc: ScanDesc, x, delta, A, B, C, D, z, delta_bias, delta_softplus:
     return int(lib().ssm_selective_scan_fwd(ctypes.byref(desc), x, delta, A, B, C, D, z,
                                             delta_bias, int(bool(delta_softplus)), y, workspace,
                                             int(workspace_bytes), stream))
+
+
+def fwd_ext_raw(desc: ScanDesc, x, delta, A, B, C, D, z, delta_bias, delta_softplus: bool, y,
+                ext: Optional[ScanExt], workspace, workspace_bytes: int, stream) -> int:
+    """Direct call of ``ssm_selective_scan_fwd_ext``; returns the status code without raising."""
+    return int(lib().ssm_selective_scan_fwd_ext(
+        ctypes.byref(desc), x, delta, A, B, C, D, z, delta_bias, int(bool(delta_softplus)), y,
+        ctypes.byref(ext) if ext is not None else None, workspace, int(workspace_bytes), stream))
 
 
 # ---------------------------------------------------------------------------------------------
@@ -178,9 +196,13 @@ def describe(x, delta, A, B, C, z=None, y=None) -> ScanDesc:
 
 
 def selective_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
-                       *, out=None, workspace=None, stream=None):
+                       *, zoh: bool = False, h0=None, final_state=None, out=None,
+                       workspace=None, stream=None):
     """y = selective scan of torch device tensors (see ``include/ssm_scan.h``).
 
+    ``zoh`` selects the zero-order-hold B discretisation. ``h0`` (batch, dim, N) float32 is the
+    initial state. ``final_state`` is True (allocate) or a (batch, dim, N) float32 tensor that
+    receives the state after the last step; the call then returns ``(y, final_state)``.
     ``out`` receives y if given (shape and dtype of x). ``workspace`` may be a uint8 device
     tensor of at least ``workspace_size`` bytes; otherwise one is allocated. ``stream`` defaults
     to the current torch stream. Raises ScanError with the library's status on failure.
@@ -188,18 +210,34 @@ def selective_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta
     import torch
     y = out if out is not None else torch.empty_like(x, memory_format=torch.contiguous_format)
     desc = describe(x, delta, A, B, C, z, y)
-    for name, t in (("D", D), ("delta_bias", delta_bias)):
+    for name, t in (("D", D), ("delta_bias", delta_bias), ("h0", h0)):
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
             raise TypeError(f"{name} must be a contiguous float32 tensor")
+    state_shape = (desc.batch, desc.dim, desc.dstate)
+    if h0 is not None and tuple(h0.shape) != state_shape:
+        raise ValueError(f"h0 must be {state_shape}, got {tuple(h0.shape)}")
+    hfin = None
+    if final_state is True:
+        hfin = torch.empty(state_shape, dtype=torch.float32, device=x.device)
+    elif final_state is not None and final_state is not False:
+        hfin = final_state
+        if (hfin.dtype != torch.float32 or not hfin.is_contiguous()
+                or tuple(hfin.shape) != state_shape):
+            raise TypeError(f"final_state must be a contiguous float32 tensor of shape {state_shape}")
     need = workspace_size(desc)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     sp = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
-    rc = fwd_raw(desc, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                 _ptr(delta_bias), delta_softplus, _ptr(y), _ptr(workspace) if need else None,
-                 need, sp)
+    args = (desc, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+            _ptr(delta_bias), delta_softplus, _ptr(y))
+    tail = (_ptr(workspace) if need else None, need, sp)
+    if zoh or h0 is not None or hfin is not None:
+        ext = ScanExt(SSM_DISC_ZOH if zoh else SSM_DISC_DELTA_B, 0, _ptr(h0), _ptr(hfin))
+        rc = fwd_ext_raw(*args, ext, *tail)
+    else:
+        rc = fwd_raw(*args, *tail)
     if rc != SSM_OK:
         raise ScanError(rc, "ssm_selective_scan_fwd")
-    return y
+    return (y, hfin) if hfin is not None else y

@@ -7,12 +7,6 @@
 #include "scan_internal.h"
 #include "ssm_scan.h"
 
-namespace ssm {
-hipError_t launch_scan_fwd(const ScanParams& p, bool bf16, bool head, hipStream_t stream);
-int time_tile();
-int channels_per_group(int64_t N);
-int waves_per_group(int64_t N);
-}  // namespace ssm
 
 namespace {
 
@@ -89,10 +83,10 @@ int check_desc(const ssm_scan_desc* d) {
 }
 
 Plan plan_segments(const ssm_scan_desc* d) {
-  const int64_t tile = ssm::time_tile();
-  const int64_t cpg = ssm::channels_per_group(d->dstate);
+  const int64_t tile = ssm::kLT;
+  const int64_t cpg = ssm::kChannelsPerGroup;
   const int64_t groups = d->batch * ((d->dim + cpg - 1) / cpg);
-  const int64_t waves = groups * ssm::waves_per_group(d->dstate);
+  const int64_t waves = groups * ssm::kWavesPerGroup;
   Plan p{1, d->seqlen > 0 ? d->seqlen : 1};
   if (groups == 0 || d->seqlen == 0) return p;
   if (waves * 4 >= kTargetWaves * 3) return p;  // enough channel groups: one pass
@@ -170,14 +164,30 @@ int ssm_selective_scan_workspace_size(const ssm_scan_desc* desc, size_t* bytes) 
   return SSM_OK;
 }
 
-int ssm_selective_scan_fwd(const ssm_scan_desc* desc, const void* x, const void* delta,
-                           const float* A, const void* B, const void* C, const float* D,
-                           const void* z, const float* delta_bias, int32_t delta_softplus,
-                           void* y, void* workspace, size_t workspace_bytes, void* stream) {
+int ssm_selective_scan_fwd_ext(const ssm_scan_desc* desc, const void* x, const void* delta,
+                               const float* A, const void* B, const void* C, const float* D,
+                               const void* z, const float* delta_bias, int32_t delta_softplus,
+                               void* y, const ssm_scan_ext* ext, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   int rc = check_desc(desc);
   if (rc != SSM_OK) return rc;
+  const int32_t disc = ext ? ext->discretization : SSM_DISC_DELTA_B;
+  if (disc != SSM_DISC_DELTA_B && disc != SSM_DISC_ZOH) return SSM_ERR_BAD_DTYPE;
+  if (ext && ext->reserved != 0) return SSM_ERR_BAD_DTYPE;
+  const float* h0 = ext ? ext->h0 : nullptr;
+  float* hfin = ext ? ext->h_final : nullptr;
   const ssm_scan_desc& d = *desc;
-  if (d.batch == 0 || d.seqlen == 0) return SSM_OK;  // nothing to compute or write
+  if (d.batch == 0) return SSM_OK;  // nothing to compute or write
+  if (d.seqlen == 0) {
+    // no steps: the final state is the initial one (zero without h0)
+    if (!hfin) return SSM_OK;
+    const size_t sbytes = (size_t)d.batch * d.dim * d.dstate * sizeof(float);
+    if (!aligned(hfin, 4) || (h0 && !aligned(h0, 4))) return SSM_ERR_MISALIGNED;
+    if (h0 && overlaps(hfin, sbytes, h0, sbytes)) return SSM_ERR_ALIAS;
+    const hipError_t e = ssm::launch_state_copy(h0, hfin, (int64_t)(sbytes / sizeof(float)),
+                                                static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+  }
   if (!x || !delta || !A || !B || !C || !y) return SSM_ERR_NULL_ARG;
 
   const bool bf16 = d.io_dtype == SSM_DTYPE_BF16;
@@ -188,12 +198,13 @@ int ssm_selective_scan_fwd(const ssm_scan_desc* desc, const void* x, const void*
   const void* io_ptrs[] = {x, delta, B, C, z, y};
   for (const void* p : io_ptrs)
     if (p && !aligned(p, es)) return SSM_ERR_MISALIGNED;
-  const void* f32_ptrs[] = {A, D, delta_bias, workspace};
+  const void* f32_ptrs[] = {A, D, delta_bias, h0, hfin};
   for (const void* p : f32_ptrs)
     if (p && !aligned(p, 4)) return SSM_ERR_MISALIGNED;
 
-  // y must not overlap any input
+  // outputs (y, the final state, the workspace) must not overlap any input or each other
   const size_t y_bytes = (size_t)extent3(d.batch, d.dim, d.seqlen, d.y_stride_batch, d.y_stride_dim) * es;
+  const size_t state_bytes = (size_t)d.batch * d.dim * d.dstate * sizeof(float);
   const size_t in_bytes[] = {
       (size_t)extent3(d.batch, d.dim, d.seqlen, d.x_stride_batch, d.x_stride_dim) * es,
       (size_t)extent3(d.batch, drows, d.seqlen, d.delta_stride_batch, d.delta_stride_dim) * es,
@@ -202,24 +213,35 @@ int ssm_selective_scan_fwd(const ssm_scan_desc* desc, const void* x, const void*
       z ? (size_t)extent3(d.batch, d.dim, d.seqlen, d.z_stride_batch, d.z_stride_dim) * es : 0,
       (size_t)(head ? nheads : d.dim * d.dstate) * 4,
       D ? (size_t)d.dim * 4 : 0,
-      delta_bias ? (size_t)drows * 4 : 0};
-  const void* in_ptrs[] = {x, delta, B, C, z, A, D, delta_bias};
-  for (int i = 0; i < 8; ++i)
+      delta_bias ? (size_t)drows * 4 : 0,
+      h0 ? state_bytes : 0};
+  const void* in_ptrs[] = {x, delta, B, C, z, A, D, delta_bias, h0};
+  constexpr int kInputs = 9;
+  for (int i = 0; i < kInputs; ++i) {
     if (overlaps(y, y_bytes, in_ptrs[i], in_bytes[i])) return SSM_ERR_ALIAS;
+    if (hfin && overlaps(hfin, state_bytes, in_ptrs[i], in_bytes[i])) return SSM_ERR_ALIAS;
+  }
+  if (hfin && overlaps(hfin, state_bytes, y, y_bytes)) return SSM_ERR_ALIAS;
 
   // B and C must be uniform over each workgroup's channels
   const int64_t ch_per_group = d.dim / d.ngroups;
-  if (d.ngroups > 1 && ch_per_group % ssm::channels_per_group(d.dstate) != 0) return SSM_ERR_UNSUPPORTED;
+  if (d.ngroups > 1 && ch_per_group % ssm::kChannelsPerGroup != 0) return SSM_ERR_UNSUPPORTED;
 
   const Plan plan = plan_segments(desc);
   const size_t need = workspace_bytes_for(desc, plan);
   if (need > 0 && (!workspace || workspace_bytes < need)) return SSM_ERR_WORKSPACE;
-  if (need > 0 && overlaps(workspace, need, y, y_bytes)) return SSM_ERR_ALIAS;
+  if (need > 0 && !aligned(workspace, 4)) return SSM_ERR_MISALIGNED;
+  if (need > 0) {
+    for (int i = 0; i < kInputs; ++i)
+      if (overlaps(workspace, need, in_ptrs[i], in_bytes[i])) return SSM_ERR_ALIAS;
+    if (overlaps(workspace, need, y, y_bytes)) return SSM_ERR_ALIAS;
+    if (hfin && overlaps(workspace, need, hfin, state_bytes)) return SSM_ERR_ALIAS;
+  }
 
   ssm::ScanParams p;
   memset(&p, 0, sizeof(p));
   p.x = x; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.delta_bias = delta_bias;
-  p.y = y;
+  p.y = y; p.h0 = h0; p.hfin = hfin;
   p.batch = d.batch; p.dim = d.dim; p.L = d.seqlen; p.N = d.dstate; p.ngroups = d.ngroups;
   p.headdim = d.headdim;
   p.x_sb = d.x_stride_batch; p.x_sd = d.x_stride_dim;
@@ -232,6 +254,7 @@ int ssm_selective_scan_fwd(const ssm_scan_desc* desc, const void* x, const void*
   p.seg_len = plan.seg_len;
   p.nseg = (int32_t)plan.nseg;
   p.softplus = delta_softplus ? 1 : 0;
+  p.zoh = disc == SSM_DISC_ZOH ? 1 : 0;
   if (plan.nseg > 1) {
     p.hend = static_cast<float*>(workspace);
     p.dsum = p.hend + (size_t)d.batch * d.dim * plan.nseg * d.dstate;
@@ -245,18 +268,29 @@ int ssm_selective_scan_fwd(const ssm_scan_desc* desc, const void* x, const void*
   const int64_t vstrides[] = {d.x_stride_batch, d.x_stride_dim, d.delta_stride_batch,
                               d.delta_stride_dim, z ? d.z_stride_batch : 0, z ? d.z_stride_dim : 0,
                               d.y_stride_batch, d.y_stride_dim};
-  for (int64_t s : vstrides)
-    if (s % vec) vec_ok = false;
+  for (int64_t st : vstrides)
+    if (st % vec) vec_ok = false;
   p.vec_io = vec_ok ? 1 : 0;
   bool bc_vec = aligned(B, 16) && aligned(C, 16);
   const int64_t bstrides[] = {d.B_stride_batch, d.B_stride_group, d.B_stride_state,
                               d.C_stride_batch, d.C_stride_group, d.C_stride_state};
-  for (int64_t s : bstrides)
-    if (s % vec) bc_vec = false;
+  for (int64_t st : bstrides)
+    if (st % vec) bc_vec = false;
   p.bc_vec = bc_vec ? 1 : 0;
 
-  const hipError_t e = ssm::launch_scan_fwd(p, bf16, head, static_cast<hipStream_t>(stream));
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (bf16) e = head ? ssm::launch_bf16_head(p, hs) : ssm::launch_bf16_diag(p, hs);
+  else e = head ? ssm::launch_f32_head(p, hs) : ssm::launch_f32_diag(p, hs);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+int ssm_selective_scan_fwd(const ssm_scan_desc* desc, const void* x, const void* delta,
+                           const float* A, const void* B, const void* C, const float* D,
+                           const void* z, const float* delta_bias, int32_t delta_softplus,
+                           void* y, void* workspace, size_t workspace_bytes, void* stream) {
+  return ssm_selective_scan_fwd_ext(desc, x, delta, A, B, C, D, z, delta_bias, delta_softplus, y,
+                                    nullptr, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

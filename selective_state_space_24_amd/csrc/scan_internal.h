@@ -1,11 +1,17 @@
 // Internal launch parameters shared by the host dispatch and the gfx950 kernels.
 #pragma once
+#include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace ssm {
 
 // Channels handled by one workgroup: one channel per lane of a 64-wide wavefront.
 constexpr int kChannelsPerGroup = 64;
+// Wavefronts per workgroup; they split the states of the workgroup's channels.
+constexpr int kWavesPerGroup = 4;
+constexpr int kTB = 32;       // time steps per compute tile
+constexpr int kLT = 2 * kTB;  // time steps per load tile (128 bytes of bf16 per row); segments
+                              // along L start at multiples of it
 
 struct ScanParams {
   // inputs / outputs (device pointers); element type is the io dtype unless noted
@@ -18,6 +24,8 @@ struct ScanParams {
   const void* z;            // nullable
   const float* delta_bias;  // nullable
   void* y;
+  const float* h0;          // nullable: initial state (batch, dim, N) fp32
+  float* hfin;              // nullable: final state (batch, dim, N) fp32
   // per-segment summaries for sequences split along L (nullable when nseg == 1):
   // hend[((b * dim + d) * nseg + s) * N + n] and dsum[(b * dim + d) * nseg + s]
   float* hend;
@@ -32,6 +40,15 @@ struct ScanParams {
   int32_t softplus;          // apply softplus to delta + bias
   int32_t vec_io;            // x/delta/z/y rows allow 16-byte vector access
   int32_t bc_vec;            // B/C rows allow 16-byte vector access
+  int32_t zoh;               // zero-order-hold B discretisation instead of delta * B
 };
+
+// One launcher per (io dtype, A mode); each is compiled in its own translation unit.
+hipError_t launch_bf16_diag(const ScanParams& p, hipStream_t stream);
+hipError_t launch_bf16_head(const ScanParams& p, hipStream_t stream);
+hipError_t launch_f32_diag(const ScanParams& p, hipStream_t stream);
+hipError_t launch_f32_head(const ScanParams& p, hipStream_t stream);
+// dst[0, n) = src[0, n), or zeros when src is null
+hipError_t launch_state_copy(const float* src, float* dst, int64_t n, hipStream_t stream);
 
 }  // namespace ssm

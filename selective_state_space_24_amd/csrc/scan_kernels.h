@@ -21,6 +21,7 @@
 //     associatively, which is what makes the split exact up to rounding.
 //
 // Arithmetic: fp32 throughout. dA = 2^(delta * A * log2 e) with the hardware exp2.
+#pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,15 +31,9 @@ namespace ssm {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kTB = 32;                 // time steps per compute tile
-constexpr int kLT = 2 * kTB;            // time steps per load tile (128 bytes of bf16 per row)
 constexpr int kDuStrideL = 2 * kLT + 4;  // floats per channel row of (delta, u) in LDS
 constexpr int kBcStrideL = kLT + 4;      // floats per state row of the B / C tile
 constexpr int kPartStride = kTB + 4;     // floats per channel row of partial readouts
-#ifndef SSM_PREFETCH_TILES
-#define SSM_PREFETCH_TILES 1
-#endif
-constexpr int kPrefetch = SSM_PREFETCH_TILES;  // load tiles fetched ahead per workgroup
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 typedef uint16_t bf16_bits;
@@ -157,6 +152,17 @@ __device__ __forceinline__ float silu_f32(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
 }
 
+// Zero-order hold: B_bar = (exp(delta a) - 1) / a * B = g * delta * B with g = expm1(x) / x,
+// x = delta a. From dA = 2^w (w = x log2 e) already computed, g = (dA - 1) / ln(dA): Kahan's
+// form, accurate to a few ulps because it is the exact ratio for the exponent ln(dA) that the
+// rounded dA represents. The limits are exact: g = 1 when dA == 1 (x -> 0, the rule tends to
+// delta * B) and g = -1 / x when dA underflows to 0.
+__device__ __forceinline__ float zoh_ratio(float dA, float w) {
+  const float g = (dA - 1.0f) * __builtin_amdgcn_rcpf(__builtin_amdgcn_logf(dA) * kLn2);
+  const float g0 = -__builtin_amdgcn_rcpf(w * kLn2);
+  return dA == 1.0f ? 1.0f : (dA == 0.0f ? g0 : g);
+}
+
 // One workgroup = NW wavefronts x 64 channels. Lane l owns channel d0 + l in every wavefront;
 // wavefront w owns states [w*NS, (w+1)*NS), so the B and C values a wavefront needs at a step
 // are the same for all of its lanes: they are read from the LDS tile with wave-uniform
@@ -170,8 +176,8 @@ __device__ __forceinline__ float silu_f32(float z) {
 // a final partial tile, or rows that do not allow 16-byte access, take a guarded path.
 //
 // HEAD: one A and one delta per head; SUMMARY: the segment summary pass (no readout, no y);
-// GATE: y is multiplied by silu(z).
-template <typename IO, int NS, int NW, bool HEAD, bool SUMMARY, bool GATE>
+// GATE: y is multiplied by silu(z); ZOH: zero-order-hold B discretisation (else delta * B).
+template <typename IO, int NS, int NW, bool HEAD, bool SUMMARY, bool GATE, bool ZOH>
 // Two workgroups fit a CU's LDS, so each SIMD holds at most two of these wavefronts: the second
 // launch bound lets the compiler use the registers that this occupancy leaves.
 __global__ void __launch_bounds__(64 * NW, 2)
@@ -180,7 +186,6 @@ __global__ void __launch_bounds__(64 * NW, 2)
                     const float* __restrict__ Am, const float* __restrict__ Dm,
                     const float* __restrict__ bias_p, float* __restrict__ hend,
                     float* __restrict__ dsum, const ScanParams p) {
-  constexpr int PF = kPrefetch;
   constexpr int NT = 64 * NW;
   constexpr int NP = NS * NW;  // padded state count
   constexpr int V = IoTraits<IO>::kVec;
@@ -225,6 +230,13 @@ __global__ void __launch_bounds__(64 * NW, 2)
   float h[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) h[j] = 0.0f;
+  if (!SUMMARY && p.h0 && live) {
+    // the caller's initial state (summaries always start from zero)
+    const float* h0r = p.h0 + (b * p.dim + d) * p.N + n0;
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+      if (n0 + j < p.N) h[j] = h0r[j];
+  }
   if (!SUMMARY && seg > 0 && live) {
     // compose the summaries of segments 0 .. seg-1: h <- exp(A * sum delta) h + h_end
     const int64_t base = (b * p.dim + d) * p.nseg;
@@ -284,9 +296,12 @@ __global__ void __launch_bounds__(64 * NW, 2)
     crow[it] = SUMMARY ? nullptr : Cg + nn * p.C_sn;
   }
 
-  // raw 16-byte words of a full load tile: each item's two halves are fetched back to back
+  // raw 16-byte words of a full load tile: each item's two halves are fetched back to back.
+  // z is not part of it: it is only needed by the epilogue, so each tile loads its own z right
+  // after its prologue (see load_z), which keeps the loop free of register copies that would
+  // make the wait for the next tile's data also wait for the y stores just issued.
   struct Raw {
-    u32x4 x[2][IPT], d[2][IPT], z[2][IPT], b[2][BPT], c[2][BPT];
+    u32x4 x[2][IPT], d[2][IPT], b[2][BPT], c[2][BPT];
   };
   auto fetch = [&](Raw& r, int64_t t0) __attribute__((always_inline)) {
 #pragma unroll
@@ -296,7 +311,6 @@ __global__ void __launch_bounds__(64 * NW, 2)
       for (int hf = 0; hf < 2; ++hf) {
         r.x[hf][it] = load16<true>(xrow[it] + t0 + hf * kTB + itl[it]);
         r.d[hf][it] = load16<true>(drow_p[it] + t0 + hf * kTB + itl[it]);
-        if constexpr (GATE) r.z[hf][it] = load16<true>(zrow[it] + t0 + hf * kTB + itl[it]);
       }
     }
 #pragma unroll
@@ -312,6 +326,17 @@ __global__ void __launch_bounds__(64 * NW, 2)
 
   float xkeep[2][IPT][V];
   u32x4 zkeep[2][IPT];
+  auto load_z = [&](int64_t t0) __attribute__((always_inline)) {
+    if constexpr (GATE) {
+#pragma unroll
+      for (int it = 0; it < IPT; ++it) {
+        if (!iown[it]) continue;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+          zkeep[hf][it] = load16<true>(zrow[it] + t0 + hf * kTB + itl[it]);
+      }
+    }
+  };
 
   // delta and u = delta * x of item it, half hf, into LDS
   auto put_du = [&](int hf, int it, float (&dv)[V]) {
@@ -359,7 +384,6 @@ __global__ void __launch_bounds__(64 * NW, 2)
         float dv[V];
         unpack16<IO>(rw.x[hf][it], xkeep[hf][it]);
         unpack16<IO>(rw.d[hf][it], dv);
-        if constexpr (GATE) zkeep[hf][it] = rw.z[hf][it];
         put_du(hf, it, dv);
       }
 #pragma unroll
@@ -455,10 +479,13 @@ __global__ void __launch_bounds__(64 * NW, 2)
       dl[2 * q + 1] = k.du[q].z; u[2 * q + 1] = k.du[q].w;
     }
     float acc[8];
-    float dA_head[HEAD ? 8 : 1];
+    float dA_head[HEAD ? 8 : 1], g_head[HEAD && ZOH ? 8 : 1];
     if constexpr (HEAD) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) dA_head[q] = __builtin_amdgcn_exp2f(dl[q] * ap[0]);
+      for (int q = 0; q < 8; ++q) {
+        dA_head[q] = __builtin_amdgcn_exp2f(dl[q] * ap[0]);
+        if constexpr (ZOH) g_head[q] = zoh_ratio(dA_head[q], dl[q] * ap[0]);
+      }
     }
     if constexpr (SUMMARY) {
       float s8 = 0.0f;
@@ -475,15 +502,17 @@ __global__ void __launch_bounds__(64 * NW, 2)
         cv[0] = k.bc[j][2].x; cv[1] = k.bc[j][2].y; cv[2] = k.bc[j][2].z; cv[3] = k.bc[j][2].w;
         cv[4] = k.bc[j][3].x; cv[5] = k.bc[j][3].y; cv[6] = k.bc[j][3].z; cv[7] = k.bc[j][3].w;
       }
-      float dA[8];
+      float dA[8], ub[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         if constexpr (HEAD) dA[q] = dA_head[q];
         else dA[q] = __builtin_amdgcn_exp2f(dl[q] * ap[j]);
+        ub[q] = u[q] * bv[q];
+        if constexpr (ZOH) ub[q] *= HEAD ? g_head[q] : zoh_ratio(dA[q], dl[q] * ap[j]);
       }
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        h[j] = fmaf(dA[q], h[j], u[q] * bv[q]);
+        h[j] = fmaf(dA[q], h[j], ub[q]);
         if constexpr (!SUMMARY) acc[q] = (j == 0) ? cv[q] * h[j] : fmaf(cv[q], h[j], acc[q]);
       }
     }
@@ -513,10 +542,13 @@ __global__ void __launch_bounds__(64 * NW, 2)
     const float dl[4] = {k.du[0].x, k.du[0].z, k.du[1].x, k.du[1].z};
     const float u[4] = {k.du[0].y, k.du[0].w, k.du[1].y, k.du[1].w};
     float acc[4];
-    float dA_head[HEAD ? 4 : 1];
+    float dA_head[HEAD ? 4 : 1], g_head[HEAD && ZOH ? 4 : 1];
     if constexpr (HEAD) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dA_head[q] = __builtin_amdgcn_exp2f(dl[q] * ap[0]);
+      for (int q = 0; q < 4; ++q) {
+        dA_head[q] = __builtin_amdgcn_exp2f(dl[q] * ap[0]);
+        if constexpr (ZOH) g_head[q] = zoh_ratio(dA_head[q], dl[q] * ap[0]);
+      }
     }
     if constexpr (SUMMARY) dsum_total += (double)((dl[0] + dl[1]) + (dl[2] + dl[3]));
 #pragma unroll
@@ -526,15 +558,17 @@ __global__ void __launch_bounds__(64 * NW, 2)
       if constexpr (!SUMMARY) {
         cv[0] = k.bc[j][1].x; cv[1] = k.bc[j][1].y; cv[2] = k.bc[j][1].z; cv[3] = k.bc[j][1].w;
       }
-      float dA[4];
+      float dA[4], ub[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if constexpr (HEAD) dA[q] = dA_head[q];
         else dA[q] = __builtin_amdgcn_exp2f(dl[q] * ap[j]);
+        ub[q] = u[q] * bv[q];
+        if constexpr (ZOH) ub[q] *= HEAD ? g_head[q] : zoh_ratio(dA[q], dl[q] * ap[j]);
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        h[j] = fmaf(dA[q], h[j], u[q] * bv[q]);
+        h[j] = fmaf(dA[q], h[j], ub[q]);
         if constexpr (!SUMMARY) acc[q] = (j == 0) ? cv[q] * h[j] : fmaf(cv[q], h[j], acc[q]);
       }
     }
@@ -617,23 +651,19 @@ __global__ void __launch_bounds__(64 * NW, 2)
     }
   };
 
-  // ---- full load tiles, with the prefetch ring
+  // ---- full load tiles: the next tile's x, delta, B and C are fetched into registers while
+  // the current one is processed
   const int64_t n_full = fast_ok ? (t_end - t_begin) / kLT : 0;
-  Raw raw[PF];
-#pragma unroll
-  for (int q = 0; q < PF; ++q)
-    if (q < n_full) fetch(raw[q], t_begin + q * kLT);
-  for (int64_t i = 0; i < n_full; i += PF) {
-#pragma unroll
-    for (int q = 0; q < PF; ++q) {
-      if (i + q >= n_full) break;
-      const int64_t t0 = t_begin + (i + q) * kLT;
-      prologue_full(raw[q]);
-      if (i + q + PF < n_full) fetch(raw[q], t0 + PF * kLT);
-      __syncthreads();
-      halves(t0, kLT, true);
-      __syncthreads();  // LDS tiles free for the next prologue
-    }
+  Raw raw;
+  if (n_full > 0) fetch(raw, t_begin);
+  for (int64_t i = 0; i < n_full; ++i) {
+    const int64_t t0 = t_begin + i * kLT;
+    prologue_full(raw);
+    load_z(t0);
+    if (i + 1 < n_full) fetch(raw, t0 + kLT);
+    __syncthreads();
+    halves(t0, kLT, true);
+    __syncthreads();  // LDS tiles free for the next prologue
   }
   // ---- the rest: one partial tile, or every tile when rows do not allow 16-byte access
   for (int64_t t0 = t_begin + n_full * kLT; t0 < t_end; t0 += kLT) {
@@ -644,6 +674,14 @@ __global__ void __launch_bounds__(64 * NW, 2)
     __syncthreads();
   }
 
+  if constexpr (!SUMMARY) {
+    if (p.hfin && live && seg == p.nseg - 1) {
+      float* hf = p.hfin + (b * p.dim + d) * p.N + n0;
+#pragma unroll
+      for (int j = 0; j < NS; ++j)
+        if (n0 + j < p.N) hf[j] = h[j];
+    }
+  }
   if constexpr (SUMMARY) {
     if (live) {
       const int64_t base = (b * p.dim + d) * p.nseg + seg;
@@ -663,48 +701,44 @@ __global__ void __launch_bounds__(64 * NW, 2)
       static_cast<const IO*>(p.C), static_cast<const IO*>(p.z), static_cast<IO*>(p.y), p.A,  \
       p.D, p.delta_bias, p.hend, p.dsum, p
 
-template <typename IO, int NS, int NW, bool HEAD>
-static hipError_t launch_cfg(const ScanParams& p, hipStream_t stream) {
+template <typename IO, int NS, int NW, bool HEAD, bool ZOH>
+hipError_t launch_cfg(const ScanParams& p, hipStream_t stream) {
   const dim3 block(64 * NW);
   const int64_t groups = p.batch * p.groups_per_batch;
   if (p.nseg > 1) {
     const dim3 grid_sum((unsigned)groups, (unsigned)(p.nseg - 1));
-    hipLaunchKernelGGL((scan_fwd_kernel<IO, NS, NW, HEAD, true, false>), grid_sum, block, 0,
+    hipLaunchKernelGGL((scan_fwd_kernel<IO, NS, NW, HEAD, true, false, ZOH>), grid_sum, block, 0,
                        stream, SCAN_ARGS(p));
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const dim3 grid((unsigned)groups, (unsigned)p.nseg);
   if (p.z)
-    hipLaunchKernelGGL((scan_fwd_kernel<IO, NS, NW, HEAD, false, true>), grid, block, 0, stream,
-                       SCAN_ARGS(p));
+    hipLaunchKernelGGL((scan_fwd_kernel<IO, NS, NW, HEAD, false, true, ZOH>), grid, block, 0,
+                       stream, SCAN_ARGS(p));
   else
-    hipLaunchKernelGGL((scan_fwd_kernel<IO, NS, NW, HEAD, false, false>), grid, block, 0, stream,
-                       SCAN_ARGS(p));
+    hipLaunchKernelGGL((scan_fwd_kernel<IO, NS, NW, HEAD, false, false, ZOH>), grid, block, 0,
+                       stream, SCAN_ARGS(p));
   return hipGetLastError();
 }
 
+template <typename IO, int NS, int NW, bool HEAD>
+hipError_t launch_disc(const ScanParams& p, hipStream_t stream) {
+  return p.zoh ? launch_cfg<IO, NS, NW, HEAD, true>(p, stream)
+               : launch_cfg<IO, NS, NW, HEAD, false>(p, stream);
+}
+
+// States per wavefront for dstate N: N / 4 rounded up to a power of two.
 template <typename IO, bool HEAD>
-static hipError_t launch_n(const ScanParams& p, hipStream_t stream) {
+hipError_t launch_n(const ScanParams& p, hipStream_t stream) {
+  static_assert(kWavesPerGroup == 4, "the state split below assumes four wavefronts");
   const int64_t N = p.N;
-  if (N <= 4) return launch_cfg<IO, 1, 4, HEAD>(p, stream);
-  if (N <= 8) return launch_cfg<IO, 2, 4, HEAD>(p, stream);
-  if (N <= 16) return launch_cfg<IO, 4, 4, HEAD>(p, stream);
-  if (N <= 32) return launch_cfg<IO, 8, 4, HEAD>(p, stream);
-  if (N <= 64) return launch_cfg<IO, 16, 4, HEAD>(p, stream);
-  return launch_cfg<IO, 32, 4, HEAD>(p, stream);  // N <= 128 (checked by the caller)
+  if (N <= 4) return launch_disc<IO, 1, 4, HEAD>(p, stream);
+  if (N <= 8) return launch_disc<IO, 2, 4, HEAD>(p, stream);
+  if (N <= 16) return launch_disc<IO, 4, 4, HEAD>(p, stream);
+  if (N <= 32) return launch_disc<IO, 8, 4, HEAD>(p, stream);
+  if (N <= 64) return launch_disc<IO, 16, 4, HEAD>(p, stream);
+  return launch_disc<IO, 32, 4, HEAD>(p, stream);  // N <= 128 (checked by the caller)
 }
-
-hipError_t launch_scan_fwd(const ScanParams& p, bool bf16, bool head, hipStream_t stream) {
-  if (bf16) return head ? launch_n<bf16_bits, true>(p, stream) : launch_n<bf16_bits, false>(p, stream);
-  return head ? launch_n<float, true>(p, stream) : launch_n<float, false>(p, stream);
-}
-
-// Segments along L start at multiples of this many steps.
-int time_tile() { return kLT; }
-
-// Channels per workgroup of the kernel that launch_scan_fwd picks for dstate N.
-int channels_per_group(int64_t) { return kChannelsPerGroup; }
-int waves_per_group(int64_t) { return 4; }
 
 }  // namespace ssm

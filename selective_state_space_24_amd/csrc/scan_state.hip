@@ -1,0 +1,25 @@
+// The final state of a scan with no time steps: a copy of the initial state, or zeros. A plain
+// kernel rather than a runtime memset or copy, so that callers may capture the call in a graph.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "scan_internal.h"
+
+namespace ssm {
+
+__global__ void __launch_bounds__(256) state_copy_kernel(const float* __restrict__ src,
+                                                         float* __restrict__ dst, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    dst[i] = src ? src[i] : 0.0f;
+}
+
+hipError_t launch_state_copy(const float* src, float* dst, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  const unsigned grid = (unsigned)(blocks < 4096 ? blocks : 4096);
+  hipLaunchKernelGGL(state_copy_kernel, dim3(grid), dim3(256), 0, stream, src, dst, n);
+  return hipGetLastError();
+}
+
+}  // namespace ssm

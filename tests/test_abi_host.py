@@ -24,15 +24,16 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert {"ssm_selective_scan_fwd", "ssm_selective_scan_workspace_size", "ssm_status_string",
-            "ssm_abi_version", "ssm_scan_desc_init_contiguous"} <= set(names)
+    assert {"ssm_selective_scan_fwd", "ssm_selective_scan_fwd_ext",
+            "ssm_selective_scan_workspace_size", "ssm_status_string", "ssm_abi_version",
+            "ssm_scan_desc_init_contiguous"} <= set(names)
     h = ctypes.CDLL(ssm.LIB_PATH)
     for n in names:
         assert hasattr(h, n), n
 
 
 def test_version_and_status_strings():
-    assert ssm.abi_version() == 1
+    assert ssm.abi_version() == 2
     for code in range(-9, 1):
         s = ssm.status_string(code)
         assert s and s != "unknown status"
@@ -42,6 +43,8 @@ def test_version_and_status_strings():
 def test_desc_size_matches_header():
     # 6 int64 + 2 int32 + 14 int64 strides
     assert ctypes.sizeof(ssm.ScanDesc) == 6 * 8 + 2 * 4 + 14 * 8
+    # 2 int32 + 2 pointers
+    assert ctypes.sizeof(ssm.ScanExt) == 2 * 4 + 2 * 8
 
 
 FAKE = 1 << 40  # never dereferenced: every call below must fail validation first
@@ -99,6 +102,44 @@ def test_validation_errors_are_reported_before_launch():
     assert _fwd(big, ws=FAKE + (20 << 30), wsb=need - 4) == -7
     g = ssm.desc_contiguous(1, 64, 128, 16, ngroups=8)     # B/C group of 8 channels: unsupported
     assert _fwd(g) == -9
+
+
+def _fwd_ext(desc, ext, **over):
+    args = dict(x=FAKE, delta=FAKE + (1 << 30), A=FAKE + (2 << 30), B=FAKE + (3 << 30),
+                C=FAKE + (4 << 30), D=None, z=None, delta_bias=None, y=FAKE + (8 << 30),
+                ws=None, wsb=0)
+    args.update(over)
+    return ssm.fwd_ext_raw(desc, args["x"], args["delta"], args["A"], args["B"], args["C"],
+                           args["D"], args["z"], args["delta_bias"], True, args["y"], ext,
+                           args["ws"], args["wsb"], None)
+
+
+def test_extended_entry_point_validation():
+    d = ssm.desc_contiguous(2, 64, 128, 16)
+    H0, HF = FAKE + (12 << 30), FAKE + (13 << 30)
+    assert _fwd_ext(d, ssm.ScanExt(2, 0, None, None)) == -3          # unknown discretisation
+    assert _fwd_ext(d, ssm.ScanExt(0, 1, None, None)) == -3          # reserved must be 0
+    assert _fwd_ext(d, ssm.ScanExt(1, 0, H0 + 2, None)) == -5        # h0 not fp32-aligned
+    assert _fwd_ext(d, ssm.ScanExt(1, 0, None, HF + 1)) == -5        # h_final not aligned
+    assert _fwd_ext(d, ssm.ScanExt(0, 0, H0, H0 + 64)) == -6         # h_final overlaps h0
+    assert _fwd_ext(d, ssm.ScanExt(0, 0, None, FAKE + 128)) == -6    # h_final overlaps x
+    assert _fwd_ext(d, ssm.ScanExt(0, 0, None, FAKE + (8 << 30))) == -6  # h_final overlaps y
+    assert _fwd_ext(d, ssm.ScanExt(0, 0, FAKE + (8 << 30) + 256, None)) == -6  # y overlaps h0
+    assert _fwd_ext(d, ssm.ScanExt(0, 0, None, None), x=None) == -1
+    big = ssm.desc_contiguous(1, 2048, 1 << 20, 16)
+    need = ssm.workspace_size(big)
+    assert _fwd_ext(big, None) == -7
+    assert _fwd_ext(big, None, ws=FAKE + 64, wsb=need) == -6          # workspace overlaps x
+    assert _fwd_ext(big, None, ws=FAKE + (20 << 30) + 2, wsb=need) == -5
+    # nothing to compute: no pointers needed, and no final state requested
+    e = ssm.desc_contiguous(0, 64, 128, 16)
+    assert ssm.fwd_ext_raw(e, None, None, None, None, None, None, None, None, 1, None,
+                           ssm.ScanExt(1, 0, None, None), None, 0, None) == 0
+    e = ssm.desc_contiguous(3, 64, 0, 16)
+    assert ssm.fwd_ext_raw(e, None, None, None, None, None, None, None, None, 1, None,
+                           ssm.ScanExt(0, 0, None, None), None, 0, None) == 0
+    assert ssm.fwd_ext_raw(e, None, None, None, None, None, None, None, None, 1, None,
+                           ssm.ScanExt(0, 0, H0, H0 + 64), None, 0, None) == -6
 
 
 def test_workspace_size_depends_only_on_shape():
