@@ -178,9 +178,10 @@ __device__ __forceinline__ float zoh_ratio(float dA, float w) {
 // HEAD: one A and one delta per head; SUMMARY: the segment summary pass (no readout, no y);
 // GATE: y is multiplied by silu(z); ZOH: zero-order-hold B discretisation (else delta * B).
 template <typename IO, int NS, int NW, bool HEAD, bool SUMMARY, bool GATE, bool ZOH>
-// Two workgroups fit a CU's LDS, so each SIMD holds at most two of these wavefronts: the second
-// launch bound lets the compiler use the registers that this occupancy leaves.
-__global__ void __launch_bounds__(64 * NW, 2)
+// At most two workgroups fit a CU's LDS (one once the B/C tile holds more than 16 states), so
+// each SIMD holds at most two (one) of these wavefronts: the second launch bound lets the
+// compiler use the registers that this occupancy leaves.
+__global__ void __launch_bounds__(64 * NW, NS <= 4 ? 2 : 1)
     scan_fwd_kernel(const IO* __restrict__ X, const IO* __restrict__ DL, const IO* __restrict__ Bm,
                     const IO* __restrict__ Cm, const IO* __restrict__ Z, IO* __restrict__ Y,
                     const float* __restrict__ Am, const float* __restrict__ Dm,
@@ -448,35 +449,17 @@ __global__ void __launch_bounds__(64 * NW, 2)
     }
   };
 
-  // the recurrence over steps [h0, h0 + tb_len) of the load tile: lane = channel.
-  // A block is 8 steps: this lane's (delta, u) pairs and, for each of the wavefront's states,
-  // B and C at those steps (the same values in every lane, read with wave-uniform addresses).
-  struct Blk {
-    f32x4 du[4];
-    f32x4 bc[NS][SUMMARY ? 2 : 4];
-  };
-  auto load_blk = [&](Blk& k, int h0, int tt) __attribute__((always_inline)) {
+  // the recurrence over steps [h0, h0 + tb_len) of the load tile: lane = channel. A block is
+  // 8 steps: this lane's (delta, u) pairs, then for each of the wavefront's states B and C at
+  // those steps (the same values in every lane, read with wave-uniform addresses) just before
+  // that state's arithmetic, which bounds the registers for many states per wavefront.
+  auto step8 = [&](int h0, int tt) __attribute__((always_inline)) {
+    float dl[8], u[8];
     const f32x4* src = reinterpret_cast<const f32x4*>(&s_du[lane * kDuStrideL + 2 * (h0 + tt)]);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) k.du[q] = src[q];
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const f32x4* bq = reinterpret_cast<const f32x4*>(&s_B[(n0 + j) * kBcStrideL + h0 + tt]);
-      k.bc[j][0] = bq[0];
-      k.bc[j][1] = bq[1];
-      if constexpr (!SUMMARY) {
-        const f32x4* cq = reinterpret_cast<const f32x4*>(&s_C[(n0 + j) * kBcStrideL + h0 + tt]);
-        k.bc[j][2] = cq[0];
-        k.bc[j][3] = cq[1];
-      }
-    }
-  };
-  auto comp_blk = [&](const Blk& k, int tt) __attribute__((always_inline)) {
-    float dl[8], u[8];
-#pragma unroll
     for (int q = 0; q < 4; ++q) {
-      dl[2 * q] = k.du[q].x; u[2 * q] = k.du[q].y;
-      dl[2 * q + 1] = k.du[q].z; u[2 * q + 1] = k.du[q].w;
+      const f32x4 v = src[q];
+      dl[2 * q] = v.x; u[2 * q] = v.y; dl[2 * q + 1] = v.z; u[2 * q + 1] = v.w;
     }
     float acc[8];
     float dA_head[HEAD ? 8 : 1], g_head[HEAD && ZOH ? 8 : 1];
@@ -495,12 +478,15 @@ __global__ void __launch_bounds__(64 * NW, 2)
     }
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
-      const float bv[8] = {k.bc[j][0].x, k.bc[j][0].y, k.bc[j][0].z, k.bc[j][0].w,
-                           k.bc[j][1].x, k.bc[j][1].y, k.bc[j][1].z, k.bc[j][1].w};
+      const f32x4* bq = reinterpret_cast<const f32x4*>(&s_B[(n0 + j) * kBcStrideL + h0 + tt]);
+      const f32x4 b0 = bq[0], b1 = bq[1];
+      const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
       float cv[8];
       if constexpr (!SUMMARY) {
-        cv[0] = k.bc[j][2].x; cv[1] = k.bc[j][2].y; cv[2] = k.bc[j][2].z; cv[3] = k.bc[j][2].w;
-        cv[4] = k.bc[j][3].x; cv[5] = k.bc[j][3].y; cv[6] = k.bc[j][3].z; cv[7] = k.bc[j][3].w;
+        const f32x4* cq = reinterpret_cast<const f32x4*>(&s_C[(n0 + j) * kBcStrideL + h0 + tt]);
+        const f32x4 c0 = cq[0], c1 = cq[1];
+        cv[0] = c0.x; cv[1] = c0.y; cv[2] = c0.z; cv[3] = c0.w;
+        cv[4] = c1.x; cv[5] = c1.y; cv[6] = c1.z; cv[7] = c1.w;
       }
       float dA[8], ub[8];
 #pragma unroll
@@ -594,11 +580,7 @@ __global__ void __launch_bounds__(64 * NW, 2)
         return;
       }
     }
-    for (int tt = 0; tt < tb_len; tt += 8) {
-      Blk k;
-      load_blk(k, h0, tt);
-      comp_blk(k, tt);
-    }
+    for (int tt = 0; tt < tb_len; tt += 8) step8(h0, tt);
   };
 
   // y = (sum of the partial readouts + D x) * silu(z) for half hf
