@@ -14,8 +14,10 @@ HBM figures beside it (algorithmic bytes and, when a counter profile of the curr
 is committed, counted bytes, against the 8 TB/s peak); and the fp64 CPU oracle timed on the host
 cores over whole batch entries of the same workload.
 
-``--copy-calibration`` runs only a plain device copy of a known size (for scaling the
-FETCH_SIZE / WRITE_SIZE counters of a profiler run).
+``--workload decode`` measures instead one recurrent decoding step (``ssm_selective_state_update``)
+on the Mamba-1.4B layer at batch 1024: a step reads and writes the fp32 state once, so its
+roofline is HBM bandwidth. ``--copy-calibration`` runs only a plain device copy of a known size
+(for scaling the FETCH_SIZE / WRITE_SIZE counters of a profiler run).
 """
 from __future__ import annotations
 
@@ -151,6 +153,99 @@ def cpu_baseline(cfg, budget_s: float):
     }
 
 
+def decode_bytes(cfg) -> int:
+    """Algorithmic bytes of one decoding step: the fp32 state read and written, every other
+    input read once and y written once."""
+    return cfg.algorithmic_bytes() + 2 * cfg.batch * cfg.dim * cfg.N * 4
+
+
+def run_decode(args, torch):
+    import numpy as np
+    import ssmgen
+    import selective_state_space_24_amd as ssm
+    cfg = ssmgen.DECODE_CONFIGS["mamba14b_decode"]
+    dev = device_inputs(cfg, torch)
+    rng = np.random.default_rng(0)
+    state0 = rng.standard_normal((cfg.batch, cfg.dim, cfg.N)).astype(np.float32)
+    state = torch.from_numpy(state0).cuda()
+    sq = {k: (v[..., 0].contiguous() if k in ("x", "delta", "z", "B", "C") else v)
+          for k, v in dev.items()}
+    y = torch.empty_like(sq["x"])
+    stream = torch.cuda.current_stream()
+    desc = ssm.describe_step(state, sq["x"], sq["delta"], sq["A"], sq["B"], sq["C"], sq["z"], y)
+
+    def step():
+        rc = ssm.state_update_raw(desc, state.data_ptr(), sq["x"].data_ptr(), sq["delta"].data_ptr(),
+                                  sq["A"].data_ptr(), sq["B"].data_ptr(), sq["C"].data_ptr(),
+                                  sq["D"].data_ptr(), sq["z"].data_ptr(), sq["delta_bias"].data_ptr(),
+                                  True, y.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise ssm.ScanError(rc, "ssm_selective_state_update")
+
+    ms, pct = timed_steps(step, args, torch, stream)
+    nbytes = decode_bytes(cfg)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "selective-SSM decode step: tokens/s and achieved HBM GB/s vs peak, 1 MI355X",
+        "value": round(cfg.batch / (ms * 1e-3), 1),
+        "unit": "tokens/s (one token per sequence per step, one layer)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "Mamba-1.4B layer decode step", "batch": cfg.batch,
+                   "d_inner": cfg.dim, "d_state": cfg.N, "io_dtype": cfg.io,
+                   "state": "fp32, updated in place", "gate": "silu(z)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profile("mamba14b_decode")},
+        "algorithmic_bytes_per_step": nbytes,
+        "step_ms": {"p10": round(pct(0.1), 5), "median": round(pct(0.5), 5),
+                    "p90": round(pct(0.9), 5)},
+        "launches_per_step": 1,
+        "kernel_source": kernel_source_hash(),
+    }
+    if args.cpu_budget > 0:
+        import oracle
+        threads = oracle.cpu_threads()
+        inputs = ssmgen.make_inputs(cfg)
+        spent, steps = 0.0, 0
+        h = state0.astype(np.float64)
+        while spent < args.cpu_budget and steps < 50:
+            t0 = time.perf_counter()
+            _, h = oracle.scan_inputs(inputs, cfg, h0=h, return_final_state=True,
+                                      nthreads=threads)
+            spent += time.perf_counter() - t0
+            steps += 1
+        out["cpu_baseline"] = {
+            "value": round(steps * cfg.batch / spent, 1), "unit": out["unit"], "cores": threads,
+            "kind": "oracle",
+            "sample": f"{steps} whole decoding steps of the workload (batch {cfg.batch}) in "
+                      f"{spent:.2f} s; input generation untimed"}
+    print(json.dumps(out), flush=True)
+
+
+def timed_steps(step, args, torch, stream):
+    """W untimed steps, then K steps between two synchronisations, timed with events on the
+    launch stream (each step also timed alone for percentiles)."""
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for s_ev, e_ev in ev:
+        s_ev.record(stream)
+        step()
+        e_ev.record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    per = sorted(s_ev.elapsed_time(e_ev) for s_ev, e_ev in ev)
+    pct = lambda q: per[min(len(per) - 1, int(q * (len(per) - 1) + 0.5))]
+    return ms, pct
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -159,6 +254,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 skips it)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--workload", choices=("scan", "decode"), default="scan")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -189,6 +285,10 @@ def main():
                           "ms": round(ms, 4), "GBs_read_plus_write": round(2 * nbytes / ms / 1e6, 1)}))
         return
 
+    if args.workload == "decode":
+        run_decode(args, torch)
+        return
+
     import ssmgen
     import selective_state_space_24_amd as ssm
 
@@ -208,22 +308,7 @@ def main():
         if rc != 0:
             raise ssm.ScanError(rc, "ssm_selective_scan_fwd")
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for s_ev, e_ev in ev:
-        s_ev.record(stream)
-        step()
-        e_ev.record(stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-    per = sorted(s_ev.elapsed_time(e_ev) for s_ev, e_ev in ev)
-    pct = lambda q: per[min(len(per) - 1, int(q * (len(per) - 1) + 0.5))]
+    ms, pct = timed_steps(step, args, torch, stream)
 
     # one launch per step when the sequence is not split along L (no workspace needed)
     launches = 1 if ws_bytes == 0 else 2

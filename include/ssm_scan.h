@@ -151,6 +151,20 @@ int ssm_selective_scan_fwd_ext(const ssm_scan_desc* desc, const void* x, const v
                                void* y, const ssm_scan_ext* ext, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* One recurrent step per sequence, for decoding one token at a time: the state carries the
+ * whole history, so each step costs the same whatever the position (page "NL-345", §1
+ * "Selection Mechanism" and §2 "Computation": the recurrent mode of a selective SSM).
+ *   `desc` describes a scan with seqlen == 1 (SSM_ERR_BAD_SHAPE otherwise): x, delta, z, y are
+ *   (batch, dim | nheads, 1) and B, C (batch, ngroups, dstate, 1), with the usual strides.
+ *   state (batch, dim, dstate) fp32 contiguous is read and overwritten in place:
+ *     state <- exp(delta A) state + delta B x,   y = C.state + D x   (times silu(z))
+ *   with delta = softplus(delta_raw + delta_bias) as in the scan; B_bar is delta * B.
+ * state and y must not overlap any input or each other. Asynchronous on `stream`; no workspace. */
+int ssm_selective_state_update(const ssm_scan_desc* desc, float* state, const void* x,
+                               const void* delta, const float* A, const void* B, const void* C,
+                               const float* D, const void* z, const float* delta_bias,
+                               int32_t delta_softplus, void* y, void* stream);
+
 /* SSM_SCAN_ABI_VERSION of the built library. */
 int ssm_abi_version(void);
 

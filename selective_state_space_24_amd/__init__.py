@@ -78,6 +78,8 @@ def lib():
         h.ssm_selective_scan_fwd_ext.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
                                                  ctypes.POINTER(ScanExt), vp, sz, vp]
         h.ssm_selective_scan_fwd_ext.restype = ctypes.c_int
+        h.ssm_selective_state_update.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]
+        h.ssm_selective_state_update.restype = ctypes.c_int
         h.ssm_status_string.argtypes = [ctypes.c_int]
         h.ssm_status_string.restype = ctypes.c_char_p
         h.ssm_abi_version.argtypes = []
@@ -127,6 +129,13 @@ def fwd_ext_raw(desc: ScanDesc, x, delta, A, B, C, D, z, delta_bias, delta_softp
     return int(lib().ssm_selective_scan_fwd_ext(
         ctypes.byref(desc), x, delta, A, B, C, D, z, delta_bias, int(bool(delta_softplus)), y,
         ctypes.byref(ext) if ext is not None else None, workspace, int(workspace_bytes), stream))
+
+
+def state_update_raw(desc: ScanDesc, state, x, delta, A, B, C, D, z, delta_bias,
+                     delta_softplus: bool, y, stream) -> int:
+    """Direct call of ``ssm_selective_state_update``; returns the status code without raising."""
+    return int(lib().ssm_selective_state_update(ctypes.byref(desc), state, x, delta, A, B, C, D, z,
+                                                delta_bias, int(bool(delta_softplus)), y, stream))
 
 
 # ---------------------------------------------------------------------------------------------
@@ -241,3 +250,37 @@ def selective_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta
     if rc != SSM_OK:
         raise ScanError(rc, "ssm_selective_scan_fwd")
     return (y, hfin) if hfin is not None else y
+
+
+def describe_step(state, x, delta, A, B, C, z=None, y=None) -> ScanDesc:
+    """Descriptor (seqlen 1) of one decoding step: x, z, y (batch, dim); delta (batch, dim) or
+    (batch, nheads); B, C (batch, ngroups, N); state (batch, dim, N) float32."""
+    x3, d3 = x.unsqueeze(-1), delta.unsqueeze(-1)
+    B4, C4 = B.unsqueeze(-1), C.unsqueeze(-1)
+    desc = describe(x3, d3, A, B4, C4, None if z is None else z.unsqueeze(-1),
+                    None if y is None else y.unsqueeze(-1))
+    if tuple(state.shape) != (desc.batch, desc.dim, desc.dstate):
+        raise ValueError(f"state must be {(desc.batch, desc.dim, desc.dstate)}, got {tuple(state.shape)}")
+    return desc
+
+
+def selective_state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None,
+                           delta_softplus=True, *, out=None, stream=None):
+    """One recurrent step per sequence (see ``ssm_selective_state_update``): updates ``state``
+    (batch, dim, N) float32 in place and returns y (batch, dim) in the dtype of x."""
+    import torch
+    if state.dtype != torch.float32 or not state.is_contiguous():
+        raise TypeError("state must be a contiguous float32 tensor")
+    for name, t in (("D", D), ("delta_bias", delta_bias)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise TypeError(f"{name} must be a contiguous float32 tensor")
+    y = out if out is not None else torch.empty_like(x, memory_format=torch.contiguous_format)
+    desc = describe_step(state, x, delta, A, B, C, z, y)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    sp = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    rc = state_update_raw(desc, _ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                          _ptr(D), _ptr(z), _ptr(delta_bias), delta_softplus, _ptr(y), sp)
+    if rc != SSM_OK:
+        raise ScanError(rc, "ssm_selective_state_update")
+    return y

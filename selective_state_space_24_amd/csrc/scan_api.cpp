@@ -293,4 +293,70 @@ int ssm_selective_scan_fwd(const ssm_scan_desc* desc, const void* x, const void*
                                     nullptr, workspace, workspace_bytes, stream);
 }
 
+int ssm_selective_state_update(const ssm_scan_desc* desc, float* state, const void* x,
+                               const void* delta, const float* A, const void* B, const void* C,
+                               const float* D, const void* z, const float* delta_bias,
+                               int32_t delta_softplus, void* y, void* stream) {
+  int rc = check_desc(desc);
+  if (rc != SSM_OK) return rc;
+  const ssm_scan_desc& d = *desc;
+  if (d.seqlen != 1) return SSM_ERR_BAD_SHAPE;
+  if (d.batch == 0) return SSM_OK;
+  if (!state || !x || !delta || !A || !B || !C || !y) return SSM_ERR_NULL_ARG;
+
+  const bool bf16 = d.io_dtype == SSM_DTYPE_BF16;
+  const bool head = d.a_mode == SSM_A_HEAD;
+  const size_t es = bf16 ? 2 : 4;
+  const int64_t nheads = d.dim / d.headdim;
+  const int64_t drows = head ? nheads : d.dim;
+  const void* io_ptrs[] = {x, delta, B, C, z, y};
+  for (const void* p : io_ptrs)
+    if (p && !aligned(p, es)) return SSM_ERR_MISALIGNED;
+  const void* f32_ptrs[] = {A, D, delta_bias, state};
+  for (const void* p : f32_ptrs)
+    if (p && !aligned(p, 4)) return SSM_ERR_MISALIGNED;
+
+  const size_t y_bytes = (size_t)extent3(d.batch, d.dim, 1, d.y_stride_batch, d.y_stride_dim) * es;
+  const size_t state_bytes = (size_t)d.batch * d.dim * d.dstate * sizeof(float);
+  const size_t in_bytes[] = {
+      (size_t)extent3(d.batch, d.dim, 1, d.x_stride_batch, d.x_stride_dim) * es,
+      (size_t)extent3(d.batch, drows, 1, d.delta_stride_batch, d.delta_stride_dim) * es,
+      (size_t)extent4(d.batch, d.ngroups, d.dstate, 1, d.B_stride_batch, d.B_stride_group, d.B_stride_state) * es,
+      (size_t)extent4(d.batch, d.ngroups, d.dstate, 1, d.C_stride_batch, d.C_stride_group, d.C_stride_state) * es,
+      z ? (size_t)extent3(d.batch, d.dim, 1, d.z_stride_batch, d.z_stride_dim) * es : 0,
+      (size_t)(head ? nheads : d.dim * d.dstate) * 4,
+      D ? (size_t)d.dim * 4 : 0,
+      delta_bias ? (size_t)drows * 4 : 0};
+  const void* in_ptrs[] = {x, delta, B, C, z, A, D, delta_bias};
+  for (int i = 0; i < 8; ++i) {
+    if (overlaps(y, y_bytes, in_ptrs[i], in_bytes[i])) return SSM_ERR_ALIAS;
+    if (overlaps(state, state_bytes, in_ptrs[i], in_bytes[i])) return SSM_ERR_ALIAS;
+  }
+  if (overlaps(state, state_bytes, y, y_bytes)) return SSM_ERR_ALIAS;
+
+  ssm::ScanParams p;
+  memset(&p, 0, sizeof(p));
+  p.x = x; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.delta_bias = delta_bias;
+  p.y = y; p.h0 = state; p.hfin = state;
+  p.batch = d.batch; p.dim = d.dim; p.L = 1; p.N = d.dstate; p.ngroups = d.ngroups;
+  p.headdim = d.headdim;
+  p.x_sb = d.x_stride_batch; p.x_sd = d.x_stride_dim;
+  p.dl_sb = d.delta_stride_batch; p.dl_sd = d.delta_stride_dim;
+  p.B_sb = d.B_stride_batch; p.B_sg = d.B_stride_group; p.B_sn = d.B_stride_state;
+  p.C_sb = d.C_stride_batch; p.C_sg = d.C_stride_group; p.C_sn = d.C_stride_state;
+  p.z_sb = d.z_stride_batch; p.z_sd = d.z_stride_dim;
+  p.y_sb = d.y_stride_batch; p.y_sd = d.y_stride_dim;
+  p.softplus = delta_softplus ? 1 : 0;
+  p.state_vec = (d.dstate % 4 == 0 && aligned(state, 16)) ? 1 : 0;
+  p.a_vec = (!head && d.dstate % 4 == 0 && aligned(A, 16)) ? 1 : 0;
+  // 4 consecutive states of B and C in one 8- (bf16) or 16-byte (fp32) load
+  const bool bc4 = d.B_stride_state == 1 && d.C_stride_state == 1 && d.dstate % 4 == 0 &&
+                   d.B_stride_batch % 4 == 0 && d.B_stride_group % 4 == 0 &&
+                   d.C_stride_batch % 4 == 0 && d.C_stride_group % 4 == 0 &&
+                   aligned(B, 4 * es) && aligned(C, 4 * es);
+  p.bc_vec = bc4 ? 1 : 0;
+  const hipError_t e = ssm::launch_decode(p, bf16, head, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 }  // extern "C"

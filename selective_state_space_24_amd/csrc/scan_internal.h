@@ -41,6 +41,8 @@ struct ScanParams {
   int32_t vec_io;            // x/delta/z/y rows allow 16-byte vector access
   int32_t bc_vec;            // B/C rows allow 16-byte vector access
   int32_t zoh;               // zero-order-hold B discretisation instead of delta * B
+  int32_t state_vec;         // decode: the state allows 16-byte access (N % 4 == 0, aligned)
+  int32_t a_vec;             // decode: rows of A allow 16-byte access
 };
 
 // One launcher per (io dtype, A mode); each is compiled in its own translation unit.
@@ -48,6 +50,8 @@ hipError_t launch_bf16_diag(const ScanParams& p, hipStream_t stream);
 hipError_t launch_bf16_head(const ScanParams& p, hipStream_t stream);
 hipError_t launch_f32_diag(const ScanParams& p, hipStream_t stream);
 hipError_t launch_f32_head(const ScanParams& p, hipStream_t stream);
+// one recurrent step per sequence: reads the state at h0, writes it at hfin (may be equal)
+hipError_t launch_decode(const ScanParams& p, bool bf16, bool head, hipStream_t stream);
 // dst[0, n) = src[0, n), or zeros when src is null
 hipError_t launch_state_copy(const float* src, float* dst, int64_t n, hipStream_t stream);
 

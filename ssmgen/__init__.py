@@ -193,6 +193,16 @@ CONFIGS: Dict[int, ScanConfig] = {
 }
 
 
+# Decoding workloads (one step per sequence, L = 1; the state is an extra fp32 input/output).
+DECODE_CONFIGS: Dict[str, ScanConfig] = {
+    "mamba14b_decode": ScanConfig(name="mamba-1.4b layer decode: batch 1024, d_inner 4096, N 16",
+                                  batch=1024, dim=4096, L=1, N=16, seed=SEED_BASE + 16),
+    "heads_decode": ScanConfig(name="scalar-decay heads decode: batch 64, 64 heads x 64, N 128",
+                               batch=64, dim=4096, L=1, N=128, headdim=64, a_mode="head",
+                               seed=SEED_BASE + 17),
+}
+
+
 def make_tensor(cfg: ScanConfig, name: str, nthreads: Optional[int] = None) -> np.ndarray:
     shp = cfg.shapes()[name]
     d = cfg.dist_of(name)

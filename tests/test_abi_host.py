@@ -142,6 +142,25 @@ def test_extended_entry_point_validation():
                            ssm.ScanExt(0, 0, H0, H0 + 64), None, 0, None) == -6
 
 
+def test_state_update_validation():
+    S = FAKE + (16 << 30)
+    def call(desc, **over):
+        args = dict(state=S, x=FAKE, delta=FAKE + (1 << 30), A=FAKE + (2 << 30),
+                    B=FAKE + (3 << 30), C=FAKE + (4 << 30), y=FAKE + (8 << 30))
+        args.update(over)
+        return ssm.state_update_raw(desc, args["state"], args["x"], args["delta"], args["A"],
+                                    args["B"], args["C"], None, None, None, True, args["y"], None)
+    d = ssm.desc_contiguous(4, 64, 1, 16)
+    assert call(ssm.desc_contiguous(4, 64, 2, 16)) == -2       # one step only
+    assert call(d, state=None) == -1
+    assert call(d, y=None) == -1
+    assert call(d, state=S + 2) == -5
+    assert call(d, state=FAKE + 16) == -6                      # state overlaps x
+    assert call(d, state=FAKE + (8 << 30)) == -6               # state overlaps y
+    assert call(d, y=FAKE + (2 << 30) + 64) == -6              # y overlaps A
+    assert call(ssm.desc_contiguous(0, 64, 1, 16), state=None, x=None) == 0
+
+
 def test_workspace_size_depends_only_on_shape():
     assert ssm.workspace_size(ssm.desc_contiguous(8, 4096, 4096, 16)) == 0
     c3 = ssm.workspace_size(ssm.desc_contiguous(1, 2048, 1 << 20, 16))

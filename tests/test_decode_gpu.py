@@ -1,0 +1,101 @@
+"""The single-step recurrent update (ssm_selective_state_update) against the fp64 oracle run with
+L = 1 and an initial state, and a loop of steps against the oracle and the scan kernel over the
+same sequence (needs an MI355X).
+
+Tolerances: y as in the scan tests (1e-4 fp32 I/O, 2e-2 bf16 I/O); the fp32 state within 1e-4.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import ssmgen
+from scan_cases import TOL, device_inputs, y_to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+STATE_TOL = 1e-4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import selective_state_space_24_amd as ssm
+    ssm.lib()  # fails loudly if the HIP library is not built
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _cfg(batch, dim, L, N, headdim=1, a_mode="diag", io="bf16", gate=True, sp=True, D=True,
+         bias=True, G=1, seed=11):
+    dists = {} if sp else {"delta": ssmgen.Dist(ssmgen.UNIFORM, 0.0, 0.2),
+                           "delta_bias": ssmgen.Dist(ssmgen.UNIFORM, 0.001, 0.01)}
+    return ssmgen.ScanConfig(name="decode", batch=batch, dim=dim, L=L, N=N, ngroups=G,
+                             headdim=headdim, a_mode=a_mode, io=io, gate=gate, softplus=sp,
+                             has_D=D, has_bias=bias, seed=seed, dists=dists)
+
+
+def _step(dev, t, state, cfg):
+    import selective_state_space_24_amd as ssm
+    sl = lambda k: dev[k][..., t].contiguous() if k in dev else None
+    return ssm.selective_state_update(state, sl("x"), sl("delta"), dev["A"], sl("B"), sl("C"),
+                                      dev.get("D"), sl("z"), dev.get("delta_bias"), cfg.softplus)
+
+
+CASES = [
+    # batch, dim, N, headdim, a_mode, io, gate, softplus, D, bias, groups
+    (4, 512, 16, 1, "diag", "bf16", True, True, True, True, 1),
+    (3, 100, 16, 1, "diag", "f32", True, True, True, True, 1),
+    (2, 96, 5, 1, "diag", "f32", False, False, False, False, 1),     # scalar state path
+    (2, 256, 128, 64, "head", "bf16", True, True, True, True, 1),
+    (1, 128, 64, 2, "head", "f32", True, True, False, True, 2),
+    (5, 64, 1, 1, "diag", "f32", True, True, True, True, 1),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_one_step_matches_oracle(case):
+    batch, dim, N, hd, mode, io, gate, sp, D, bias, G = case
+    cfg = _cfg(batch, dim, 1, N, hd, mode, io, gate, sp, D, bias, G, seed=31 + N)
+    _say(f"[decode] {case}")
+    inputs = ssmgen.make_inputs(cfg)
+    h0 = np.random.default_rng(N).standard_normal((batch, dim, N)).astype(np.float32)
+    dev = device_inputs(inputs)
+    state = torch.from_numpy(h0).cuda()
+    y = _step(dev, 0, state, cfg)
+    torch.cuda.synchronize()
+    yref, href = oracle.scan_inputs(inputs, cfg, h0=h0.astype(np.float64), return_final_state=True)
+    assert oracle.rel_err(y_to_f64(y), yref[..., 0]) <= TOL[io]
+    assert oracle.rel_err(state.cpu().numpy().astype(np.float64), href) <= STATE_TOL
+
+
+@pytest.mark.parametrize("io,mode,N,hd", [("f32", "diag", 16, 1), ("bf16", "head", 128, 64)])
+def test_step_loop_equals_scan(io, mode, N, hd):
+    """Twelve steps one at a time = the scan over the twelve steps (oracle and scan kernel)."""
+    import selective_state_space_24_amd as ssm
+    L = 12
+    cfg = _cfg(2, 128, L, N, hd, mode, io, seed=5)
+    _say(f"[decode] loop {io} {mode}")
+    inputs = ssmgen.make_inputs(cfg)
+    dev = device_inputs(inputs)
+    h0 = np.random.default_rng(1).standard_normal((2, 128, N)).astype(np.float32)
+    state = torch.from_numpy(h0).cuda()
+    ys = [y_to_f64(_step(dev, t, state, cfg)) for t in range(L)]
+    torch.cuda.synchronize()
+    y_steps = np.stack(ys, axis=-1)
+    yref, href = oracle.scan_inputs(inputs, cfg, h0=h0.astype(np.float64), return_final_state=True)
+    assert oracle.rel_err(y_steps, yref) <= TOL[io]
+    assert oracle.rel_err(state.cpu().numpy().astype(np.float64), href) <= STATE_TOL
+    y_scan, h_scan = ssm.selective_scan_fwd(dev["x"], dev["delta"], dev["A"], dev["B"], dev["C"],
+                                            dev.get("D"), dev.get("z"), dev.get("delta_bias"),
+                                            True, h0=torch.from_numpy(h0).cuda(), final_state=True)
+    torch.cuda.synchronize()
+    assert oracle.rel_err(y_steps, y_to_f64(y_scan)) <= TOL[io]
+    assert oracle.rel_err(state.cpu().numpy().astype(np.float64),
+                          h_scan.cpu().numpy().astype(np.float64)) <= STATE_TOL
