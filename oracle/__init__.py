@@ -45,6 +45,8 @@ def load_library(path: str):
     i64, ci = ctypes.c_int64, ctypes.c_int
     lib.ssm_oracle_scan.argtypes = [i64, i64, i64, i64, i64, i64, ci, ci, ci] + [_dp] * 11 + [ci]
     lib.ssm_oracle_scan.restype = ci
+    lib.ssm_oracle_scan_bwd.argtypes = [i64, i64, i64, i64, i64, i64, ci, ci, ci] + [_dp] * 19 + [ci]
+    lib.ssm_oracle_scan_bwd.restype = ci
     return lib
 
 
@@ -115,6 +117,48 @@ def selective_scan(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_sof
     if rc != 0:
         raise ValueError("oracle rejected the problem sizes")
     return (y, hT) if return_final_state else y
+
+
+def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                       dy=None, *, headdim: int = 1, head_mode: bool = False, zoh: bool = False,
+                       h0=None, nthreads: Optional[int] = None, lib=None) -> dict:
+    """fp64 gradients of ``selective_scan`` with respect to every input, given ``dy`` (the
+    gradient of y, shaped like x). Returns a dict with dx, ddelta, dA, dB, dC, and dD, dz,
+    ddelta_bias, dh0 for the optional inputs that were given."""
+    x, delta, A, B, C = (as_f64(t) for t in (x, delta, A, B, C))
+    D, z, delta_bias, h0, dy = (as_f64(t) for t in (D, z, delta_bias, h0, dy))
+    batch, dim, L = x.shape
+    _, ngroups, N, _ = B.shape
+    out = {"dx": np.empty_like(x), "ddelta": np.empty_like(delta), "dA": np.empty_like(A),
+           "dB": np.empty_like(B), "dC": np.empty_like(C)}
+    if D is not None:
+        out["dD"] = np.empty_like(D)
+    if z is not None:
+        out["dz"] = np.empty_like(z)
+    if delta_bias is not None:
+        out["ddelta_bias"] = np.empty_like(delta_bias)
+    if h0 is not None:
+        out["dh0"] = np.empty_like(h0)
+    rc = (lib or _load()).ssm_oracle_scan_bwd(
+        batch, dim, L, N, ngroups, headdim, int(head_mode), int(bool(delta_softplus)), int(zoh),
+        _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+        _ptr(h0), _ptr(dy), _ptr(out["dx"]), _ptr(out["ddelta"]), _ptr(out["dA"]),
+        _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out.get("dD")), _ptr(out.get("dz")),
+        _ptr(out.get("ddelta_bias")), _ptr(out.get("dh0")), nthreads or cpu_threads())
+    if rc != 0:
+        raise ValueError("oracle backward rejected the problem sizes")
+    return out
+
+
+def scan_inputs_bwd(inputs: dict, dy, cfg=None, **kw) -> dict:
+    """``selective_scan_bwd`` on a dict of generated inputs."""
+    if cfg is not None:
+        kw.setdefault("headdim", cfg.headdim)
+        kw.setdefault("head_mode", cfg.a_mode == "head")
+        kw.setdefault("delta_softplus", cfg.softplus)
+    return selective_scan_bwd(inputs["x"], inputs["delta"], inputs["A"], inputs["B"], inputs["C"],
+                              inputs.get("D"), inputs.get("z"), inputs.get("delta_bias"),
+                              dy=dy, **kw)
 
 
 def scan_inputs(inputs: dict, cfg=None, **kw):

@@ -1,13 +1,19 @@
-"""Planted mistakes in copies of the oracle (built on the CPU) must each fail at least one pin."""
+"""Planted mistakes in copies of the oracle (built on the CPU) must each fail at least one pin.
+
+Forward mutants edit the forward section of the source (before the backward section's marker)
+and must fail a forward pin; backward mutants edit the backward section and must fail a
+backward pin (finite differences, torch autograd or the transposed-matrix closed form)."""
 import os
 import subprocess
 
 import pytest
 
 import oracle
+import oracle_bwd_pins as BP
 import oracle_pins as P
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ssm_oracle.c")
+BWD_MARK = "Gradients of the scan above"
 
 MUTANTS = {
     "drop_D": ("double yt = acc + Dd * xt;", "double yt = acc;"),
@@ -30,21 +36,63 @@ MUTANTS = {
 }
 
 
+BWD_MUTANTS = {
+    "bwd_no_decay_of_gh": ("gh[n] *= Abar;", ""),
+    "bwd_dC_with_previous_state": ("dCg[n * L + t] += gy * ht[n];", "dCg[n * L + t] += gy * hp[n];"),
+    "bwd_softplus_derivative_sign": ("gdelta * sigmoid(v)", "gdelta * sigmoid(-v)"),
+    "bwd_silu_derivative": ("s * (1.0 + zr[t] * (1.0 - s))", "s"),
+    "bwd_dA_without_delta": ("gh[n] * (delta * Abar * hp[n]", "gh[n] * (Abar * hp[n]"),
+    "bwd_dx_without_state_path": ("gx += gh[n] * Bbar;", ""),
+    "bwd_zoh_dBbar_ddelta": ("df_ddelta = Abar;", "df_ddelta = 1.0;"),
+    "bwd_dB_without_factor": ("dBg[n * L + t] += gh[n] * xt * f;", "dBg[n * L + t] += gh[n] * xt;"),
+    "bwd_gate_not_applied": ("gy = gyr[t] * zr[t] * s;", "gy = gyr[t];"),
+}
+
+
 @pytest.fixture(scope="module")
 def src():
     return open(SRC).read()
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_mutant_is_caught(name, src, tmp_path):
-    old, new = MUTANTS[name]
-    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+def _build(tmp_path, name, text):
     cpath = tmp_path / f"{name}.c"
-    cpath.write_text(src.replace(old, new))
+    cpath.write_text(text)
     so = tmp_path / f"{name}.so"
     subprocess.run(["gcc", "-O2", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off",
                     str(cpath), "-o", str(so), "-lm", "-lpthread"], check=True)
-    lib = oracle.load_library(str(so))
+    return oracle.load_library(str(so))
+
+
+def _mutate(src, old, new, backward):
+    cut = src.index(BWD_MARK)
+    head, tail = src[:cut], src[cut:]
+    part = tail if backward else head
+    assert part.count(old) == 1, f"mutation site not found exactly once: {old!r}"
+    part = part.replace(old, new)
+    return head + part if backward else part + tail
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_backward_mutant_is_caught(name, src, tmp_path):
+    old, new = BWD_MUTANTS[name]
+    lib = _build(tmp_path, name, _mutate(src, old, new, backward=True))
+
+    def bwd(*a, **k):
+        return oracle.selective_scan_bwd(*a, lib=lib, **k)
+
+    def fwd(*a, **k):
+        return oracle.selective_scan(*a, lib=lib, **k)
+    errs = [BP.finite_differences(bwd, fwd, head_mode=h, zoh=z, softplus=sp, gate=g)
+            for (h, z, sp, g) in [(False, False, True, True), (False, True, True, True),
+                                  (True, False, True, True)]]
+    errs.append(BP.dx_closed_form(bwd))
+    assert max(errs) > 1e-4, f"backward mutant {name} passed every pin: {errs}"
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, src, tmp_path):
+    old, new = MUTANTS[name]
+    lib = _build(tmp_path, name, _mutate(src, old, new, backward=False))
 
     def scan(*a, **k):
         return oracle.selective_scan(*a, lib=lib, **k)
