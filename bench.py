@@ -14,6 +14,7 @@ HBM figures beside it (algorithmic bytes and, when a counter profile of the curr
 is committed, counted bytes, against the 8 TB/s peak); and the fp64 CPU oracle timed on the host
 cores over whole batch entries of the same workload.
 
+``--workload bwd`` measures the backward pass (all input gradients) of the same workload.
 ``--workload decode`` measures instead one recurrent decoding step (``ssm_selective_state_update``)
 on the Mamba-1.4B layer at batch 1024: a step reads and writes the fp32 state once, so its
 roofline is HBM bandwidth. ``--copy-calibration`` runs only a plain device copy of a known size
@@ -153,6 +154,115 @@ def cpu_baseline(cfg, budget_s: float):
     }
 
 
+def alu_model_bwd(cfg):
+    """Minimal fp32 instruction stream of the gradient per token*channel: (flops, SIMD cycles),
+    costs as in ``alu_model`` (diagonal A, delta * B rule).
+      per state update: the states recomputed once (delta*a, exp2, u*B, fma: 5 flops, 14 cyc)
+        and the reverse step (gh += gy C; gy h for dC; exp2; h_prev dA; a h_prev dA + B x;
+        ddelta += gh (.); da += gh h_prev dA delta; gh u for dB; dx += gh delta B; gh *= dA:
+        18 flops, 12 plain ops + 1 transcendental = 32 cyc)
+      per (t, channel): softplus and its derivative sigmoid (14 flops, 44 cyc), u = delta*x,
+        the gate silu and silu' (12 flops, 34 cyc), y = readout + D x and dz (3 flops, 4 cyc),
+        dx += gy D, dD += gy x, dbias += (4 fma/add: 7 flops, 8 cyc)
+    The sums over lanes for dB and dC and over the batch are not counted."""
+    valu, trans = 2, 8
+    fl = cfg.N * (5 + 18)
+    cy = cfg.N * ((3 * valu + trans) + (12 * valu + trans))
+    if cfg.softplus:
+        fl += 14
+        cy += 10 * valu + 3 * trans
+    fl += 1
+    cy += valu
+    if cfg.gate:
+        fl += 12
+        cy += 9 * valu + 2 * trans
+    fl += 3 + 7
+    cy += 2 * valu + 4 * valu
+    return fl, cy
+
+
+def bwd_bytes(cfg) -> int:
+    """Algorithmic bytes of the backward pass: the forward's inputs and dy read once; dx, ddelta,
+    dz written in the io dtype; dB, dC (fp32), dA, dD, dbias written once."""
+    io = 4 if cfg.io == "f32" else 2
+    tok = cfg.batch * cfg.dim * cfg.L
+    reads = cfg.algorithmic_bytes() - tok * io  # forward inputs (without y)
+    reads += tok * io                           # dy
+    writes = tok * io * (3 if cfg.gate else 2)  # dx, ddelta, dz
+    writes += 2 * cfg.batch * cfg.ngroups * cfg.N * cfg.L * 4 + cfg.dim * cfg.N * 4 + 2 * cfg.dim * 4
+    return reads + writes
+
+
+def run_bwd(args, torch):
+    import numpy as np
+    import ssmgen
+    import selective_state_space_24_amd as ssm
+    cfg = ssmgen.CONFIGS[WORKLOAD]
+    dev = device_inputs(cfg, torch)
+    dy = torch.randn(cfg.batch, cfg.dim, cfg.L, device="cuda").to(dev["x"].dtype)
+    stream = torch.cuda.current_stream()
+    desc = ssm.describe(dev["x"], dev["delta"], dev["A"], dev["B"], dev["C"], dev["z"], dy)
+    g = {"dx": torch.empty_like(dev["x"]), "ddelta": torch.empty_like(dev["delta"]),
+         "dz": torch.empty_like(dev["z"]), "dA": torch.empty_like(dev["A"]),
+         "dB": torch.empty(dev["B"].shape, device="cuda"),
+         "dC": torch.empty(dev["C"].shape, device="cuda"),
+         "dD": torch.empty_like(dev["D"]), "ddelta_bias": torch.empty_like(dev["delta_bias"])}
+    ws_bytes = ssm.bwd_workspace_size(desc)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+
+    def step():
+        rc = ssm.bwd_raw(desc, dev["x"].data_ptr(), dev["delta"].data_ptr(), dev["A"].data_ptr(),
+                         dev["B"].data_ptr(), dev["C"].data_ptr(), dev["D"].data_ptr(),
+                         dev["z"].data_ptr(), dev["delta_bias"].data_ptr(), True, None,
+                         dy.data_ptr(), g["dx"].data_ptr(), g["ddelta"].data_ptr(),
+                         g["dA"].data_ptr(), g["dB"].data_ptr(), g["dC"].data_ptr(),
+                         g["dD"].data_ptr(), g["dz"].data_ptr(), g["ddelta_bias"].data_ptr(),
+                         None, ws.data_ptr(), ws_bytes, stream.cuda_stream)
+        if rc != 0:
+            raise ssm.ScanError(rc, "ssm_selective_scan_bwd")
+
+    ms, pct = timed_steps(step, args, torch, stream)
+    fl, cy = alu_model_bwd(cfg)
+    peak = fl * 64 / cy * SIMDS * CLOCK_HZ / 1e12
+    achieved = fl * cfg.tokch / (ms * 1e-3) / 1e12
+    nbytes = bwd_bytes(cfg)
+    out = {
+        "metric": "selective-scan backward Gtoken\u00b7channel/s, 1 MI355X",
+        "value": round(cfg.tokch / (ms * 1e-3) / 1e9, 3),
+        "unit": "Gtoken\u00b7channel/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "Mamba-1.4B layer selective scan backward (all input gradients)",
+                   "batch": cfg.batch, "d_inner": cfg.dim, "seq_len": cfg.L, "d_state": cfg.N,
+                   "io_dtype": cfg.io, "gate": "silu(z)", "delta_softplus": cfg.softplus},
+        "roofline": {"bound": "alu", "achieved": round(achieved, 2), "peak": round(peak, 2),
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None},
+        "hbm": {"algorithmic_bytes": nbytes,
+                "algorithmic_GBs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "step_ms": {"p10": round(pct(0.1), 5), "median": round(pct(0.5), 5),
+                    "p90": round(pct(0.9), 5)},
+        "launches_per_step": 4,
+        "kernel_source": kernel_source_hash(),
+    }
+    if args.cpu_budget > 0:
+        import oracle
+        del dev, dy, g, ws
+        torch.cuda.empty_cache()
+        threads = min(oracle.cpu_threads(), cfg.batch)  # the oracle's backward splits the batch
+        inputs = ssmgen.make_inputs(cfg)
+        dyh = np.random.default_rng(0).standard_normal((cfg.batch, cfg.dim, cfg.L))
+        t0 = time.perf_counter()
+        oracle.scan_inputs_bwd(inputs, dyh, cfg, nthreads=threads)
+        spent = time.perf_counter() - t0
+        out["cpu_baseline"] = {
+            "value": round(cfg.tokch / spent / 1e9, 6), "unit": out["unit"], "cores": threads,
+            "kind": "oracle",
+            "sample": f"the whole workload once ({cfg.batch} batch entries, one thread each) in "
+                      f"{spent:.2f} s; input generation untimed"}
+    print(json.dumps(out), flush=True)
+
+
 def decode_bytes(cfg) -> int:
     """Algorithmic bytes of one decoding step: the fp32 state read and written, every other
     input read once and y written once."""
@@ -254,7 +364,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 skips it)")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--workload", choices=("scan", "decode"), default="scan")
+    ap.add_argument("--workload", choices=("scan", "decode", "bwd"), default="scan")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -287,6 +397,9 @@ def main():
 
     if args.workload == "decode":
         run_decode(args, torch)
+        return
+    if args.workload == "bwd":
+        run_bwd(args, torch)
         return
 
     import ssmgen

@@ -165,6 +165,33 @@ int ssm_selective_state_update(const ssm_scan_desc* desc, float* state, const vo
                                const float* D, const void* z, const float* delta_bias,
                                int32_t delta_softplus, void* y, void* stream);
 
+/* Bytes of device workspace that ssm_selective_scan_bwd needs for `desc` (0 when batch or
+ * seqlen is 0). The value depends only on the descriptor. */
+int ssm_selective_scan_bwd_workspace_size(const ssm_scan_desc* desc, size_t* bytes);
+
+/* Gradients of ssm_selective_scan_fwd (delta * B discretisation) with respect to every input,
+ * given dy, the gradient of its output y: the backward half of training the layer (page
+ * "NL-345", §1 "Hardware-aware Algorithm": the states are recomputed, not stored).
+ *   inputs   : the forward call's desc, x, delta, A, B, C, D, z, delta_bias, delta_softplus and
+ *              h0 (nullable initial state, (batch, dim, dstate) fp32 contiguous)
+ *   dy       : io dtype with the strides of y
+ *   dx       : io dtype, strides of x;  ddelta: io dtype, strides of delta (gradient of the raw
+ *              delta, before bias and softplus);  dz: io dtype, strides of z (required when z is
+ *              given, ignored otherwise)
+ *   dB, dC   : fp32 with the element strides of B and C (summed over the channels of a group)
+ *   dA       : (dim, dstate) fp32;  dD, ddelta_bias: (dim,) fp32, nullable (not computed);
+ *              summed over the batch
+ *   dh0      : nullable, (batch, dim, dstate) fp32: the gradient of the initial state
+ *   workspace: at least ssm_selective_scan_bwd_workspace_size bytes, 4-byte aligned
+ * Supported: A_DIAG mode with dstate <= 16 (SSM_ERR_UNSUPPORTED otherwise). Outputs must not
+ * overlap any input or each other. Results are deterministic (fixed-order reductions). */
+int ssm_selective_scan_bwd(const ssm_scan_desc* desc, const void* x, const void* delta,
+                           const float* A, const void* B, const void* C, const float* D,
+                           const void* z, const float* delta_bias, int32_t delta_softplus,
+                           const float* h0, const void* dy, void* dx, void* ddelta, float* dA,
+                           float* dB, float* dC, float* dD, void* dz, float* ddelta_bias,
+                           float* dh0, void* workspace, size_t workspace_bytes, void* stream);
+
 /* SSM_SCAN_ABI_VERSION of the built library. */
 int ssm_abi_version(void);
 

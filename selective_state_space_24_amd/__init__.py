@@ -80,6 +80,10 @@ def lib():
         h.ssm_selective_scan_fwd_ext.restype = ctypes.c_int
         h.ssm_selective_state_update.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]
         h.ssm_selective_state_update.restype = ctypes.c_int
+        h.ssm_selective_scan_bwd_workspace_size.argtypes = [dp, ctypes.POINTER(sz)]
+        h.ssm_selective_scan_bwd_workspace_size.restype = ctypes.c_int
+        h.ssm_selective_scan_bwd.argtypes = [dp] + [vp] * 8 + [i32] + [vp] * 11 + [vp, sz, vp]
+        h.ssm_selective_scan_bwd.restype = ctypes.c_int
         h.ssm_status_string.argtypes = [ctypes.c_int]
         h.ssm_status_string.restype = ctypes.c_char_p
         h.ssm_abi_version.argtypes = []
@@ -129,6 +133,23 @@ def fwd_ext_raw(desc: ScanDesc, x, delta, A, B, C, D, z, delta_bias, delta_softp
     return int(lib().ssm_selective_scan_fwd_ext(
         ctypes.byref(desc), x, delta, A, B, C, D, z, delta_bias, int(bool(delta_softplus)), y,
         ctypes.byref(ext) if ext is not None else None, workspace, int(workspace_bytes), stream))
+
+
+def bwd_workspace_size(desc: ScanDesc) -> int:
+    out = ctypes.c_size_t(0)
+    rc = lib().ssm_selective_scan_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(out))
+    if rc != SSM_OK:
+        raise ScanError(rc, "ssm_selective_scan_bwd_workspace_size")
+    return int(out.value)
+
+
+def bwd_raw(desc: ScanDesc, x, delta, A, B, C, D, z, delta_bias, delta_softplus: bool, h0, dy,
+            dx, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0, workspace, workspace_bytes: int,
+            stream) -> int:
+    """Direct call of ``ssm_selective_scan_bwd``; returns the status code without raising."""
+    return int(lib().ssm_selective_scan_bwd(
+        ctypes.byref(desc), x, delta, A, B, C, D, z, delta_bias, int(bool(delta_softplus)), h0, dy,
+        dx, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0, workspace, int(workspace_bytes), stream))
 
 
 def state_update_raw(desc: ScanDesc, state, x, delta, A, B, C, D, z, delta_bias,
@@ -284,3 +305,48 @@ def selective_state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=
     if rc != SSM_OK:
         raise ScanError(rc, "ssm_selective_state_update")
     return y
+
+
+def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                       dy=None, *, h0=None, want_dh0=False, workspace=None, stream=None) -> dict:
+    """Gradients of ``selective_scan_fwd`` (delta * B rule) for dy, the gradient of y. Returns a
+    dict: dx, ddelta, dz (io dtype, like x, delta, z), dA, dB, dC, dD, ddelta_bias (float32) and
+    dh0 when ``want_dh0``. See ``ssm_selective_scan_bwd``."""
+    import torch
+    desc = describe(x, delta, A, B, C, z, dy)
+    for name, t in (("D", D), ("delta_bias", delta_bias), ("h0", h0)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise TypeError(f"{name} must be a contiguous float32 tensor")
+    g = {"dx": torch.empty_like(x), "ddelta": torch.empty_like(delta),
+         "dA": torch.empty_like(A),
+         "dB": torch.empty(B.shape, dtype=torch.float32, device=x.device),
+         "dC": torch.empty(C.shape, dtype=torch.float32, device=x.device)}
+    if x.stride() != g["dx"].stride() or delta.stride() != g["ddelta"].stride():
+        raise ValueError("x and delta must be contiguous (their gradients use their strides)")
+    if B.stride() != g["dB"].stride() or C.stride() != g["dC"].stride():
+        raise ValueError("B and C must be contiguous (their gradients use their strides)")
+    if D is not None:
+        g["dD"] = torch.empty_like(D)
+    if z is not None:
+        g["dz"] = torch.empty_like(z)
+        if z.stride() != g["dz"].stride():
+            raise ValueError("z must be contiguous (its gradient uses its strides)")
+    if delta_bias is not None:
+        g["ddelta_bias"] = torch.empty_like(delta_bias)
+    if want_dh0:
+        g["dh0"] = torch.empty((desc.batch, desc.dim, desc.dstate), dtype=torch.float32,
+                               device=x.device)
+    need = bwd_workspace_size(desc)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    sp = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    rc = bwd_raw(desc, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                 _ptr(delta_bias), delta_softplus, _ptr(h0), _ptr(dy), _ptr(g["dx"]),
+                 _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g.get("dD")),
+                 _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")), _ptr(g.get("dh0")),
+                 _ptr(workspace) if need else None, need, sp)
+    if rc != SSM_OK:
+        raise ScanError(rc, "ssm_selective_scan_bwd")
+    return g

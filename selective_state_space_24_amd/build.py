@@ -13,7 +13,8 @@ LIB = os.path.join(LIBDIR, "libssm_scan.so")
 
 # Kernel instantiations are split by io dtype and A mode so that the units compile in parallel.
 SOURCES = ["scan_fwd_bf16_diag.hip", "scan_fwd_bf16_head.hip", "scan_fwd_f32_diag.hip",
-           "scan_fwd_f32_head.hip", "scan_state.hip", "scan_decode.hip", "scan_api.cpp"]
+           "scan_fwd_f32_head.hip", "scan_state.hip", "scan_decode.hip",
+           "scan_bwd.hip", "scan_api.cpp"]
 
 # Packed fp32 instructions are switched off for all device code.
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

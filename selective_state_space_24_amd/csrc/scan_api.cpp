@@ -109,6 +109,31 @@ size_t workspace_bytes_for(const ssm_scan_desc* d, const Plan& p) {
   return (size_t)d->batch * (size_t)d->dim * (size_t)p.nseg * (size_t)(d->dstate + 1) * sizeof(float);
 }
 
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Workspace of the backward pass: checkpoints (batch, dim, ntiles, N), the dB and dC partials
+// (batch, groups_per_batch, N, L), the dA partials (batch, dim, N), dD and dbias partials
+// (batch, dim); fp32, each section 256-byte aligned.
+struct BwdLayout {
+  size_t ckpt, dB, dC, dA, dD, dbias, total;
+};
+
+BwdLayout bwd_layout(const ssm_scan_desc* d) {
+  const size_t ntiles = (size_t)((d->seqlen + ssm::kLT - 1) / ssm::kLT);
+  const size_t gpb = (size_t)((d->dim + ssm::kChannelsPerGroup - 1) / ssm::kChannelsPerGroup);
+  const size_t B = (size_t)d->batch, D = (size_t)d->dim, N = (size_t)d->dstate, L = (size_t)d->seqlen;
+  BwdLayout l;
+  size_t off = 0;
+  l.ckpt = off; off += align256(B * D * ntiles * N * 4);
+  l.dB = off; off += align256(B * gpb * N * L * 4);
+  l.dC = off; off += align256(B * gpb * N * L * 4);
+  l.dA = off; off += align256(B * D * N * 4);
+  l.dD = off; off += align256(B * D * 4);
+  l.dbias = off; off += align256(B * D * 4);
+  l.total = (B == 0 || L == 0) ? 0 : off;
+  return l;
+}
+
 bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
   if (!a || !b || abytes == 0 || bbytes == 0) return false;
   const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
@@ -356,6 +381,127 @@ int ssm_selective_state_update(const ssm_scan_desc* desc, float* state, const vo
                    aligned(B, 4 * es) && aligned(C, 4 * es);
   p.bc_vec = bc4 ? 1 : 0;
   const hipError_t e = ssm::launch_decode(p, bf16, head, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+int ssm_selective_scan_bwd_workspace_size(const ssm_scan_desc* desc, size_t* bytes) {
+  if (!bytes) return SSM_ERR_NULL_ARG;
+  const int rc = check_desc(desc);
+  if (rc != SSM_OK) return rc;
+  *bytes = bwd_layout(desc).total;
+  return SSM_OK;
+}
+
+int ssm_selective_scan_bwd(const ssm_scan_desc* desc, const void* x, const void* delta,
+                           const float* A, const void* B, const void* C, const float* D,
+                           const void* z, const float* delta_bias, int32_t delta_softplus,
+                           const float* h0, const void* dy, void* dx, void* ddelta, float* dA,
+                           float* dB, float* dC, float* dD, void* dz, float* ddelta_bias,
+                           float* dh0, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_desc(desc);
+  if (rc != SSM_OK) return rc;
+  const ssm_scan_desc& d = *desc;
+  if (d.a_mode != SSM_A_DIAG || d.dstate > 16) return SSM_ERR_UNSUPPORTED;
+  const int64_t ch_per_group = d.dim / d.ngroups;
+  if (d.ngroups > 1 && ch_per_group % ssm::kChannelsPerGroup != 0) return SSM_ERR_UNSUPPORTED;
+  if (!dA) return SSM_ERR_NULL_ARG;
+  if (z && !dz) return SSM_ERR_NULL_ARG;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const size_t es = d.io_dtype == SSM_DTYPE_BF16 ? 2 : 4;
+  const size_t a_bytes = (size_t)d.dim * d.dstate * 4;
+  const size_t state_bytes = (size_t)d.batch * d.dim * d.dstate * 4;
+  if (d.batch == 0 || d.seqlen == 0) {
+    // nothing depends on the parameters or on h0: their gradients are zero
+    if (!aligned(dA, 4) || (dD && !aligned(dD, 4)) || (ddelta_bias && !aligned(ddelta_bias, 4)) ||
+        (dh0 && !aligned(dh0, 4)))
+      return SSM_ERR_MISALIGNED;
+    hipError_t e = ssm::launch_state_copy(nullptr, dA, d.dim * d.dstate, hs);
+    if (e == hipSuccess && dD) e = ssm::launch_state_copy(nullptr, dD, d.dim, hs);
+    if (e == hipSuccess && ddelta_bias) e = ssm::launch_state_copy(nullptr, ddelta_bias, d.dim, hs);
+    if (e == hipSuccess && dh0) e = ssm::launch_state_copy(nullptr, dh0, (int64_t)(state_bytes / 4), hs);
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+  }
+  if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dB || !dC) return SSM_ERR_NULL_ARG;
+
+  const void* io_ptrs[] = {x, delta, B, C, z, dy, dx, ddelta, dz};
+  for (const void* q : io_ptrs)
+    if (q && !aligned(q, es)) return SSM_ERR_MISALIGNED;
+  const void* f32_ptrs[] = {A, D, delta_bias, h0, dA, dB, dC, dD, ddelta_bias, dh0, workspace};
+  for (const void* q : f32_ptrs)
+    if (q && !aligned(q, 4)) return SSM_ERR_MISALIGNED;
+
+  const size_t x_bytes = (size_t)extent3(d.batch, d.dim, d.seqlen, d.x_stride_batch, d.x_stride_dim) * es;
+  const size_t dl_bytes = (size_t)extent3(d.batch, d.dim, d.seqlen, d.delta_stride_batch, d.delta_stride_dim) * es;
+  const size_t z_bytes = (size_t)extent3(d.batch, d.dim, d.seqlen, d.z_stride_batch, d.z_stride_dim) * es;
+  const size_t y_bytes = (size_t)extent3(d.batch, d.dim, d.seqlen, d.y_stride_batch, d.y_stride_dim) * es;
+  const int64_t Bext = extent4(d.batch, d.ngroups, d.dstate, d.seqlen, d.B_stride_batch, d.B_stride_group, d.B_stride_state);
+  const int64_t Cext = extent4(d.batch, d.ngroups, d.dstate, d.seqlen, d.C_stride_batch, d.C_stride_group, d.C_stride_state);
+  const BwdLayout lay = bwd_layout(desc);
+  if (!workspace || workspace_bytes < lay.total) return SSM_ERR_WORKSPACE;
+
+  const void* in_ptrs[] = {x, delta, A, B, C, D, z, delta_bias, h0, dy};
+  const size_t in_bytes[] = {x_bytes, dl_bytes, a_bytes, (size_t)Bext * es, (size_t)Cext * es,
+                             D ? (size_t)d.dim * 4 : 0, z ? z_bytes : 0,
+                             delta_bias ? (size_t)d.dim * 4 : 0, h0 ? state_bytes : 0, y_bytes};
+  const void* out_ptrs[] = {dx, ddelta, dz, dA, dB, dC, dD, ddelta_bias, dh0, workspace};
+  const size_t out_bytes[] = {x_bytes, dl_bytes, dz ? z_bytes : 0, a_bytes, (size_t)Bext * 4,
+                              (size_t)Cext * 4, dD ? (size_t)d.dim * 4 : 0,
+                              ddelta_bias ? (size_t)d.dim * 4 : 0, dh0 ? state_bytes : 0,
+                              lay.total};
+  for (int i = 0; i < 10; ++i) {
+    for (int j = 0; j < 10; ++j)
+      if (overlaps(out_ptrs[i], out_bytes[i], in_ptrs[j], in_bytes[j])) return SSM_ERR_ALIAS;
+    for (int j = i + 1; j < 10; ++j)
+      if (overlaps(out_ptrs[i], out_bytes[i], out_ptrs[j], out_bytes[j])) return SSM_ERR_ALIAS;
+  }
+
+  ssm::BwdParams q;
+  memset(&q, 0, sizeof(q));
+  ssm::ScanParams& p = q.f;
+  p.x = x; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.delta_bias = delta_bias;
+  p.h0 = h0;
+  p.batch = d.batch; p.dim = d.dim; p.L = d.seqlen; p.N = d.dstate; p.ngroups = d.ngroups;
+  p.headdim = d.headdim;
+  p.x_sb = d.x_stride_batch; p.x_sd = d.x_stride_dim;
+  p.dl_sb = d.delta_stride_batch; p.dl_sd = d.delta_stride_dim;
+  p.B_sb = d.B_stride_batch; p.B_sg = d.B_stride_group; p.B_sn = d.B_stride_state;
+  p.C_sb = d.C_stride_batch; p.C_sg = d.C_stride_group; p.C_sn = d.C_stride_state;
+  p.z_sb = d.z_stride_batch; p.z_sd = d.z_stride_dim;
+  p.y_sb = d.y_stride_batch; p.y_sd = d.y_stride_dim;
+  p.groups_per_batch = (d.dim + ssm::kChannelsPerGroup - 1) / ssm::kChannelsPerGroup;
+  p.seg_len = d.seqlen;
+  p.nseg = 1;
+  p.softplus = delta_softplus ? 1 : 0;
+  p.ntiles = (d.seqlen + ssm::kLT - 1) / ssm::kLT;
+  char* ws = static_cast<char*>(workspace);
+  p.ckpt = reinterpret_cast<float*>(ws + lay.ckpt);
+  // 16-byte rows for x, delta, dy, z (the checkpoint pass and the backward prologue)
+  const int64_t vec = 16 / (int64_t)es;
+  bool vec_ok = true;
+  const void* vptrs[] = {x, delta, z, dy};
+  for (const void* v : vptrs)
+    if (v && !aligned(v, 16)) vec_ok = false;
+  const int64_t vstrides[] = {d.x_stride_batch, d.x_stride_dim, d.delta_stride_batch,
+                              d.delta_stride_dim, z ? d.z_stride_batch : 0, z ? d.z_stride_dim : 0,
+                              d.y_stride_batch, d.y_stride_dim};
+  for (int64_t st : vstrides)
+    if (st % vec) vec_ok = false;
+  p.vec_io = vec_ok ? 1 : 0;
+  bool bc_vec = aligned(B, 16) && aligned(C, 16);
+  const int64_t bstrides[] = {d.B_stride_batch, d.B_stride_group, d.B_stride_state,
+                              d.C_stride_batch, d.C_stride_group, d.C_stride_state};
+  for (int64_t st : bstrides)
+    if (st % vec) bc_vec = false;
+  p.bc_vec = bc_vec ? 1 : 0;
+
+  q.dy = dy; q.dx = dx; q.ddelta = ddelta; q.dz = dz;
+  q.dA = dA; q.dB = dB; q.dC = dC; q.dD = dD; q.dbias = ddelta_bias; q.dh0 = dh0;
+  q.dB_part = reinterpret_cast<float*>(ws + lay.dB);
+  q.dC_part = reinterpret_cast<float*>(ws + lay.dC);
+  q.dA_part = reinterpret_cast<float*>(ws + lay.dA);
+  q.dD_part = reinterpret_cast<float*>(ws + lay.dD);
+  q.dbias_part = reinterpret_cast<float*>(ws + lay.dbias);
+  const hipError_t e = ssm::launch_bwd(q, d.io_dtype == SSM_DTYPE_BF16, hs);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 

@@ -1,0 +1,398 @@
+// gfx950 kernels of the selective-scan backward pass: the gradients of every input.
+//
+// The pages train the layer end to end and recompute the states in the backward pass rather
+// than storing them (page "NL-345", §1 "Hardware-aware Algorithm"). Here:
+//   1. a checkpoint pass (the forward kernel without readout) stores the state at the start of
+//      every 64-step load tile: N fp32 values per channel per tile;
+//   2. the backward kernel walks each channel group's tiles in reverse. A tile is processed in
+//      16-step sub-tiles, last first: the states of the tile's sub-tile starts are recomputed
+//      from the checkpoint, then each sub-tile's 16 states are recomputed into registers and
+//      the reverse recurrence runs over them:
+//        gh += gy C;  dC += gy h;  ddelta += gh (a dA h_prev + B x);  da += gh dA h_prev delta;
+//        dB += gh delta x;  dx += gh delta B;  gh *= dA
+//      (gy = dy silu(z) is the gradient of the ungated readout). As in the forward pass, lane =
+//      channel and the four wavefronts split the states, so the per-channel sums over states
+//      (ddelta, dx, and the readout needed by dz) are added across wavefronts in LDS, and the
+//      per-(t, n) sums over channels (dB, dC) are added over the lanes of each wavefront in
+//      wave-private LDS, giving one partial per workgroup;
+//   3. reduce kernels add the partials: dB, dC over the workgroups of a batch entry's group,
+//      dA, dD, dbias over the batch, in a fixed order (results are deterministic).
+// Arithmetic: fp32. Supported: diagonal A, dstate <= 16, delta * B discretisation.
+#include "scan_kernels.h"
+
+namespace ssm {
+
+constexpr int kSub = 16;            // steps per sub-tile (their states are held in registers)
+constexpr int kSubs = kLT / kSub;   // sub-tiles per load tile
+constexpr int kInStride = kLT + 1;  // entries per channel row of the per-step LDS arrays
+constexpr int kRedStride = kSub + 1;
+
+template <typename IO, int NS, bool GATE>
+__global__ void __launch_bounds__(256, 1) bwd_kernel(const BwdParams q) {
+  constexpr int NW = kWavesPerGroup;
+  constexpr int NT = 64 * NW;
+  constexpr int NP = NS * NW;
+  constexpr int V = IoTraits<IO>::kVec;
+  constexpr int CPT = kLT / V;                      // chunks per channel row of a tile
+  constexpr int ITEMS = kChannelsPerGroup * CPT;
+  constexpr int IPT = ITEMS / NT;                   // prologue items per thread
+  constexpr int NV = 8 * NS;                        // dB/dC values per lane per 4 steps
+  static_assert(ITEMS % NT == 0, "prologue items must divide evenly");
+  static_assert(NV <= 32 && 64 % NV == 0, "dB/dC reduction layout");
+
+  __shared__ __align__(16) f32x4 s_in[kChannelsPerGroup * kInStride];   // delta, u, gy, x
+  __shared__ __align__(8) float2 s_in2[kChannelsPerGroup * kInStride];  // gzf, sigmoid(v)
+  __shared__ __align__(16) float s_B[NP * kBcStrideL];
+  __shared__ __align__(16) float s_C[NP * kBcStrideL];
+  __shared__ __align__(16) float s_red[3 * NW * kChannelsPerGroup * kRedStride];
+
+  const ScanParams& p = q.f;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t wg = blockIdx.x % p.groups_per_batch;
+  const int64_t b = blockIdx.x / p.groups_per_batch;
+  const int64_t d0 = wg * kChannelsPerGroup;
+  const int64_t grp = d0 / (p.dim / p.ngroups);
+  const int n0 = w * NS;
+  const int64_t L = p.L;
+  const bool vec = p.vec_io != 0;
+  const IO* X = static_cast<const IO*>(p.x);
+  const IO* DL = static_cast<const IO*>(p.delta);
+  const IO* Z = static_cast<const IO*>(p.z);
+  const IO* DY = static_cast<const IO*>(q.dy);
+  const IO* Bg = static_cast<const IO*>(p.B) + b * p.B_sb + grp * p.B_sg;
+  const IO* Cg = static_cast<const IO*>(p.C) + b * p.C_sb + grp * p.C_sg;
+
+  // this lane's channel and states
+  const int64_t d = d0 + lane;
+  const bool live = d < p.dim;
+  float ap[NS], an[NS];  // a * log2(e) for exp2, and a itself
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    an[j] = (live && n0 + j < p.N) ? p.A[d * p.N + n0 + j] : 0.0f;
+    ap[j] = an[j] * kLog2e;
+  }
+
+  // the epilogue's item: channel er, steps [4 * eq, 4 * eq + 4) of each sub-tile
+  const int er = tid >> 2, eq = tid & 3;
+  const int64_t ed = d0 + er;
+  const bool elive = ed < p.dim;
+  const float eD = (elive && p.D) ? p.D[ed] : 0.0f;
+  float dD_acc = 0.0f, dbias_acc = 0.0f;
+
+  float gh[NS], da[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) gh[j] = da[j] = 0.0f;
+
+  for (int64_t tile = p.ntiles - 1; tile >= 0; --tile) {
+    const int64_t t0 = tile * kLT;
+    const int lt_len = (int)min<int64_t>(kLT, L - t0);
+
+    // ---- prologue: per (channel, step) values of the tile into LDS; padding steps are zero
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+      const int item = tid + it * NT;
+      const int r = item / CPT, tl = (item % CPT) * V;
+      const int64_t dd = d0 + r;
+      const int64_t dv = min(dd, p.dim - 1);
+      const int cnt = dd < p.dim ? max(0, min(V, lt_len - tl)) : 0;
+      float xv[V], dv_raw[V], zv[V], gv[V];
+      load_chunk<IO, true>(X + b * p.x_sb + dv * p.x_sd, t0 + tl, cnt, vec, xv);
+      load_chunk<IO, true>(DL + b * p.dl_sb + dv * p.dl_sd, t0 + tl, cnt, vec, dv_raw);
+      load_chunk<IO, true>(DY + b * p.y_sb + dv * p.y_sd, t0 + tl, cnt, vec, gv);
+      if constexpr (GATE) load_chunk<IO, true>(Z + b * p.z_sb + dv * p.z_sd, t0 + tl, cnt, vec, zv);
+      const float bias = (dd < p.dim && p.delta_bias) ? p.delta_bias[dv] : 0.0f;
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        float dl = 0.0f, u = 0.0f, gy = 0.0f, xx = 0.0f, gzf = 0.0f, sig = 0.0f;
+        if (e < cnt) {
+          const float v = dv_raw[e] + bias;
+          dl = p.softplus ? softplus_f32(v) : v;
+          sig = p.softplus ? __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v * kLog2e)) : 1.0f;
+          xx = xv[e];
+          u = dl * xx;
+          gy = gv[e];
+          if constexpr (GATE) {
+            const float zz = zv[e];
+            const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zz * kLog2e));
+            gzf = gv[e] * s * fmaf(zz, 1.0f - s, 1.0f);
+            gy = gv[e] * zz * s;
+          }
+        }
+        s_in[r * kInStride + tl + e] = f32x4{dl, u, gy, xx};
+        s_in2[r * kInStride + tl + e] = make_float2(gzf, sig);
+      }
+    }
+    for (int i = tid; i < NP * kLT; i += NT) {
+      const int n = i / kLT, t = i % kLT;
+      const bool on = n < p.N && t < lt_len;
+      s_B[n * kBcStrideL + t] = on ? to_f32(Bg[n * p.B_sn + t0 + t]) : 0.0f;
+      s_C[n * kBcStrideL + t] = on ? to_f32(Cg[n * p.C_sn + t0 + t]) : 0.0f;
+    }
+    // the state at the start of the tile
+    float h[NS];
+    {
+      const float* c = p.ckpt + ((b * p.dim + (live ? d : 0)) * p.ntiles + tile) * p.N + n0;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) h[j] = (live && n0 + j < p.N) ? c[j] : 0.0f;
+    }
+    __syncthreads();
+
+    // ---- the states at the sub-tile starts: hs[k] = state before step kSub * k
+    float hs[kSubs][NS];
+#pragma unroll
+    for (int k = 0; k < kSubs; ++k) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) hs[k][j] = h[j];
+      if (k + 1 == kSubs) break;
+      for (int i = 0; i < kSub; ++i) {
+        const int t = k * kSub + i;
+        const f32x4 in = s_in[lane * kInStride + t];
+#pragma unroll
+        for (int j = 0; j < NS; ++j)
+          h[j] = fmaf(__builtin_amdgcn_exp2f(in.x * ap[j]), h[j], in.y * s_B[(n0 + j) * kBcStrideL + t]);
+      }
+    }
+
+    // ---- sub-tiles, last first (unrolled: hs is indexed by k)
+#pragma unroll
+    for (int k = kSubs - 1; k >= 0; --k) {
+      const int tb = k * kSub;
+      // recompute the sub-tile's states (after each step) and the readout partials
+      float hh[kSub][NS];
+      float yp[kSub];
+#pragma unroll
+      for (int i = 0; i < kSub; ++i) {
+        const f32x4 in = s_in[lane * kInStride + tb + i];
+        float acc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          const float prev = i == 0 ? hs[k][j] : hh[i - 1][j];
+          hh[i][j] = fmaf(__builtin_amdgcn_exp2f(in.x * ap[j]), prev,
+                          in.y * s_B[(n0 + j) * kBcStrideL + tb + i]);
+          acc = fmaf(s_C[(n0 + j) * kBcStrideL + tb + i], hh[i][j], acc);
+        }
+        yp[i] = acc;
+      }
+      // reverse recurrence over the sub-tile
+      float gdel[kSub], gxs[kSub];
+      // wavefront w's block of s_red (its three partial arrays) doubles as its private scratch
+      float* scratch = s_red + w * 3 * kChannelsPerGroup * kRedStride;
+#pragma unroll
+      for (int i4 = kSub - 4; i4 >= 0; i4 -= 4) {
+        float red[NV];  // [tensor (dC, dB)][state j][step e]
+#pragma unroll
+        for (int e = 3; e >= 0; --e) {
+          const int i = i4 + e;
+          const int t = tb + i;
+          const f32x4 in = s_in[lane * kInStride + t];
+          const float dl = in.x, u = in.y, gy = in.z, xx = in.w;
+          float gd = 0.0f, gx = 0.0f;
+#pragma unroll
+          for (int j = 0; j < NS; ++j) {
+            const float Bv = s_B[(n0 + j) * kBcStrideL + t];
+            const float Cv = s_C[(n0 + j) * kBcStrideL + t];
+            gh[j] = fmaf(gy, Cv, gh[j]);
+            red[j * 4 + e] = gy * hh[i][j];                        // dC
+            const float dA = __builtin_amdgcn_exp2f(dl * ap[j]);
+            const float hp = i == 0 ? hs[k][j] : hh[i - 1][j];
+            const float tmp = hp * dA;
+            gd = fmaf(gh[j], fmaf(tmp, an[j], Bv * xx), gd);
+            da[j] = fmaf(gh[j] * tmp, dl, da[j]);
+            red[4 * NS + j * 4 + e] = gh[j] * u;                   // dB
+            gx = fmaf(gh[j], dl * Bv, gx);
+            gh[j] *= dA;
+          }
+          gdel[i] = gd;
+          gxs[i] = gx;
+        }
+        // sum the 4 steps' dC, dB over the wavefront's lanes (channels) through wave-private LDS
+#pragma unroll
+        for (int c = 0; c < NV; ++c) scratch[lane * (NV + 1) + c] = red[c];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // lane sums NV rows of column lane % NV; the 64 / NV lanes of a column then combine
+        const int col = lane % NV, part = lane / NV;
+        float sum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < NV; ++r) sum += scratch[(part * NV + r) * (NV + 1) + col];
+#pragma unroll
+        for (int off = NV; off < 64; off <<= 1) sum += __shfl_xor(sum, off);
+        if (lane < NV) {
+          const int tensor = col / (4 * NS), j = (col / 4) % NS, e = col % 4;
+          const int64_t t = t0 + tb + i4 + e;
+          if (n0 + j < p.N && t < L) {
+            float* dst = tensor == 0 ? q.dC_part : q.dB_part;
+            dst[((b * p.groups_per_batch + wg) * p.N + n0 + j) * L + t] = sum;
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+      // per-channel partial sums over this wavefront's states
+      {
+        float* ry = s_red + ((w * 3 + 0) * kChannelsPerGroup + lane) * kRedStride;
+        float* rg = s_red + ((w * 3 + 1) * kChannelsPerGroup + lane) * kRedStride;
+        float* rx = s_red + ((w * 3 + 2) * kChannelsPerGroup + lane) * kRedStride;
+#pragma unroll
+        for (int i = 0; i < kSub; ++i) {
+          ry[i] = yp[i];
+          rg[i] = gdel[i];
+          rx[i] = gxs[i];
+        }
+      }
+      __syncthreads();
+      // epilogue: add the wavefronts' partials; dx, ddelta, dz for 4 steps of one channel
+      {
+        float vx[4], vd[4], vz[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = eq * 4 + e;
+          const int t = tb + i;
+          float ys = 0.0f, gds = 0.0f, gxsum = 0.0f;
+#pragma unroll
+          for (int ww = 0; ww < NW; ++ww) {
+            ys += s_red[((ww * 3 + 0) * kChannelsPerGroup + er) * kRedStride + i];
+            gds += s_red[((ww * 3 + 1) * kChannelsPerGroup + er) * kRedStride + i];
+            gxsum += s_red[((ww * 3 + 2) * kChannelsPerGroup + er) * kRedStride + i];
+          }
+          const f32x4 in = s_in[er * kInStride + t];
+          const float2 in2 = s_in2[er * kInStride + t];
+          const float y = fmaf(eD, in.w, ys);
+          vz[e] = in2.x * y;
+          vx[e] = fmaf(in.z, eD, gxsum);
+          vd[e] = gds * in2.y;
+          dD_acc = fmaf(in.z, in.w, dD_acc);
+          dbias_acc += vd[e];
+        }
+        if (elive) {
+          const int64_t tt = t0 + tb + eq * 4;
+          IO* dxr = static_cast<IO*>(q.dx) + b * p.x_sb + ed * p.x_sd;
+          IO* ddr = static_cast<IO*>(q.ddelta) + b * p.dl_sb + ed * p.dl_sd;
+          IO* dzr = GATE ? static_cast<IO*>(q.dz) + b * p.z_sb + ed * p.z_sd : nullptr;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (tt + e < L) {
+              store_elem(dxr + tt + e, vx[e]);
+              store_elem(ddr + tt + e, vd[e]);
+              if constexpr (GATE) store_elem(dzr + tt + e, vz[e]);
+            }
+          }
+        }
+      }
+      __syncthreads();  // s_red is reused by the next sub-tile
+    }
+  }
+
+  // ---- per-workgroup partials of the batch-summed gradients, and dh0
+  if (live) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      if (n0 + j >= p.N) continue;
+      q.dA_part[(b * p.dim + d) * p.N + n0 + j] = da[j];
+      if (q.dh0) q.dh0[(b * p.dim + d) * p.N + n0 + j] = gh[j];
+    }
+  }
+  dD_acc += __shfl_xor(dD_acc, 1);
+  dD_acc += __shfl_xor(dD_acc, 2);
+  dbias_acc += __shfl_xor(dbias_acc, 1);
+  dbias_acc += __shfl_xor(dbias_acc, 2);
+  if (elive && eq == 0) {
+    q.dD_part[b * p.dim + ed] = dD_acc;
+    q.dbias_part[b * p.dim + ed] = dbias_acc;
+  }
+}
+
+// dB, dC: the sum over the workgroups of each (batch entry, group), one thread per (b, g, n, t)
+__global__ void __launch_bounds__(256) bwd_reduce_bc(const BwdParams q) {
+  const ScanParams& p = q.f;
+  const int64_t L = p.L, N = p.N;
+  const int64_t total = p.batch * p.ngroups * N * L;
+  const int64_t wg_per_group = p.groups_per_batch / p.ngroups;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t t = i % L, n = (i / L) % N, g = (i / (L * N)) % p.ngroups, b = i / (L * N * p.ngroups);
+    float sb = 0.0f, sc = 0.0f;
+    for (int64_t k = 0; k < wg_per_group; ++k) {
+      const int64_t idx = ((b * p.groups_per_batch + g * wg_per_group + k) * N + n) * L + t;
+      sb += q.dB_part[idx];
+      sc += q.dC_part[idx];
+    }
+    q.dB[b * p.B_sb + g * p.B_sg + n * p.B_sn + t] = sb;
+    q.dC[b * p.C_sb + g * p.C_sg + n * p.C_sn + t] = sc;
+  }
+}
+
+// dA, dD, dbias: the sums over the batch, one thread per (d, n)
+__global__ void __launch_bounds__(256) bwd_reduce_params(const BwdParams q) {
+  const ScanParams& p = q.f;
+  const int64_t N = p.N;
+  const int64_t total = p.dim * N;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    float s = 0.0f;
+    for (int64_t b = 0; b < p.batch; ++b) s += q.dA_part[b * total + i];
+    q.dA[i] = s;
+    if (i % N == 0) {
+      const int64_t d = i / N;
+      float sd = 0.0f, sbias = 0.0f;
+      for (int64_t b = 0; b < p.batch; ++b) {
+        sd += q.dD_part[b * p.dim + d];
+        sbias += q.dbias_part[b * p.dim + d];
+      }
+      if (q.dD) q.dD[d] = sd;
+      if (q.dbias) q.dbias[d] = sbias;
+    }
+  }
+}
+
+template <typename IO, int NS>
+static hipError_t bwd_cfg(const BwdParams& q, hipStream_t stream) {
+  const ScanParams& p = q.f;
+  const int64_t groups = p.batch * p.groups_per_batch;
+  // 1. checkpoints
+  hipLaunchKernelGGL((scan_fwd_kernel<IO, NS, kWavesPerGroup, false, false, false, false, true>),
+                     dim3((unsigned)groups, 1), dim3(64 * kWavesPerGroup), 0, stream,
+                     static_cast<const IO*>(p.x), static_cast<const IO*>(p.delta),
+                     static_cast<const IO*>(p.B), static_cast<const IO*>(p.C),
+                     static_cast<const IO*>(nullptr), static_cast<IO*>(nullptr), p.A, p.D,
+                     p.delta_bias, nullptr, nullptr, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // 2. the reverse pass
+  if (p.z)
+    hipLaunchKernelGGL((bwd_kernel<IO, NS, true>), dim3((unsigned)groups), dim3(256), 0, stream, q);
+  else
+    hipLaunchKernelGGL((bwd_kernel<IO, NS, false>), dim3((unsigned)groups), dim3(256), 0, stream, q);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // 3. reductions
+  const int64_t nbc = p.batch * p.ngroups * p.N * p.L;
+  const int64_t bbc = (nbc + 255) / 256;
+  const unsigned gbc = (unsigned)(bbc < 65536 ? bbc : 65536);
+  hipLaunchKernelGGL(bwd_reduce_bc, dim3(gbc > 0 ? gbc : 1), dim3(256), 0, stream, q);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t np = p.dim * p.N;
+  const int64_t bp = (np + 255) / 256;
+  hipLaunchKernelGGL(bwd_reduce_params, dim3((unsigned)(bp < 65536 ? bp : 65536)), dim3(256), 0,
+                     stream, q);
+  return hipGetLastError();
+}
+
+template <typename IO>
+static hipError_t bwd_n(const BwdParams& q, hipStream_t stream) {
+  const int64_t N = q.f.N;
+  if (N <= 4) return bwd_cfg<IO, 1>(q, stream);
+  if (N <= 8) return bwd_cfg<IO, 2>(q, stream);
+  return bwd_cfg<IO, 4>(q, stream);  // N <= 16 (checked by the caller)
+}
+
+hipError_t launch_bwd(const BwdParams& q, bool bf16, hipStream_t stream) {
+  return bf16 ? bwd_n<bf16_bits>(q, stream) : bwd_n<float>(q, stream);
+}
+
+}  // namespace ssm

@@ -26,6 +26,9 @@ struct ScanParams {
   void* y;
   const float* h0;          // nullable: initial state (batch, dim, N) fp32
   float* hfin;              // nullable: final state (batch, dim, N) fp32
+  float* ckpt;              // backward checkpoints: state at each load tile start,
+                            // ckpt[((b * dim + d) * ntiles + tile) * N + n]
+  int64_t ntiles;           // load tiles per sequence (checkpoint pass)
   // per-segment summaries for sequences split along L (nullable when nseg == 1):
   // hend[((b * dim + d) * nseg + s) * N + n] and dsum[(b * dim + d) * nseg + s]
   float* hend;
@@ -52,6 +55,29 @@ hipError_t launch_f32_diag(const ScanParams& p, hipStream_t stream);
 hipError_t launch_f32_head(const ScanParams& p, hipStream_t stream);
 // one recurrent step per sequence: reads the state at h0, writes it at hfin (may be equal)
 hipError_t launch_decode(const ScanParams& p, bool bf16, bool head, hipStream_t stream);
+// Arguments of the backward pass: the forward's (f, single segment) and the gradients. dy has
+// the strides of y, dx those of x, ddelta those of delta, dz those of z; dB, dC are fp32 with
+// the strides of B and C. The *_part arrays are workspace partials reduced by the last kernels.
+struct BwdParams {
+  ScanParams f;
+  const void* dy;
+  void* dx;
+  void* ddelta;
+  void* dz;       // nullable (no gate)
+  float* dA;      // (dim, N)
+  float* dB;
+  float* dC;
+  float* dD;      // nullable
+  float* dbias;   // nullable
+  float* dh0;     // nullable
+  float* dB_part; // (batch, groups_per_batch, N, L)
+  float* dC_part;
+  float* dA_part; // (batch, dim, N)
+  float* dD_part; // (batch, dim)
+  float* dbias_part;
+};
+hipError_t launch_bwd(const BwdParams& q, bool bf16, hipStream_t stream);
+
 // dst[0, n) = src[0, n), or zeros when src is null
 hipError_t launch_state_copy(const float* src, float* dst, int64_t n, hipStream_t stream);
 

@@ -176,8 +176,11 @@ __device__ __forceinline__ float zoh_ratio(float dA, float w) {
 // a final partial tile, or rows that do not allow 16-byte access, take a guarded path.
 //
 // HEAD: one A and one delta per head; SUMMARY: the segment summary pass (no readout, no y);
-// GATE: y is multiplied by silu(z); ZOH: zero-order-hold B discretisation (else delta * B).
-template <typename IO, int NS, int NW, bool HEAD, bool SUMMARY, bool GATE, bool ZOH>
+// GATE: y is multiplied by silu(z); ZOH: zero-order-hold B discretisation (else delta * B);
+// CKPT: the checkpoint pass of the backward pass (no readout, no y; the state at the start of
+// every load tile is stored).
+template <typename IO, int NS, int NW, bool HEAD, bool SUMMARY, bool GATE, bool ZOH,
+          bool CKPT = false>
 // At most two workgroups fit a CU's LDS (one once the B/C tile holds more than 16 states), so
 // each SIMD holds at most two (one) of these wavefronts: the second launch bound lets the
 // compiler use the registers that this occupancy leaves.
@@ -195,12 +198,13 @@ __global__ void __launch_bounds__(64 * NW, NS <= 4 ? 2 : 1)
   constexpr int IPT = (ITEMS + NT - 1) / NT;
   constexpr int BC_ITEMS = NP * CPR;
   constexpr int BPT = (BC_ITEMS + NT - 1) / NT;
-  static_assert(!(SUMMARY && GATE), "the summary pass has no gate");
+  constexpr bool NOREAD = SUMMARY || CKPT;  // no readout, no y
+  static_assert(!(NOREAD && GATE), "the summary and checkpoint passes have no gate");
   __shared__ __align__(16) float s_du[kChannelsPerGroup * kDuStrideL];
-  __shared__ __align__(16) float s_bc[(SUMMARY ? 1 : 2) * NP * kBcStrideL];
+  __shared__ __align__(16) float s_bc[(NOREAD ? 1 : 2) * NP * kBcStrideL];
   float* const s_B = s_bc;
-  float* const s_C = s_bc + (SUMMARY ? 0 : NP * kBcStrideL);
-  __shared__ __align__(16) float s_part[SUMMARY ? 4 : NW * kChannelsPerGroup * kPartStride];
+  float* const s_C = s_bc + (NOREAD ? 0 : NP * kBcStrideL);
+  __shared__ __align__(16) float s_part[NOREAD ? 4 : NW * kChannelsPerGroup * kPartStride];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -277,9 +281,9 @@ __global__ void __launch_bounds__(64 * NW, NS <= 4 ? 2 : 1)
     xrow[it] = X + b * p.x_sb + dv * p.x_sd;
     drow_p[it] = DL + b * p.dl_sb + dr * p.dl_sd;
     zrow[it] = GATE ? Z + b * p.z_sb + dv * p.z_sd : nullptr;
-    yrow[it] = SUMMARY ? nullptr : Y + b * p.y_sb + dv * p.y_sd;
+    yrow[it] = NOREAD ? nullptr : Y + b * p.y_sb + dv * p.y_sd;
     ibias[it] = bias_p ? bias_p[dr] : 0.0f;
-    iD[it] = (!SUMMARY && Dm) ? Dm[dv] : 0.0f;
+    iD[it] = (!NOREAD && Dm) ? Dm[dv] : 0.0f;
   }
   const IO* brow[BPT];
   const IO* crow[BPT];
@@ -294,7 +298,7 @@ __global__ void __launch_bounds__(64 * NW, NS <= 4 ? 2 : 1)
     btl[it] = (itc % CPR) * V;
     const int64_t nn = min<int64_t>(bn[it], p.N - 1);
     brow[it] = Bg + nn * p.B_sn;
-    crow[it] = SUMMARY ? nullptr : Cg + nn * p.C_sn;
+    crow[it] = NOREAD ? nullptr : Cg + nn * p.C_sn;
   }
 
   // raw 16-byte words of a full load tile: each item's two halves are fetched back to back.
@@ -320,7 +324,7 @@ __global__ void __launch_bounds__(64 * NW, NS <= 4 ? 2 : 1)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         r.b[hf][it] = load16<false>(brow[it] + t0 + hf * kTB + btl[it]);
-        if constexpr (!SUMMARY) r.c[hf][it] = load16<false>(crow[it] + t0 + hf * kTB + btl[it]);
+        if constexpr (!NOREAD) r.c[hf][it] = load16<false>(crow[it] + t0 + hf * kTB + btl[it]);
       }
     }
   };
@@ -367,7 +371,7 @@ __global__ void __launch_bounds__(64 * NW, NS <= 4 ? 2 : 1)
 #pragma unroll
     for (int k = 0; k < V / 4; ++k)
       db[k] = make_float4(bv[4 * k], bv[4 * k + 1], bv[4 * k + 2], bv[4 * k + 3]);
-    if constexpr (!SUMMARY) {
+    if constexpr (!NOREAD) {
       float4* dc = reinterpret_cast<float4*>(&s_C[bn[it] * kBcStrideL + hf * kTB + btl[it]]);
 #pragma unroll
       for (int k = 0; k < V / 4; ++k)
@@ -392,7 +396,7 @@ __global__ void __launch_bounds__(64 * NW, NS <= 4 ? 2 : 1)
         if (!bown[it]) continue;
         float bv[V], cv[V];
         unpack16<IO>(rw.b[hf][it], bv);
-        if constexpr (!SUMMARY) unpack16<IO>(rw.c[hf][it], cv);
+        if constexpr (!NOREAD) unpack16<IO>(rw.c[hf][it], cv);
         if (bn[it] >= p.N) {
 #pragma unroll
           for (int e = 0; e < V; ++e) { bv[e] = 0.0f; cv[e] = 0.0f; }
@@ -438,7 +442,7 @@ __global__ void __launch_bounds__(64 * NW, NS <= 4 ? 2 : 1)
         const int cnt = bn[it] < p.N ? max(0, min(V, tb_len - btl[it])) : 0;
         float bv[V], cv[V];
         load_chunk<IO, false>(brow[it], t0 + hf * kTB + btl[it], cnt, false, bv);
-        if constexpr (!SUMMARY) {
+        if constexpr (!NOREAD) {
           load_chunk<IO, false>(crow[it], t0 + hf * kTB + btl[it], cnt, false, cv);
         } else {
 #pragma unroll
@@ -482,7 +486,7 @@ __global__ void __launch_bounds__(64 * NW, NS <= 4 ? 2 : 1)
       const f32x4 b0 = bq[0], b1 = bq[1];
       const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
       float cv[8];
-      if constexpr (!SUMMARY) {
+      if constexpr (!NOREAD) {
         const f32x4* cq = reinterpret_cast<const f32x4*>(&s_C[(n0 + j) * kBcStrideL + h0 + tt]);
         const f32x4 c0 = cq[0], c1 = cq[1];
         cv[0] = c0.x; cv[1] = c0.y; cv[2] = c0.z; cv[3] = c0.w;
@@ -499,10 +503,10 @@ __global__ void __launch_bounds__(64 * NW, NS <= 4 ? 2 : 1)
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         h[j] = fmaf(dA[q], h[j], ub[q]);
-        if constexpr (!SUMMARY) acc[q] = (j == 0) ? cv[q] * h[j] : fmaf(cv[q], h[j], acc[q]);
+        if constexpr (!NOREAD) acc[q] = (j == 0) ? cv[q] * h[j] : fmaf(cv[q], h[j], acc[q]);
       }
     }
-    if constexpr (!SUMMARY) {
+    if constexpr (!NOREAD) {
       float4* dst = reinterpret_cast<float4*>(&s_part[(w * kChannelsPerGroup + lane) * kPartStride + tt]);
       dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
       dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
@@ -511,7 +515,7 @@ __global__ void __launch_bounds__(64 * NW, NS <= 4 ? 2 : 1)
   // 4-step blocks for the software-pipelined full half
   struct Blk4 {
     f32x4 du[2];
-    f32x4 bc[NS][SUMMARY ? 1 : 2];
+    f32x4 bc[NS][NOREAD ? 1 : 2];
   };
   auto load4 = [&](Blk4& k, int h0, int tt) __attribute__((always_inline)) {
     const f32x4* src = reinterpret_cast<const f32x4*>(&s_du[lane * kDuStrideL + 2 * (h0 + tt)]);
@@ -520,7 +524,7 @@ __global__ void __launch_bounds__(64 * NW, NS <= 4 ? 2 : 1)
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       k.bc[j][0] = *reinterpret_cast<const f32x4*>(&s_B[(n0 + j) * kBcStrideL + h0 + tt]);
-      if constexpr (!SUMMARY)
+      if constexpr (!NOREAD)
         k.bc[j][1] = *reinterpret_cast<const f32x4*>(&s_C[(n0 + j) * kBcStrideL + h0 + tt]);
     }
   };
@@ -541,7 +545,7 @@ __global__ void __launch_bounds__(64 * NW, NS <= 4 ? 2 : 1)
     for (int j = 0; j < NS; ++j) {
       const float bv[4] = {k.bc[j][0].x, k.bc[j][0].y, k.bc[j][0].z, k.bc[j][0].w};
       float cv[4];
-      if constexpr (!SUMMARY) {
+      if constexpr (!NOREAD) {
         cv[0] = k.bc[j][1].x; cv[1] = k.bc[j][1].y; cv[2] = k.bc[j][1].z; cv[3] = k.bc[j][1].w;
       }
       float dA[4], ub[4];
@@ -555,10 +559,10 @@ __global__ void __launch_bounds__(64 * NW, NS <= 4 ? 2 : 1)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         h[j] = fmaf(dA[q], h[j], ub[q]);
-        if constexpr (!SUMMARY) acc[q] = (j == 0) ? cv[q] * h[j] : fmaf(cv[q], h[j], acc[q]);
+        if constexpr (!NOREAD) acc[q] = (j == 0) ? cv[q] * h[j] : fmaf(cv[q], h[j], acc[q]);
       }
     }
-    if constexpr (!SUMMARY) {
+    if constexpr (!NOREAD) {
       float4* dst = reinterpret_cast<float4*>(&s_part[(w * kChannelsPerGroup + lane) * kPartStride + tt]);
       dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
@@ -625,10 +629,22 @@ __global__ void __launch_bounds__(64 * NW, NS <= 4 ? 2 : 1)
       if (h0 >= lt_len) break;
       const int tb_len = min(kTB, lt_len - h0);
       recurrence(h0, tb_len);
-      if constexpr (!SUMMARY) {
+      if constexpr (!NOREAD) {
         __syncthreads();  // partial readouts complete
         epilogue(hf, t0, tb_len, full);
         if (hf == 0 && kTB < lt_len) __syncthreads();  // the next half overwrites them
+      }
+    }
+  };
+
+  // the checkpoint pass stores the state at the start of every load tile
+  auto store_ckpt = [&](int64_t t0) __attribute__((always_inline)) {
+    if constexpr (CKPT) {
+      if (live) {
+        float* c = p.ckpt + ((b * p.dim + d) * p.ntiles + (t0 - t_begin) / kLT) * p.N + n0;
+#pragma unroll
+        for (int j = 0; j < NS; ++j)
+          if (n0 + j < p.N) c[j] = h[j];
       }
     }
   };
@@ -643,6 +659,7 @@ __global__ void __launch_bounds__(64 * NW, NS <= 4 ? 2 : 1)
     prologue_full(raw);
     load_z(t0);
     if (i + 1 < n_full) fetch(raw, t0 + kLT);
+    store_ckpt(t0);
     __syncthreads();
     halves(t0, kLT, true);
     __syncthreads();  // LDS tiles free for the next prologue
@@ -651,6 +668,7 @@ __global__ void __launch_bounds__(64 * NW, NS <= 4 ? 2 : 1)
   for (int64_t t0 = t_begin + n_full * kLT; t0 < t_end; t0 += kLT) {
     const int lt_len = (int)min<int64_t>(kLT, t_end - t0);
     prologue_partial(t0, lt_len);
+    store_ckpt(t0);
     __syncthreads();
     halves(t0, lt_len, false);
     __syncthreads();

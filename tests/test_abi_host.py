@@ -161,6 +161,34 @@ def test_state_update_validation():
     assert call(ssm.desc_contiguous(0, 64, 1, 16), state=None, x=None) == 0
 
 
+def test_backward_validation():
+    def call(desc, **over):
+        a = dict(x=FAKE, delta=FAKE + (1 << 30), A=FAKE + (2 << 30), B=FAKE + (3 << 30),
+                 C=FAKE + (4 << 30), D=None, z=None, bias=None, h0=None, dy=FAKE + (5 << 30),
+                 dx=FAKE + (6 << 30), ddelta=FAKE + (7 << 30), dA=FAKE + (9 << 30),
+                 dB=FAKE + (10 << 30), dC=FAKE + (11 << 30), dD=None, dz=None, dbias=None,
+                 dh0=None, ws=FAKE + (20 << 30), wsb=1 << 40)
+        a.update(over)
+        return ssm.bwd_raw(desc, a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                           a["bias"], True, a["h0"], a["dy"], a["dx"], a["ddelta"], a["dA"],
+                           a["dB"], a["dC"], a["dD"], a["dz"], a["dbias"], a["dh0"], a["ws"],
+                           a["wsb"], None)
+    d = ssm.desc_contiguous(2, 64, 128, 16)
+    assert ssm.bwd_workspace_size(d) > 0
+    assert call(ssm.desc_contiguous(2, 64, 128, 32)) == -9                     # dstate > 16
+    assert call(ssm.desc_contiguous(2, 64, 128, 16, headdim=64, a_mode=ssm.SSM_A_HEAD)) == -9
+    assert call(d, dA=None) == -1
+    assert call(d, z=FAKE + (12 << 30)) == -1                                  # z without dz
+    assert call(d, dx=None) == -1
+    assert call(d, ws=None) == -7
+    assert call(d, wsb=ssm.bwd_workspace_size(d) - 4) == -7
+    assert call(d, dx=FAKE + (6 << 30) + 1) == -5
+    assert call(d, dx=FAKE + 64) == -6                                         # dx overlaps x
+    assert call(d, dB=FAKE + (11 << 30)) == -6                                 # dB overlaps dC
+    assert call(d, ws=FAKE + (10 << 30)) == -6                                 # workspace overlaps dB
+    assert ssm.bwd_workspace_size(ssm.desc_contiguous(2, 64, 0, 16)) == 0
+
+
 def test_workspace_size_depends_only_on_shape():
     assert ssm.workspace_size(ssm.desc_contiguous(8, 4096, 4096, 16)) == 0
     c3 = ssm.workspace_size(ssm.desc_contiguous(1, 2048, 1 << 20, 16))

@@ -1,0 +1,108 @@
+"""The backward pass (ssm_selective_scan_bwd) against the fp64 oracle's gradients (needs an
+MI355X). Every gradient is compared with the parity metric of the forward tests,
+max |g - g_ref| / max(|g_ref|, rms(g_ref)): within 1e-4 with fp32 I/O and 2e-2 with bf16 I/O
+(fp32 arithmetic in both; the bf16 gradients dx, ddelta, dz are rounded once to bf16).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import ssmgen
+from scan_cases import TOL, device_inputs, to_torch, y_to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import selective_state_space_24_amd as ssm
+    ssm.lib()  # fails loudly if the HIP library is not built
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _run(cfg, inputs, dy, h0=None):
+    import selective_state_space_24_amd as ssm
+    dev = device_inputs(inputs)
+    dyd = to_torch(dy, dy.dtype == np.uint16, "cuda")
+    h0d = torch.from_numpy(h0).cuda() if h0 is not None else None
+    g = ssm.selective_scan_bwd(dev["x"], dev["delta"], dev["A"], dev["B"], dev["C"], dev.get("D"),
+                               dev.get("z"), dev.get("delta_bias"), cfg.softplus, dyd, h0=h0d,
+                               want_dh0=h0 is not None)
+    torch.cuda.synchronize()
+    return {k: y_to_f64(v) for k, v in g.items()}
+
+
+def _dy(cfg, seed):
+    """dL/dy drawn N(0, 1) with the io dtype (bf16 bit patterns for bf16)."""
+    n = cfg.batch * cfg.dim * cfg.L
+    return ssmgen.fill(cfg.seed ^ 0xD1, 9, ssmgen.NORMAL, 0.0, 1.0, n, cfg.io_code).reshape(
+        cfg.batch, cfg.dim, cfg.L)
+
+
+def _compare(cfg, inputs, dy, h0=None, tol=None):
+    g = _run(cfg, inputs, dy, h0)
+    ref = oracle.scan_inputs_bwd(inputs, dy, cfg, h0=None if h0 is None else h0.astype(np.float64))
+    tol = tol or TOL[cfg.io]
+    errs = {}
+    for k, v in ref.items():
+        assert k in g, k
+        assert np.isfinite(g[k]).all(), k
+        errs[k] = oracle.rel_err(g[k], v)
+    _say(f"[bwd] errors {', '.join(f'{k} {e:.2e}' for k, e in errs.items())}")
+    bad = {k: e for k, e in errs.items() if e > tol}
+    assert not bad, f"gradients beyond {tol}: {bad}"
+
+
+CASES = [
+    # batch, dim, L, N, io, gate, softplus, D, bias, groups, h0
+    (2, 64, 100, 16, "f32", False, True, True, True, 1, False),
+    (2, 130, 77, 8, "bf16", True, True, True, True, 1, False),     # ragged dim and L
+    (1, 64, 256, 16, "f32", True, True, True, True, 1, True),      # initial state and dh0
+    (3, 128, 200, 4, "bf16", True, True, True, True, 2, False),    # two B/C groups
+    (1, 70, 130, 16, "f32", True, False, False, False, 1, False),  # no softplus, D, bias
+    (2, 64, 65, 1, "f32", True, True, True, True, 1, True),        # one state
+    (1, 96, 64, 5, "f32", False, True, True, True, 1, False),      # ragged state count
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_backward_matches_oracle(case):
+    batch, dim, L, N, io, gate, sp, hasD, bias, G, h0 = case
+    dists = {} if sp else {"delta": ssmgen.Dist(ssmgen.UNIFORM, 0.0, 0.2),
+                           "delta_bias": ssmgen.Dist(ssmgen.UNIFORM, 0.001, 0.01)}
+    cfg = ssmgen.ScanConfig(name="bwd", batch=batch, dim=dim, L=L, N=N, ngroups=G, io=io,
+                            gate=gate, softplus=sp, has_D=hasD, has_bias=bias, seed=400 + L,
+                            dists=dists)
+    _say(f"[bwd] {case}")
+    inputs = ssmgen.make_inputs(cfg)
+    hinit = np.random.default_rng(L).standard_normal((batch, dim, N)).astype(np.float32) if h0 else None
+    _compare(cfg, inputs, _dy(cfg, L), hinit)
+
+
+@pytest.mark.parametrize("ci", [0, 1])
+def test_backward_configs(ci):
+    cfg = ssmgen.CONFIGS[ci]
+    _say(f"[bwd] config {ci} {cfg.name}")
+    inputs = ssmgen.make_inputs(cfg)
+    _compare(cfg, inputs, _dy(cfg, ci))
+
+
+def test_backward_is_deterministic():
+    import selective_state_space_24_amd as ssm
+    cfg = ssmgen.ScanConfig(name="bwd-det", batch=2, dim=192, L=300, N=16, seed=5)
+    inputs = ssmgen.make_inputs(cfg)
+    dy = _dy(cfg, 1)
+    a = _run(cfg, inputs, dy)
+    b = _run(cfg, inputs, dy)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
