@@ -111,7 +111,8 @@ size_t workspace_bytes_for(const ssm_scan_desc* d, const Plan& p) {
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Workspace of the backward pass: checkpoints (batch, dim, ntiles, N), the dB and dC partials
+// Workspace of the backward pass: checkpoints (batch, dim, ntiles, N) every kTB steps, the dB
+// and dC partials
 // (batch, groups_per_batch, N, L), the dA partials (batch, dim, N), dD and dbias partials
 // (batch, dim); fp32, each section 256-byte aligned.
 struct BwdLayout {
@@ -119,7 +120,7 @@ struct BwdLayout {
 };
 
 BwdLayout bwd_layout(const ssm_scan_desc* d) {
-  const size_t ntiles = (size_t)((d->seqlen + ssm::kLT - 1) / ssm::kLT);
+  const size_t ntiles = (size_t)((d->seqlen + ssm::kTB - 1) / ssm::kTB);
   const size_t gpb = (size_t)((d->dim + ssm::kChannelsPerGroup - 1) / ssm::kChannelsPerGroup);
   const size_t B = (size_t)d->batch, D = (size_t)d->dim, N = (size_t)d->dstate, L = (size_t)d->seqlen;
   BwdLayout l;
@@ -472,7 +473,7 @@ int ssm_selective_scan_bwd(const ssm_scan_desc* desc, const void* x, const void*
   p.seg_len = d.seqlen;
   p.nseg = 1;
   p.softplus = delta_softplus ? 1 : 0;
-  p.ntiles = (d.seqlen + ssm::kLT - 1) / ssm::kLT;
+  p.ntiles = (d.seqlen + ssm::kTB - 1) / ssm::kTB;
   char* ws = static_cast<char*>(workspace);
   p.ckpt = reinterpret_cast<float*>(ws + lay.ckpt);
   // 16-byte rows for x, delta, dy, z (the checkpoint pass and the backward prologue)

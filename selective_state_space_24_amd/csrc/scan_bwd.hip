@@ -3,10 +3,10 @@
 // The pages train the layer end to end and recompute the states in the backward pass rather
 // than storing them (page "NL-345", §1 "Hardware-aware Algorithm"). Here:
 //   1. a checkpoint pass (the forward kernel without readout) stores the state at the start of
-//      every 64-step load tile: N fp32 values per channel per tile;
+//      every 32-step tile: N fp32 values per channel per tile;
 //   2. the backward kernel walks each channel group's tiles in reverse. A tile is processed in
-//      16-step sub-tiles, last first: the states of the tile's sub-tile starts are recomputed
-//      from the checkpoint, then each sub-tile's 16 states are recomputed into registers and
+//      8-step sub-tiles, last first: the states of the tile's sub-tile starts are recomputed
+//      from the checkpoint, then each sub-tile's 8 states are recomputed into registers and
 //      the reverse recurrence runs over them:
 //        gh += gy C;  dC += gy h;  ddelta += gh (a dA h_prev + B x);  da += gh dA h_prev delta;
 //        dB += gh delta x;  dx += gh delta B;  gh *= dA
@@ -17,33 +17,44 @@
 //      wave-private LDS, giving one partial per workgroup;
 //   3. reduce kernels add the partials: dB, dC over the workgroups of a batch entry's group,
 //      dA, dD, dbias over the batch, in a fixed order (results are deterministic).
-// Arithmetic: fp32. Supported: diagonal A, dstate <= 16, delta * B discretisation.
+// The LDS use (about 74 KB) lets two workgroups share a CU. Arithmetic: fp32. Supported:
+// diagonal A, dstate <= 16, delta * B discretisation.
 #include "scan_kernels.h"
 
 namespace ssm {
 
-constexpr int kSub = 16;            // steps per sub-tile (their states are held in registers)
-constexpr int kSubs = kLT / kSub;   // sub-tiles per load tile
-constexpr int kInStride = kLT + 1;  // entries per channel row of the per-step LDS arrays
+constexpr int kBT = kTB;            // steps per backward tile (the checkpoint interval)
+constexpr int kSub = 8;             // steps per sub-tile (their states are held in registers)
+constexpr int kSubs = kBT / kSub;   // sub-tiles per tile
+constexpr int kInStride = kBT + 1;  // entries per channel row of the per-step LDS arrays
 constexpr int kRedStride = kSub + 1;
 
+// sigmoid(v) from delta = softplus(v): e^delta = 1 + e^v gives sigmoid(v) = 1 - e^-delta. For
+// small delta the series delta (1 - delta/2 + delta^2/6 - delta^3/24) avoids the cancellation
+// (its first dropped term is below 1e-7 relative at delta = 0.1).
+__device__ __forceinline__ float sigmoid_from_softplus(float dl) {
+  const float series = dl * fmaf(dl, fmaf(dl, fmaf(dl, -1.0f / 24.0f, 1.0f / 6.0f), -0.5f), 1.0f);
+  return dl < 0.1f ? series : 1.0f - __builtin_amdgcn_exp2f(-dl * kLog2e);
+}
+
 template <typename IO, int NS, bool GATE>
-__global__ void __launch_bounds__(256, 1) bwd_kernel(const BwdParams q) {
+__global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
   constexpr int NW = kWavesPerGroup;
   constexpr int NT = 64 * NW;
   constexpr int NP = NS * NW;
   constexpr int V = IoTraits<IO>::kVec;
-  constexpr int CPT = kLT / V;                      // chunks per channel row of a tile
+  constexpr int CPT = kBT / V;                      // chunks per channel row of a tile
   constexpr int ITEMS = kChannelsPerGroup * CPT;
   constexpr int IPT = ITEMS / NT;                   // prologue items per thread
-  constexpr int NV = 8 * NS;                        // dB/dC values per lane per 4 steps
+  constexpr int RS = NS >= 4 ? 2 : 4;               // steps per dB/dC lane reduction
+  constexpr int NV = 2 * NS * RS;                   // dB/dC values per lane per reduction
   static_assert(ITEMS % NT == 0, "prologue items must divide evenly");
   static_assert(NV <= 32 && 64 % NV == 0, "dB/dC reduction layout");
 
-  __shared__ __align__(16) f32x4 s_in[kChannelsPerGroup * kInStride];   // delta, u, gy, x
-  __shared__ __align__(8) float2 s_in2[kChannelsPerGroup * kInStride];  // gzf, sigmoid(v)
-  __shared__ __align__(16) float s_B[NP * kBcStrideL];
-  __shared__ __align__(16) float s_C[NP * kBcStrideL];
+  __shared__ __align__(16) f32x4 s_in[kChannelsPerGroup * kInStride];  // delta, u, gy, x
+  __shared__ float s_gz[kChannelsPerGroup * kInStride];                 // dy silu'(z)
+  __shared__ __align__(16) float s_B[NP * kBT];
+  __shared__ __align__(16) float s_C[NP * kBT];
   __shared__ __align__(16) float s_red[3 * NW * kChannelsPerGroup * kRedStride];
 
   const ScanParams& p = q.f;
@@ -74,7 +85,7 @@ __global__ void __launch_bounds__(256, 1) bwd_kernel(const BwdParams q) {
     ap[j] = an[j] * kLog2e;
   }
 
-  // the epilogue's item: channel er, steps [4 * eq, 4 * eq + 4) of each sub-tile
+  // the epilogue's item: channel er, steps [2 * eq, 2 * eq + 2) of each sub-tile
   const int er = tid >> 2, eq = tid & 3;
   const int64_t ed = d0 + er;
   const bool elive = ed < p.dim;
@@ -86,8 +97,8 @@ __global__ void __launch_bounds__(256, 1) bwd_kernel(const BwdParams q) {
   for (int j = 0; j < NS; ++j) gh[j] = da[j] = 0.0f;
 
   for (int64_t tile = p.ntiles - 1; tile >= 0; --tile) {
-    const int64_t t0 = tile * kLT;
-    const int lt_len = (int)min<int64_t>(kLT, L - t0);
+    const int64_t t0 = tile * kBT;
+    const int lt_len = (int)min<int64_t>(kBT, L - t0);
 
     // ---- prologue: per (channel, step) values of the tile into LDS; padding steps are zero
 #pragma unroll
@@ -105,11 +116,10 @@ __global__ void __launch_bounds__(256, 1) bwd_kernel(const BwdParams q) {
       const float bias = (dd < p.dim && p.delta_bias) ? p.delta_bias[dv] : 0.0f;
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        float dl = 0.0f, u = 0.0f, gy = 0.0f, xx = 0.0f, gzf = 0.0f, sig = 0.0f;
+        float dl = 0.0f, u = 0.0f, gy = 0.0f, xx = 0.0f, gzf = 0.0f;
         if (e < cnt) {
           const float v = dv_raw[e] + bias;
           dl = p.softplus ? softplus_f32(v) : v;
-          sig = p.softplus ? __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v * kLog2e)) : 1.0f;
           xx = xv[e];
           u = dl * xx;
           gy = gv[e];
@@ -121,14 +131,14 @@ __global__ void __launch_bounds__(256, 1) bwd_kernel(const BwdParams q) {
           }
         }
         s_in[r * kInStride + tl + e] = f32x4{dl, u, gy, xx};
-        s_in2[r * kInStride + tl + e] = make_float2(gzf, sig);
+        s_gz[r * kInStride + tl + e] = gzf;
       }
     }
-    for (int i = tid; i < NP * kLT; i += NT) {
-      const int n = i / kLT, t = i % kLT;
+    for (int i = tid; i < NP * kBT; i += NT) {
+      const int n = i / kBT, t = i % kBT;
       const bool on = n < p.N && t < lt_len;
-      s_B[n * kBcStrideL + t] = on ? to_f32(Bg[n * p.B_sn + t0 + t]) : 0.0f;
-      s_C[n * kBcStrideL + t] = on ? to_f32(Cg[n * p.C_sn + t0 + t]) : 0.0f;
+      s_B[n * kBT + t] = on ? to_f32(Bg[n * p.B_sn + t0 + t]) : 0.0f;
+      s_C[n * kBT + t] = on ? to_f32(Cg[n * p.C_sn + t0 + t]) : 0.0f;
     }
     // the state at the start of the tile
     float h[NS];
@@ -151,7 +161,7 @@ __global__ void __launch_bounds__(256, 1) bwd_kernel(const BwdParams q) {
         const f32x4 in = s_in[lane * kInStride + t];
 #pragma unroll
         for (int j = 0; j < NS; ++j)
-          h[j] = fmaf(__builtin_amdgcn_exp2f(in.x * ap[j]), h[j], in.y * s_B[(n0 + j) * kBcStrideL + t]);
+          h[j] = fmaf(__builtin_amdgcn_exp2f(in.x * ap[j]), h[j], in.y * s_B[(n0 + j) * kBT + t]);
       }
     }
 
@@ -170,8 +180,8 @@ __global__ void __launch_bounds__(256, 1) bwd_kernel(const BwdParams q) {
         for (int j = 0; j < NS; ++j) {
           const float prev = i == 0 ? hs[k][j] : hh[i - 1][j];
           hh[i][j] = fmaf(__builtin_amdgcn_exp2f(in.x * ap[j]), prev,
-                          in.y * s_B[(n0 + j) * kBcStrideL + tb + i]);
-          acc = fmaf(s_C[(n0 + j) * kBcStrideL + tb + i], hh[i][j], acc);
+                          in.y * s_B[(n0 + j) * kBT + tb + i]);
+          acc = fmaf(s_C[(n0 + j) * kBT + tb + i], hh[i][j], acc);
         }
         yp[i] = acc;
       }
@@ -180,10 +190,10 @@ __global__ void __launch_bounds__(256, 1) bwd_kernel(const BwdParams q) {
       // wavefront w's block of s_red (its three partial arrays) doubles as its private scratch
       float* scratch = s_red + w * 3 * kChannelsPerGroup * kRedStride;
 #pragma unroll
-      for (int i4 = kSub - 4; i4 >= 0; i4 -= 4) {
+      for (int i4 = kSub - RS; i4 >= 0; i4 -= RS) {
         float red[NV];  // [tensor (dC, dB)][state j][step e]
 #pragma unroll
-        for (int e = 3; e >= 0; --e) {
+        for (int e = RS - 1; e >= 0; --e) {
           const int i = i4 + e;
           const int t = tb + i;
           const f32x4 in = s_in[lane * kInStride + t];
@@ -191,23 +201,23 @@ __global__ void __launch_bounds__(256, 1) bwd_kernel(const BwdParams q) {
           float gd = 0.0f, gx = 0.0f;
 #pragma unroll
           for (int j = 0; j < NS; ++j) {
-            const float Bv = s_B[(n0 + j) * kBcStrideL + t];
-            const float Cv = s_C[(n0 + j) * kBcStrideL + t];
+            const float Bv = s_B[(n0 + j) * kBT + t];
+            const float Cv = s_C[(n0 + j) * kBT + t];
             gh[j] = fmaf(gy, Cv, gh[j]);
-            red[j * 4 + e] = gy * hh[i][j];                        // dC
+            red[j * RS + e] = gy * hh[i][j];                       // dC
             const float dA = __builtin_amdgcn_exp2f(dl * ap[j]);
             const float hp = i == 0 ? hs[k][j] : hh[i - 1][j];
             const float tmp = hp * dA;
             gd = fmaf(gh[j], fmaf(tmp, an[j], Bv * xx), gd);
             da[j] = fmaf(gh[j] * tmp, dl, da[j]);
-            red[4 * NS + j * 4 + e] = gh[j] * u;                   // dB
+            red[RS * NS + j * RS + e] = gh[j] * u;                 // dB
             gx = fmaf(gh[j], dl * Bv, gx);
             gh[j] *= dA;
           }
           gdel[i] = gd;
           gxs[i] = gx;
         }
-        // sum the 4 steps' dC, dB over the wavefront's lanes (channels) through wave-private LDS
+        // sum the RS steps' dC, dB over the wavefront's lanes (channels) via wave-private LDS
 #pragma unroll
         for (int c = 0; c < NV; ++c) scratch[lane * (NV + 1) + c] = red[c];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -221,7 +231,7 @@ __global__ void __launch_bounds__(256, 1) bwd_kernel(const BwdParams q) {
 #pragma unroll
         for (int off = NV; off < 64; off <<= 1) sum += __shfl_xor(sum, off);
         if (lane < NV) {
-          const int tensor = col / (4 * NS), j = (col / 4) % NS, e = col % 4;
+          const int tensor = col / (RS * NS), j = (col / RS) % NS, e = col % RS;
           const int64_t t = t0 + tb + i4 + e;
           if (n0 + j < p.N && t < L) {
             float* dst = tensor == 0 ? q.dC_part : q.dB_part;
@@ -245,12 +255,12 @@ __global__ void __launch_bounds__(256, 1) bwd_kernel(const BwdParams q) {
         }
       }
       __syncthreads();
-      // epilogue: add the wavefronts' partials; dx, ddelta, dz for 4 steps of one channel
+      // epilogue: add the wavefronts' partials; dx, ddelta, dz for 2 steps of one channel
       {
-        float vx[4], vd[4], vz[4];
+        float vx[2], vd[2], vz[2];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = eq * 4 + e;
+        for (int e = 0; e < 2; ++e) {
+          const int i = eq * 2 + e;
           const int t = tb + i;
           float ys = 0.0f, gds = 0.0f, gxsum = 0.0f;
 #pragma unroll
@@ -260,21 +270,20 @@ __global__ void __launch_bounds__(256, 1) bwd_kernel(const BwdParams q) {
             gxsum += s_red[((ww * 3 + 2) * kChannelsPerGroup + er) * kRedStride + i];
           }
           const f32x4 in = s_in[er * kInStride + t];
-          const float2 in2 = s_in2[er * kInStride + t];
           const float y = fmaf(eD, in.w, ys);
-          vz[e] = in2.x * y;
+          vz[e] = s_gz[er * kInStride + t] * y;
           vx[e] = fmaf(in.z, eD, gxsum);
-          vd[e] = gds * in2.y;
+          vd[e] = gds * (p.softplus ? sigmoid_from_softplus(in.x) : 1.0f);
           dD_acc = fmaf(in.z, in.w, dD_acc);
           dbias_acc += vd[e];
         }
         if (elive) {
-          const int64_t tt = t0 + tb + eq * 4;
+          const int64_t tt = t0 + tb + eq * 2;
           IO* dxr = static_cast<IO*>(q.dx) + b * p.x_sb + ed * p.x_sd;
           IO* ddr = static_cast<IO*>(q.ddelta) + b * p.dl_sb + ed * p.dl_sd;
           IO* dzr = GATE ? static_cast<IO*>(q.dz) + b * p.z_sb + ed * p.z_sd : nullptr;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
+          for (int e = 0; e < 2; ++e) {
             if (tt + e < L) {
               store_elem(dxr + tt + e, vx[e]);
               store_elem(ddr + tt + e, vd[e]);

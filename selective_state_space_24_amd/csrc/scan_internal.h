@@ -26,9 +26,9 @@ struct ScanParams {
   void* y;
   const float* h0;          // nullable: initial state (batch, dim, N) fp32
   float* hfin;              // nullable: final state (batch, dim, N) fp32
-  float* ckpt;              // backward checkpoints: state at each load tile start,
+  float* ckpt;              // backward checkpoints: the state before every kTB-th step,
                             // ckpt[((b * dim + d) * ntiles + tile) * N + n]
-  int64_t ntiles;           // load tiles per sequence (checkpoint pass)
+  int64_t ntiles;           // ceil(L / kTB) (checkpoint pass)
   // per-segment summaries for sequences split along L (nullable when nseg == 1):
   // hend[((b * dim + d) * nseg + s) * N + n] and dsum[(b * dim + d) * nseg + s]
   float* hend;

@@ -178,7 +178,7 @@ __device__ __forceinline__ float zoh_ratio(float dA, float w) {
 // HEAD: one A and one delta per head; SUMMARY: the segment summary pass (no readout, no y);
 // GATE: y is multiplied by silu(z); ZOH: zero-order-hold B discretisation (else delta * B);
 // CKPT: the checkpoint pass of the backward pass (no readout, no y; the state at the start of
-// every load tile is stored).
+// every kTB-step half tile is stored).
 template <typename IO, int NS, int NW, bool HEAD, bool SUMMARY, bool GATE, bool ZOH,
           bool CKPT = false>
 // At most two workgroups fit a CU's LDS (one once the B/C tile holds more than 16 states), so
@@ -621,6 +621,18 @@ __global__ void __launch_bounds__(64 * NW, NS <= 4 ? 2 : 1)
     }
   };
 
+  // the checkpoint pass stores the state before step t (t a multiple of kTB)
+  auto store_ckpt = [&](int64_t t) __attribute__((always_inline)) {
+    if constexpr (CKPT) {
+      if (live) {
+        float* c = p.ckpt + ((b * p.dim + d) * p.ntiles + (t - t_begin) / kTB) * p.N + n0;
+#pragma unroll
+        for (int j = 0; j < NS; ++j)
+          if (n0 + j < p.N) c[j] = h[j];
+      }
+    }
+  };
+
   // the two halves of a load tile whose prologue is in LDS
   auto halves = [&](int64_t t0, int lt_len, bool full) __attribute__((always_inline)) {
 #pragma unroll
@@ -628,23 +640,12 @@ __global__ void __launch_bounds__(64 * NW, NS <= 4 ? 2 : 1)
       const int h0 = hf * kTB;
       if (h0 >= lt_len) break;
       const int tb_len = min(kTB, lt_len - h0);
+      if constexpr (CKPT) store_ckpt(t0 + h0);
       recurrence(h0, tb_len);
       if constexpr (!NOREAD) {
         __syncthreads();  // partial readouts complete
         epilogue(hf, t0, tb_len, full);
         if (hf == 0 && kTB < lt_len) __syncthreads();  // the next half overwrites them
-      }
-    }
-  };
-
-  // the checkpoint pass stores the state at the start of every load tile
-  auto store_ckpt = [&](int64_t t0) __attribute__((always_inline)) {
-    if constexpr (CKPT) {
-      if (live) {
-        float* c = p.ckpt + ((b * p.dim + d) * p.ntiles + (t0 - t_begin) / kLT) * p.N + n0;
-#pragma unroll
-        for (int j = 0; j < NS; ++j)
-          if (n0 + j < p.N) c[j] = h[j];
       }
     }
   };
@@ -659,7 +660,6 @@ __global__ void __launch_bounds__(64 * NW, NS <= 4 ? 2 : 1)
     prologue_full(raw);
     load_z(t0);
     if (i + 1 < n_full) fetch(raw, t0 + kLT);
-    store_ckpt(t0);
     __syncthreads();
     halves(t0, kLT, true);
     __syncthreads();  // LDS tiles free for the next prologue
@@ -668,7 +668,6 @@ __global__ void __launch_bounds__(64 * NW, NS <= 4 ? 2 : 1)
   for (int64_t t0 = t_begin + n_full * kLT; t0 < t_end; t0 += kLT) {
     const int lt_len = (int)min<int64_t>(kLT, t_end - t0);
     prologue_partial(t0, lt_len);
-    store_ckpt(t0);
     __syncthreads();
     halves(t0, lt_len, false);
     __syncthreads();
