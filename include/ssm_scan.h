@@ -50,15 +50,15 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_ABI_VERSION 2
+#define SSM_SCAN_ABI_VERSION 3
 
 typedef enum {
   SSM_OK = 0,
   SSM_ERR_NULL_ARG = -1,       /* a required pointer (desc, x, delta, A, B, C, y) is NULL */
   SSM_ERR_BAD_SHAPE = -2,      /* a size < 0, dim/dstate/ngroups/headdim < 1, dim % ngroups,
                                   dim % headdim, dstate > SSM_MAX_DSTATE (128), or sizes that overflow */
-  SSM_ERR_BAD_DTYPE = -3,      /* io_dtype, a_mode or discretization not one of the enums below,
-                                  or a nonzero reserved field */
+  SSM_ERR_BAD_DTYPE = -3,      /* io_dtype, a_mode, discretization or algorithm not one of the
+                                  enums below */
   SSM_ERR_BAD_STRIDE = -4,     /* a negative stride, or strides that make rows overlap */
   SSM_ERR_MISALIGNED = -5,     /* a pointer not aligned to its element size */
   SSM_ERR_ALIAS = -6,          /* an output (y, h_final, workspace) overlaps an input or another
@@ -130,12 +130,26 @@ const char* ssm_status_string(int status);
  *                     §2 "Discretization", eq. (4); memo page, "数式解説".) */
 typedef enum { SSM_DISC_DELTA_B = 0, SSM_DISC_ZOH = 1 } ssm_discretization;
 
+/* How the forward pass evaluates the scan. Both compute the same recurrence.
+ *   SSM_ALGO_AUTO:      the chunked form where it applies (below), else the recurrent one.
+ *   SSM_ALGO_RECURRENT: the recurrence step by step, fp32 arithmetic throughout.
+ *   SSM_ALGO_CHUNKED:   the block decomposition of the semiseparable matrix (review page of
+ *                       "Transformers are SSMs", proposed method: the SSD algorithm): per chunk
+ *                       of 64 steps a masked, decay-weighted quadratic product inside the chunk
+ *                       and a state of dstate x 64 channels passed between chunks, evaluated as
+ *                       bf16 matrix products with fp32 accumulation and an fp32 state. It applies
+ *                       to io_dtype BF16, a_mode HEAD, headdim a multiple of 64, dstate 64 or
+ *                       128, dim / ngroups a multiple of 64, 16-byte aligned x, delta, z, y, B, C,
+ *                       h0 and h_final with strides that are multiples of 8 elements. Requested
+ *                       outside that it returns SSM_ERR_UNSUPPORTED. It needs no workspace. */
+typedef enum { SSM_ALGO_AUTO = 0, SSM_ALGO_RECURRENT = 1, SSM_ALGO_CHUNKED = 2 } ssm_algorithm;
+
 /* Options of ssm_selective_scan_fwd_ext. A zero-filled struct gives ssm_selective_scan_fwd.
  * The state carried between calls lets a long sequence be scanned in pieces (the recurrence is
  * the same across a call boundary: page "NL-345", §2 "Computation", recurrent mode). */
 typedef struct ssm_scan_ext {
   int32_t discretization; /* ssm_discretization */
-  int32_t reserved;       /* must be 0 */
+  int32_t algorithm;      /* ssm_algorithm */
   const float* h0;        /* nullable: initial state (batch, dim, dstate) fp32, contiguous, read
                              before the first step; NULL starts from zeros */
   float* h_final;         /* nullable: receives the state after the last step, (batch, dim,

@@ -19,6 +19,8 @@ SSM_OK = 0
 SSM_DTYPE_F32, SSM_DTYPE_BF16 = 0, 1
 SSM_A_DIAG, SSM_A_HEAD = 0, 1
 SSM_DISC_DELTA_B, SSM_DISC_ZOH = 0, 1
+SSM_ALGO_AUTO, SSM_ALGO_RECURRENT, SSM_ALGO_CHUNKED = 0, 1, 2
+ALGORITHMS = {"auto": SSM_ALGO_AUTO, "recurrent": SSM_ALGO_RECURRENT, "chunked": SSM_ALGO_CHUNKED}
 SSM_MAX_DSTATE = 128
 
 STATUS_NAMES = {
@@ -47,7 +49,7 @@ class ScanDesc(ctypes.Structure):
 
 class ScanExt(ctypes.Structure):
     """Mirror of ``ssm_scan_ext``."""
-    _fields_ = [("discretization", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    _fields_ = [("discretization", ctypes.c_int32), ("algorithm", ctypes.c_int32),
                 ("h0", ctypes.c_void_p), ("h_final", ctypes.c_void_p)]
 
 
@@ -227,17 +229,22 @@ def describe(x, delta, A, B, C, z=None, y=None) -> ScanDesc:
 
 def selective_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
                        *, zoh: bool = False, h0=None, final_state=None, out=None,
-                       workspace=None, stream=None):
+                       algorithm: str = "auto", workspace=None, stream=None):
     """y = selective scan of torch device tensors (see ``include/ssm_scan.h``).
 
     ``zoh`` selects the zero-order-hold B discretisation. ``h0`` (batch, dim, N) float32 is the
     initial state. ``final_state`` is True (allocate) or a (batch, dim, N) float32 tensor that
     receives the state after the last step; the call then returns ``(y, final_state)``.
+    ``algorithm`` is "auto", "recurrent" or "chunked" (``ssm_algorithm``: the chunked matrix
+    form needs bf16 io and one A per head, see the header for the full conditions).
     ``out`` receives y if given (shape and dtype of x). ``workspace`` may be a uint8 device
     tensor of at least ``workspace_size`` bytes; otherwise one is allocated. ``stream`` defaults
     to the current torch stream. Raises ScanError with the library's status on failure.
     """
     import torch
+    if algorithm not in ALGORITHMS:
+        raise ValueError(f"algorithm must be one of {sorted(ALGORITHMS)}, got {algorithm!r}")
+    algo = ALGORITHMS[algorithm]
     y = out if out is not None else torch.empty_like(x, memory_format=torch.contiguous_format)
     desc = describe(x, delta, A, B, C, z, y)
     for name, t in (("D", D), ("delta_bias", delta_bias), ("h0", h0)):
@@ -263,8 +270,8 @@ def selective_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta
     args = (desc, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
             _ptr(delta_bias), delta_softplus, _ptr(y))
     tail = (_ptr(workspace) if need else None, need, sp)
-    if zoh or h0 is not None or hfin is not None:
-        ext = ScanExt(SSM_DISC_ZOH if zoh else SSM_DISC_DELTA_B, 0, _ptr(h0), _ptr(hfin))
+    if zoh or h0 is not None or hfin is not None or algo != SSM_ALGO_AUTO:
+        ext = ScanExt(SSM_DISC_ZOH if zoh else SSM_DISC_DELTA_B, algo, _ptr(h0), _ptr(hfin))
         rc = fwd_ext_raw(*args, ext, *tail)
     else:
         rc = fwd_raw(*args, *tail)

@@ -14,7 +14,7 @@ LIB = os.path.join(LIBDIR, "libssm_scan.so")
 # Kernel instantiations are split by io dtype and A mode so that the units compile in parallel.
 SOURCES = ["scan_fwd_bf16_diag.hip", "scan_fwd_bf16_head.hip", "scan_fwd_f32_diag.hip",
            "scan_fwd_f32_head.hip", "scan_state.hip", "scan_decode.hip",
-           "scan_bwd.hip", "scan_api.cpp"]
+           "scan_bwd.hip", "scan_ssd.hip", "scan_api.cpp"]
 
 # Packed fp32 instructions are switched off for all device code.
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -35,8 +35,11 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False, jobs: int = 0) -> str:
-    """Compiles every source to an object in parallel, then links the shared library."""
+def build(verbose: bool = False, jobs: int = 0, only=None) -> str:
+    """Compiles every source to an object in parallel, then links the shared library.
+
+    ``only``: names of the sources to recompile; the objects of the others are reused (they
+    must exist from an earlier full build)."""
     os.makedirs(LIBDIR, exist_ok=True)
     objdir = os.path.join(LIBDIR, "obj")
     os.makedirs(objdir, exist_ok=True)
@@ -47,6 +50,10 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
     for src in SOURCES:
         obj = os.path.join(objdir, src + ".o")
         objs.append(obj)
+        if only is not None and src not in only:
+            if not os.path.exists(obj):
+                raise RuntimeError(f"{obj} is missing: run a full build first")
+            continue
         cmd = [hipcc()] + HIPCC_FLAGS + inc + ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
@@ -82,4 +89,4 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, only=sys.argv[1:] or None))

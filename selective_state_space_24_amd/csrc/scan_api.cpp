@@ -199,7 +199,9 @@ int ssm_selective_scan_fwd_ext(const ssm_scan_desc* desc, const void* x, const v
   if (rc != SSM_OK) return rc;
   const int32_t disc = ext ? ext->discretization : SSM_DISC_DELTA_B;
   if (disc != SSM_DISC_DELTA_B && disc != SSM_DISC_ZOH) return SSM_ERR_BAD_DTYPE;
-  if (ext && ext->reserved != 0) return SSM_ERR_BAD_DTYPE;
+  const int32_t algo = ext ? ext->algorithm : SSM_ALGO_AUTO;
+  if (algo != SSM_ALGO_AUTO && algo != SSM_ALGO_RECURRENT && algo != SSM_ALGO_CHUNKED)
+    return SSM_ERR_BAD_DTYPE;
   const float* h0 = ext ? ext->h0 : nullptr;
   float* hfin = ext ? ext->h_final : nullptr;
   const ssm_scan_desc& d = *desc;
@@ -254,15 +256,6 @@ int ssm_selective_scan_fwd_ext(const ssm_scan_desc* desc, const void* x, const v
   if (d.ngroups > 1 && ch_per_group % ssm::kChannelsPerGroup != 0) return SSM_ERR_UNSUPPORTED;
 
   const Plan plan = plan_segments(desc);
-  const size_t need = workspace_bytes_for(desc, plan);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return SSM_ERR_WORKSPACE;
-  if (need > 0 && !aligned(workspace, 4)) return SSM_ERR_MISALIGNED;
-  if (need > 0) {
-    for (int i = 0; i < kInputs; ++i)
-      if (overlaps(workspace, need, in_ptrs[i], in_bytes[i])) return SSM_ERR_ALIAS;
-    if (overlaps(workspace, need, y, y_bytes)) return SSM_ERR_ALIAS;
-    if (hfin && overlaps(workspace, need, hfin, state_bytes)) return SSM_ERR_ALIAS;
-  }
 
   ssm::ScanParams p;
   memset(&p, 0, sizeof(p));
@@ -281,10 +274,6 @@ int ssm_selective_scan_fwd_ext(const ssm_scan_desc* desc, const void* x, const v
   p.nseg = (int32_t)plan.nseg;
   p.softplus = delta_softplus ? 1 : 0;
   p.zoh = disc == SSM_DISC_ZOH ? 1 : 0;
-  if (plan.nseg > 1) {
-    p.hend = static_cast<float*>(workspace);
-    p.dsum = p.hend + (size_t)d.batch * d.dim * plan.nseg * d.dstate;
-  }
   // 16-byte vector access of x/delta/z/y rows: 16-byte aligned bases, strides multiple of 16 B
   const int64_t vec = 16 / (int64_t)es;
   bool vec_ok = true;
@@ -303,8 +292,31 @@ int ssm_selective_scan_fwd_ext(const ssm_scan_desc* desc, const void* x, const v
   for (int64_t st : bstrides)
     if (st % vec) bc_vec = false;
   p.bc_vec = bc_vec ? 1 : 0;
-
   const hipStream_t hs = static_cast<hipStream_t>(stream);
+
+  // the chunked form: bf16 io, one A per head, 16-byte access everywhere (states included)
+  const bool chunked_ok = bf16 && head && ssm::ssd_supported(p) && (!h0 || aligned(h0, 16)) &&
+                          (!hfin || aligned(hfin, 16));
+  if (algo == SSM_ALGO_CHUNKED && !chunked_ok) return SSM_ERR_UNSUPPORTED;
+  if (algo != SSM_ALGO_RECURRENT && chunked_ok) {
+    const hipError_t e = ssm::launch_ssd(p, hs);
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+  }
+
+  const size_t need = workspace_bytes_for(desc, plan);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SSM_ERR_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 4)) return SSM_ERR_MISALIGNED;
+  if (need > 0) {
+    for (int i = 0; i < kInputs; ++i)
+      if (overlaps(workspace, need, in_ptrs[i], in_bytes[i])) return SSM_ERR_ALIAS;
+    if (overlaps(workspace, need, y, y_bytes)) return SSM_ERR_ALIAS;
+    if (hfin && overlaps(workspace, need, hfin, state_bytes)) return SSM_ERR_ALIAS;
+  }
+  if (plan.nseg > 1) {
+    p.hend = static_cast<float*>(workspace);
+    p.dsum = p.hend + (size_t)d.batch * d.dim * plan.nseg * d.dstate;
+  }
+
   hipError_t e;
   if (bf16) e = head ? ssm::launch_bf16_head(p, hs) : ssm::launch_bf16_diag(p, hs);
   else e = head ? ssm::launch_f32_head(p, hs) : ssm::launch_f32_diag(p, hs);

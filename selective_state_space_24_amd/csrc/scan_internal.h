@@ -77,6 +77,11 @@ struct BwdParams {
   float* dbias_part;
 };
 hipError_t launch_bwd(const BwdParams& q, bool bf16, hipStream_t stream);
+// Chunked matrix form of the head-mode forward pass (bf16 io, MFMA). ssd_supported checks the
+// shape and access conditions it needs (dstate 64 or 128, 64-channel blocks within one head and
+// one group, 16-byte vector access of every row); the caller checks h0 / hfin alignment.
+bool ssd_supported(const ScanParams& p);
+hipError_t launch_ssd(const ScanParams& p, hipStream_t stream);
 
 // dst[0, n) = src[0, n), or zeros when src is null
 hipError_t launch_state_copy(const float* src, float* dst, int64_t n, hipStream_t stream);

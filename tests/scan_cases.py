@@ -24,11 +24,11 @@ def device_inputs(inputs: dict, device="cuda"):
     return {k: to_torch(v, v.dtype == np.uint16, device) for k, v in inputs.items()}
 
 
-def run_hip(dev: dict, softplus=True, out=None):
+def run_hip(dev: dict, softplus=True, out=None, algorithm="auto"):
     import selective_state_space_24_amd as ssm
     return ssm.selective_scan_fwd(dev["x"], dev["delta"], dev["A"], dev["B"], dev["C"],
                                   dev.get("D"), dev.get("z"), dev.get("delta_bias"), softplus,
-                                  out=out)
+                                  out=out, algorithm=algorithm)
 
 
 def y_to_f64(y) -> np.ndarray:

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert ssm.abi_version() == 2
+    assert ssm.abi_version() == 3
     for code in range(-9, 1):
         s = ssm.status_string(code)
         assert s and s != "unknown status"
@@ -118,7 +118,9 @@ def test_extended_entry_point_validation():
     d = ssm.desc_contiguous(2, 64, 128, 16)
     H0, HF = FAKE + (12 << 30), FAKE + (13 << 30)
     assert _fwd_ext(d, ssm.ScanExt(2, 0, None, None)) == -3          # unknown discretisation
-    assert _fwd_ext(d, ssm.ScanExt(0, 1, None, None)) == -3          # reserved must be 0
+    assert _fwd_ext(d, ssm.ScanExt(0, 3, None, None)) == -3          # unknown algorithm
+    assert _fwd_ext(d, ssm.ScanExt(0, -1, None, None)) == -3
+    assert _fwd_ext(d, ssm.ScanExt(0, 2, None, None)) == -9          # chunked: diagonal A
     assert _fwd_ext(d, ssm.ScanExt(1, 0, H0 + 2, None)) == -5        # h0 not fp32-aligned
     assert _fwd_ext(d, ssm.ScanExt(1, 0, None, HF + 1)) == -5        # h_final not aligned
     assert _fwd_ext(d, ssm.ScanExt(0, 0, H0, H0 + 64)) == -6         # h_final overlaps h0

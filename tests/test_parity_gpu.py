@@ -50,17 +50,19 @@ def test_config_full_parity(ci):
     _say(f"[parity] config {ci} rel err {err:.3e}")
 
 
-@pytest.mark.parametrize("ci,nsamp", [(2, 24), (4, 12), (3, 6)])
-def test_config_sampled_parity(ci, nsamp):
+@pytest.mark.parametrize("ci,nsamp,algo", [(2, 24, "auto"), (4, 12, "chunked"),
+                                           (4, 6, "recurrent"), (3, 6, "auto")])
+def test_config_sampled_parity(ci, nsamp, algo):
     """Full-size run in the bench's launch configuration; sampled channels against the oracle
-    computed channel by channel from regenerated inputs."""
+    computed channel by channel from regenerated inputs. The scalar-decay heads config runs
+    through both the chunked matrix form (what "auto" picks for it) and the recurrence."""
     cfg = ssmgen.CONFIGS[ci]
-    _say(f"[parity] config {ci} {cfg.name}: generating inputs")
+    _say(f"[parity] config {ci} {cfg.name} ({algo}): generating inputs")
     dev = {}
     for name in cfg.shapes():
         dev.update(device_inputs({name: ssmgen.make_tensor(cfg, name)}))
     _say(f"[parity] config {ci}: running")
-    y = run_hip(dev)
+    y = run_hip(dev, algorithm=algo)
     torch.cuda.synchronize()
     del dev
     worst = 0.0
