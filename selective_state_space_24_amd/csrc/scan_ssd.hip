@@ -88,17 +88,25 @@ __device__ __forceinline__ void sts16(uint8_t* base, int off, u32x4 v) {
   *reinterpret_cast<u32x4*>(base + off) = v;
 }
 
-// 8 bf16 of a row starting at t (n_ok of them in range, the rest zero)
+// The 16-byte word of a row at [t, t + 8), t a multiple of 8 and the row 16-byte aligned, with
+// one aligned 16-byte load whatever t: a word that reaches past L is still read whole (an
+// aligned 16-byte block that holds a valid element lies in that element's page), and a word
+// wholly past L is replaced by the word that holds element L - 1. Every chunk thus issues the
+// same loads into the same registers, ragged last chunk or not; mask8 zeroes the elements at or
+// past L when the word is used (not here, which would make the load wait for its data).
+template <bool STREAM>
 __device__ __forceinline__ u32x4 load8(const bf16_bits* row, int64_t t, int64_t L) {
-  if (t + 8 <= L) return load16<false>(row + t);
-  uint32_t w[4] = {0, 0, 0, 0};
-  for (int e = 0; e < 8; ++e)
-    if (t + e < L) w[e >> 1] |= (uint32_t)row[t + e] << (16 * (e & 1));
-  return u32x4{w[0], w[1], w[2], w[3]};
+  return load16<STREAM>(row + (t < L ? t : ((L - 1) & ~(int64_t)7)));
 }
-__device__ __forceinline__ u32x4 load8_stream(const bf16_bits* row, int64_t t, int64_t L) {
-  if (t + 8 <= L) return load16<true>(row + t);
-  return load8(row, t, L);
+// w with the elements at index >= nv zeroed (nv = valid elements of the word; <= 0: none)
+__device__ __forceinline__ u32x4 mask8(const u32x4 w, int64_t nv) {
+  u32x4 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t keep = nv >= 2 * k + 2 ? 0xffffffffu : (nv == 2 * k + 1 ? 0x0000ffffu : 0u);
+    r[k] = w[k] & keep;
+  }
+  return r;
 }
 
 // Per-chunk step arrays in LDS, kQ floats each: s2 = s_t log2 e, w = w_t, es = e^{s_t},
@@ -163,12 +171,15 @@ __global__ void __launch_bounds__(kThreads, 1)
   const bf16_bits* dlrow = DL + b * p.dl_sb + head * p.dl_sd;
   const float Dp = Dm ? Dm[d] : 0.0f;
 
-  // staging role: thread -> one 8 x 8 block (8 states x 8 steps) of B (mat 0) or C (mat 1)
-  const bool stager = tid < 16 * NB;
-  const int mat = tid / (8 * NB);
-  const int sb = tid % (8 * NB);
-  const int nb = sb % NB;
-  const int tb = sb / NB;
+  // staging role: thread -> one 8 x 8 block (8 states x 8 steps) of B (mat 0) or C (mat 1).
+  // With N = 64 there are 128 blocks for 256 threads: the upper half of the threads loads the
+  // blocks of the lower half again (L2 hits) and writes nothing, so every load is unconditional.
+  constexpr int kBlocks = 2 * N;
+  const int blk = tid % kBlocks;
+  const bool stager = kBlocks == kThreads || tid < kBlocks;  // uniform per wavefront
+  const int mat = blk / (8 * NB);
+  const int nb = blk % NB;
+  const int tb = (blk % (8 * NB)) / NB;
   const bf16_bits* bcrow = (mat == 0 ? Bm + b * p.B_sb + grp * p.B_sg + (int64_t)(8 * nb) * p.B_sn
                                      : Cm + b * p.C_sb + grp * p.C_sg + (int64_t)(8 * nb) * p.C_sn);
   const int64_t bc_sn = mat == 0 ? p.B_sn : p.C_sn;
@@ -193,34 +204,34 @@ __global__ void __launch_bounds__(kThreads, 1)
     }
   }
 
-  // chunk loads (registers): this thread's B/C block, its x and z words, wave 3's delta.
-  // stage() moves them on: B, C and the step arrays into LDS, x and z into cx / cz, which the
-  // next chunk computes from while the loads of the one after it are in flight.
-  u32x4 pbc[8], px[2], pz[2], cx[2], cz[2];
-  float pdl = 0.0f;
-  auto issue = [&](int64_t ch) __attribute__((always_inline)) {
+  // Loads of a chunk into registers (load8: the same instructions for every chunk). B/C go to
+  // pbc and delta to pdl, which stage() moves into LDS one chunk later; x and z go to one of two
+  // register sets that the chunks use alternately, so a set is read one chunk after its loads
+  // were issued and never copied.
+  u32x4 pbc[8];
+  bf16_bits pdl = 0;
+  auto issue_bc = [&](int64_t ch) __attribute__((always_inline)) {
     const int64_t t0 = ch * kQ;
-    if (stager) {
 #pragma unroll
-      for (int r = 0; r < 8; ++r) pbc[r] = load8(bcrow + r * bc_sn, t0 + 8 * tb, L);
-    }
+    for (int r = 0; r < 8; ++r) pbc[r] = load8<false>(bcrow + r * bc_sn, t0 + 8 * tb, L);
+    const int64_t t = t0 + lane;
+    pdl = dlrow[t < L ? t : L - 1];  // past L: masked when staged
+  };
+  auto issue_xz = [&](int64_t ch, u32x4 (&xr)[2], u32x4 (&zr)[2]) __attribute__((always_inline)) {
+    const int64_t t = ch * kQ + 16 * g;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) px[s] = load8_stream(xrow, t0 + 16 * g + 8 * s, L);
+    for (int s = 0; s < 2; ++s) xr[s] = load8<true>(xrow, t + 8 * s, L);
     if constexpr (GATE) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s) pz[s] = load8_stream(zrow, t0 + 16 * g + 8 * s, L);
+      for (int s = 0; s < 2; ++s) zr[s] = load8<true>(zrow, t + 8 * s, L);
     }
-    if (wave == 3) pdl = (t0 + lane < L) ? to_f32(dlrow[t0 + lane]) : 0.0f;
   };
-  // registers -> LDS buffer `buf`: transposed and plain tiles, and the step arrays
+  // pbc / pdl -> LDS buffer `buf`: transposed and plain tiles, and the step arrays
   auto stage = [&](int buf, int64_t ch) __attribute__((always_inline)) {
     uint8_t* base = smem + buf * kBuf;
-    cx[0] = px[0];
-    cx[1] = px[1];
-    if constexpr (GATE) {
-      cz[0] = pz[0];
-      cz[1] = pz[1];
-    }
+    const int64_t nv = L - (ch * kQ + 8 * tb);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) pbc[r] = mask8(pbc[r], nv);
     if (stager) {
       uint8_t* tr = base + mat * kMat;
       // transpose the 8x8 block: output row (step) e holds states 8nb .. 8nb+8
@@ -243,7 +254,7 @@ __global__ void __launch_bounds__(kThreads, 1)
     if (wave == 3) {
       const int64_t t = ch * kQ + lane;
       const bool valid = t < L;
-      float dl = pdl + bias;
+      float dl = to_f32(pdl) + bias;
       if (softplus) dl = softplus_f32(dl);
       float a2 = dl * a_log2;  // a_t log2 e
       float w = dl;
@@ -265,87 +276,123 @@ __global__ void __launch_bounds__(kThreads, 1)
     }
   };
 
-  if (nchunks > 0) {
-    issue(0);
-    stage(0, 0);
-    if (nchunks > 1) issue(1);
-  }
-  __syncthreads();
+  // G^T tile k of the 10 causal tiles (jt <= tt), in the order (0,0) (0,1) (0,2) (0,3) (1,1)
+  // (1,2) (1,3) (2,2) (2,3) (3,3): masked, decay-weighted, split and stored into Lmat.
+  auto tile_jt = [](int k) { return k < 4 ? 0 : (k < 7 ? 1 : (k < 9 ? 2 : 3)); };
+  auto tile_tt = [](int k, int jt) { return jt + k - (jt == 0 ? 0 : (jt == 1 ? 4 : (jt == 2 ? 7 : 9))); };
+  auto store_lmat = [&](const StepArrays& A, int jt, int tt, const f32x4 acc)
+      __attribute__((always_inline)) {
+    // acc[q] = G^T[j = 16jt + 4g + q][t = 16tt + c]
+    const int t = 16 * tt + c;
+    const int j0 = 16 * jt + 4 * g;
+    const float st = A.s2[t];
+    const f32x4 sj = *reinterpret_cast<const f32x4*>(&A.s2[j0]);
+    const f32x4 wj = *reinterpret_cast<const f32x4*>(&A.w[j0]);
+    float v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      v[q] = (j0 + q <= t) ? acc[q] * __builtin_amdgcn_exp2f(st - sj[q]) * wj[q] : 0.0f;
+    const u32x2 s01 = split2(v[0], v[1]), s23 = split2(v[2], v[3]);
+    const int o = off_lm(t, 2 * jt + (g >> 1)) + 8 * (g & 1);
+    *reinterpret_cast<u32x2*>(lm + o) = u32x2{s01[0], s23[0]};
+    *reinterpret_cast<u32x2*>(lml + o) = u32x2{s01[1], s23[1]};
+  };
 
-  for (int64_t ch = 0; ch < nchunks; ++ch) {
-    const int buf = (int)(ch & 1);
+  auto chunk = [&](int64_t ch, const int buf, u32x4 (&xr)[2], u32x4 (&zr)[2])
+      __attribute__((always_inline)) {
+    u32x4 xv[2], zv[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      xv[s] = mask8(xr[s], L - (ch * kQ + 16 * g + 8 * s));
+      if constexpr (GATE) zv[s] = mask8(zr[s], L - (ch * kQ + 16 * g + 8 * s));
+    }
     const uint8_t* base = smem + buf * kBuf;
     const uint8_t* bt = base;
     const uint8_t* ct = base + kMat;
     const uint8_t* bn = base + 2 * kMat;
     const StepArrays& A = sa[buf];
     const int64_t t0 = ch * kQ;
-    const u32x4 xv[2] = {cx[0], cx[1]};
-    u32x4 zv[2];
-    if constexpr (GATE) { zv[0] = cz[0]; zv[1] = cz[1]; }
 
-    // 1. masked, decay-weighted G^T tiles -> Lmat (bf16). The 10 causal tiles (jt <= tt), in
-    //    the order (0,0) (0,1) (0,2) (0,3) (1,1) (1,2) (1,3) (2,2) (2,3) (3,3), are dealt to
-    //    the wavefronts round robin.
-    for (int k = wave; k < 10; k += 4) {
-      const int jt = k < 4 ? 0 : (k < 7 ? 1 : (k < 9 ? 2 : 3));
-      const int tt = jt + k - (jt == 0 ? 0 : (jt == 1 ? 4 : (jt == 2 ? 7 : 9)));
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // 1. Lmat: tiles wave and wave + 4 for every wavefront, wave + 8 for wavefronts 0 and 1
+    {
+      const int jt0 = tile_jt(wave), tt0 = tile_tt(wave, jt0);
+      const int jt1 = tile_jt(wave + 4), tt1 = tile_tt(wave + 4, jt1);
+      u32x4 a0[NK], b0[NK], a1[NK], b1[NK];
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        const u32x4 a = lds16(bt, off_tr<N>(16 * jt + c, 4 * kk + g));
-        const u32x4 bb = lds16(ct, off_tr<N>(16 * tt + c, 4 * kk + g));
-        acc = mma(a, bb, acc);
+        a0[kk] = lds16(bt, off_tr<N>(16 * jt0 + c, 4 * kk + g));
+        b0[kk] = lds16(ct, off_tr<N>(16 * tt0 + c, 4 * kk + g));
+        a1[kk] = lds16(bt, off_tr<N>(16 * jt1 + c, 4 * kk + g));
+        b1[kk] = lds16(ct, off_tr<N>(16 * tt1 + c, 4 * kk + g));
       }
-      // acc[q] = G^T[j = 16jt + 4g + q][t = 16tt + c]
-      const int t = 16 * tt + c;
-      const int j0 = 16 * jt + 4 * g;
-      const float st = A.s2[t];
-      const f32x4 sj = *reinterpret_cast<const f32x4*>(&A.s2[j0]);
-      const f32x4 wj = *reinterpret_cast<const f32x4*>(&A.w[j0]);
-      float v[4];
+      f32x4 g0 = {0.f, 0.f, 0.f, 0.f}, g1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        v[q] = (j0 + q <= t) ? acc[q] * __builtin_amdgcn_exp2f(st - sj[q]) * wj[q] : 0.0f;
-      const u32x2 s01 = split2(v[0], v[1]), s23 = split2(v[2], v[3]);
-      const u32x2 hi = {s01[0], s23[0]}, lo = {s01[1], s23[1]};
-      const int o = off_lm(t, 2 * jt + (g >> 1)) + 8 * (g & 1);
-      *reinterpret_cast<u32x2*>(lm + o) = hi;
-      *reinterpret_cast<u32x2*>(lml + o) = lo;
+      for (int kk = 0; kk < NK; ++kk) {
+        g0 = mma(a0[kk], b0[kk], g0);
+        g1 = mma(a1[kk], b1[kk], g1);
+      }
+      store_lmat(A, jt0, tt0, g0);
+      store_lmat(A, jt1, tt1, g1);
+      if (wave < 2) {
+        const int jt2 = tile_jt(wave + 8), tt2 = tile_tt(wave + 8, jt2);
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+          a0[kk] = lds16(bt, off_tr<N>(16 * jt2 + c, 4 * kk + g));
+          b0[kk] = lds16(ct, off_tr<N>(16 * tt2 + c, 4 * kk + g));
+        }
+        f32x4 g2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) g2 = mma(a0[kk], b0[kk], g2);
+        store_lmat(A, jt2, tt2, g2);
+      }
     }
     __syncthreads();
 
-    // 2. Y tiles: row r of tile i is step 16 (r / 4) + 4i + r % 4
-    u32x4 hb[NK], hl[NK];
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      const u32x2 a = split2(H[2 * kk][0], H[2 * kk][1]), b2 = split2(H[2 * kk][2], H[2 * kk][3]);
-      const u32x2 c2 = split2(H[2 * kk + 1][0], H[2 * kk + 1][1]);
-      const u32x2 d2 = split2(H[2 * kk + 1][2], H[2 * kk + 1][3]);
-      hb[kk] = u32x4{a[0], b2[0], c2[0], d2[0]};
-      hl[kk] = u32x4{a[1], b2[1], c2[1], d2[1]};
-    }
+    // 2. Y tiles i = 0..3: row r of tile i is step 16 (r / 4) + 4i + r % 4. First the
+    //    inter-chunk part e^{s_t} C^T H, then the intra-chunk part Lmat x.
     f32x4 Y[4];
+    {
+      int tr[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tr = 16 * (c >> 2) + 4 * i + (c & 3);
-      Y[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < 4; ++i) {
+        tr[i] = 16 * (c >> 2) + 4 * i + (c & 3);
+        Y[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        // k-slots: states 32kk + 4g + (0..3) then 32kk + 16 + 4g + (0..3), as in hb[kk]
-        const int slot = 4 * kk + (g >> 1);
-        const u32x2 lo = lds8(ct, off_tr<N>(tr, slot) + 8 * (g & 1));
-        const u32x2 hi = lds8(ct, off_tr<N>(tr, slot + 2) + 8 * (g & 1));
-        const u32x4 ca = {lo[0], lo[1], hi[0], hi[1]};
-        Y[i] = mma(ca, hb[kk], Y[i]);
-        Y[i] = mma(ca, hl[kk], Y[i]);
+        // k-slots: states 32kk + 4g + (0..3), then 32kk + 16 + 4g + (0..3)
+        const u32x2 h01 = split2(H[2 * kk][0], H[2 * kk][1]), h23 = split2(H[2 * kk][2], H[2 * kk][3]);
+        const u32x2 h45 = split2(H[2 * kk + 1][0], H[2 * kk + 1][1]);
+        const u32x2 h67 = split2(H[2 * kk + 1][2], H[2 * kk + 1][3]);
+        const u32x4 hb = {h01[0], h23[0], h45[0], h67[0]};
+        const u32x4 hl = {h01[1], h23[1], h45[1], h67[1]};
+        u32x4 ca[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int slot = 4 * kk + (g >> 1);
+          const u32x2 lo = lds8(ct, off_tr<N>(tr[i], slot) + 8 * (g & 1));
+          const u32x2 hi = lds8(ct, off_tr<N>(tr[i], slot + 2) + 8 * (g & 1));
+          ca[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Y[i] = mma(ca[i], hb, Y[i]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Y[i] = mma(ca[i], hl, Y[i]);
       }
-      const f32x4 es = *reinterpret_cast<const f32x4*>(&A.es[16 * g + 4 * i]);
-      Y[i] *= es;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Y[i] *= *reinterpret_cast<const f32x4*>(&A.es[16 * g + 4 * i]);
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        Y[i] = mma(lds16(lm, off_lm(tr, 2 * g + s)), xv[s], Y[i]);
-        Y[i] = mma(lds16(lml, off_lm(tr, 2 * g + s)), xv[s], Y[i]);
+        u32x4 la[4], ll[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          la[i] = lds16(lm, off_lm(tr[i], 2 * g + s));
+          ll[i] = lds16(lml, off_lm(tr[i], 2 * g + s));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Y[i] = mma(la[i], xv[s], Y[i]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Y[i] = mma(ll[i], xv[s], Y[i]);
       }
     }
 
@@ -371,16 +418,15 @@ __global__ void __launch_bounds__(kThreads, 1)
         out[2 * i + 1] = pack_bf16x2(v[2], v[3]);
       }
       const int64_t ts = t0 + 16 * g;
+      if (t0 + kQ <= L) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const u32x4 o = {out[4 * s], out[4 * s + 1], out[4 * s + 2], out[4 * s + 3]};
-        const int64_t t = ts + 8 * s;
-        if (t + 8 <= L) {
-          __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(yrow + t));
-        } else {
-          for (int e = 0; e < 8; ++e)
-            if (t + e < L) yrow[t + e] = (bf16_bits)((o[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+        for (int s = 0; s < 2; ++s) {
+          const u32x4 o = {out[4 * s], out[4 * s + 1], out[4 * s + 2], out[4 * s + 3]};
+          __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(yrow + ts + 8 * s));
         }
+      } else {
+        for (int e = 0; e < 16; ++e)
+          if (ts + e < L) yrow[ts + e] = (bf16_bits)((out[e >> 1] >> (16 * (e & 1))) & 0xffffu);
       }
     }
 
@@ -401,23 +447,41 @@ __global__ void __launch_bounds__(kThreads, 1)
       }
       const float eQ = A.es[kQ - 1];
 #pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        H[m] *= eQ;
+      for (int m = 0; m < NM; ++m) H[m] *= eQ;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const u32x4 ba = lds16(bn, off_bn(16 * m + c, 2 * g + s));
-          H[m] = mma(ba, xs[s], H[m]);
-          H[m] = mma(ba, xl[s], H[m]);
-        }
+      for (int s = 0; s < 2; ++s) {
+        u32x4 ba[NM];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) ba[m] = lds16(bn, off_bn(16 * m + c, 2 * g + s));
+#pragma unroll
+        for (int m = 0; m < NM; ++m) H[m] = mma(ba[m], xs[s], H[m]);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) H[m] = mma(ba[m], xl[s], H[m]);
       }
     }
 
-    // next chunk: stage the loaded registers into the other buffer, then load the one after
-    if (ch + 1 < nchunks) {
-      stage(buf ^ 1, ch + 1);
-      if (ch + 2 < nchunks) issue(ch + 2);
+    // 5. the next chunk's B/C into the other buffer, then this register set's next loads
+    if (ch + 1 < nchunks) stage(buf ^ 1, ch + 1);
+    if (ch + 2 < nchunks) {
+      issue_bc(ch + 2);
+      issue_xz(ch + 2, xr, zr);
     }
     __syncthreads();
+  };
+
+  u32x4 xa[2], za[2], xb[2], zb[2];
+  issue_bc(0);
+  issue_xz(0, xa, za);
+  stage(0, 0);
+  if (nchunks > 1) {
+    issue_bc(1);
+    issue_xz(1, xb, zb);
+  }
+  __syncthreads();
+  for (int64_t ch = 0; ch < nchunks; ch += 2) {
+    chunk(ch, 0, xa, za);
+    if (ch + 1 >= nchunks) break;
+    chunk(ch + 1, 1, xb, zb);
   }
 
   if (p.hfin) {
