@@ -15,6 +15,10 @@ is committed, counted bytes, against the 8 TB/s peak); and the fp64 CPU oracle t
 cores over whole batch entries of the same workload.
 
 ``--workload bwd`` measures the backward pass (all input gradients) of the same workload.
+``--workload heads`` measures the scalar-decay heads scan (batch 4, 64 heads x 64 channels,
+N 128, L 8192, bf16 I/O) in its chunked matrix form on the matrix cores (``--algorithm
+recurrent`` for the step-by-step recurrence instead); its roofline is HBM bandwidth, with the
+algorithmic matrix flops reported beside it against the bf16 MFMA peak.
 ``--workload decode`` measures instead one recurrent decoding step (``ssm_selective_state_update``)
 on the Mamba-1.4B layer at batch 1024: a step reads and writes the fp32 state once, so its
 roofline is HBM bandwidth. ``--copy-calibration`` runs only a plain device copy of a known size
@@ -33,7 +37,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, vendor figure
 WORKLOAD = 2           # Mamba-1.4B layer scan
+HEADS_WORKLOAD = 4     # scalar-decay heads scan
 
 
 def kernel_source_hash() -> str:
@@ -263,6 +269,80 @@ def run_bwd(args, torch):
     print(json.dumps(out), flush=True)
 
 
+def chunked_flops(cfg, Q: int = 64) -> int:
+    """Algorithmic matrix flops of the chunked form per launch, per (batch, head, chunk of Q):
+    the causal C.B tile (Q(Q+1)/2 entries of N multiply-adds), the causal intra-chunk product
+    (Q(Q+1)/2 x headdim), the inter-chunk product C^T H and the state update B x (Q N headdim
+    each); a multiply-add counts 2. The bf16 hi + lo operand pairs, which double some of the
+    executed products, are not counted."""
+    P, N = cfg.headdim, cfg.N
+    tri = Q * (Q + 1) // 2
+    per_chunk = 2 * (tri * N + tri * P + 2 * Q * N * P)
+    nchunks = (cfg.L + Q - 1) // Q
+    return per_chunk * nchunks * cfg.batch * (cfg.dim // P)
+
+
+def run_heads(args, torch):
+    import ssmgen
+    import selective_state_space_24_amd as ssm
+    cfg = ssmgen.CONFIGS[HEADS_WORKLOAD]
+    dev = device_inputs(cfg, torch)
+    y = torch.empty_like(dev["x"])
+    stream = torch.cuda.current_stream()
+    desc = ssm.describe(dev["x"], dev["delta"], dev["A"], dev["B"], dev["C"], dev["z"], y)
+    algo = ssm.ALGORITHMS[args.algorithm]
+    ext = ssm.ScanExt(ssm.SSM_DISC_DELTA_B, algo, None, None)
+    ws_bytes = ssm.workspace_size(desc) if algo == ssm.SSM_ALGO_RECURRENT else 0
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+
+    def step():
+        rc = ssm.fwd_ext_raw(desc, dev["x"].data_ptr(), dev["delta"].data_ptr(),
+                             dev["A"].data_ptr(), dev["B"].data_ptr(), dev["C"].data_ptr(),
+                             dev["D"].data_ptr(), dev["z"].data_ptr(),
+                             dev["delta_bias"].data_ptr(), True, y.data_ptr(), ext,
+                             ws.data_ptr() if ws_bytes else None, ws_bytes, stream.cuda_stream)
+        if rc != 0:
+            raise ssm.ScanError(rc, "ssm_selective_scan_fwd_ext")
+
+    ms, pct = timed_steps(step, args, torch, stream)
+    nbytes = cfg.algorithmic_bytes()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    flops = chunked_flops(cfg)
+    tflops = flops / (ms * 1e-3) / 1e12
+    chunked = algo != ssm.SSM_ALGO_RECURRENT
+    out = {
+        "metric": "selective-scan Gtoken\u00b7channel/s and achieved HBM GB/s vs peak, 1 MI355X",
+        "value": round(cfg.tokch / (ms * 1e-3) / 1e9, 3),
+        "unit": "Gtoken\u00b7channel/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 matrix products, fp32 accumulation and state" if chunked else "f32",
+        "data": "synthetic",
+        "config": {"workload": "scalar-decay heads selective scan (one A per head, B/C shared "
+                               "by all heads)" + (", chunked matrix form" if chunked else
+                                                  ", recurrent form"),
+                   "batch": cfg.batch, "d_inner": cfg.dim, "heads": cfg.dim // cfg.headdim,
+                   "headdim": cfg.headdim, "seq_len": cfg.L, "d_state": cfg.N,
+                   "io_dtype": cfg.io, "gate": "silu(z)", "delta_softplus": cfg.softplus,
+                   "algorithm": args.algorithm},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profile("heads_chunked") if chunked else None},
+        "mfma": {"algorithmic_flops": flops, "achieved_TFLOPs": round(tflops, 1),
+                 "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                 "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)} if chunked else None,
+        "step_ms": {"p10": round(pct(0.1), 5), "median": round(pct(0.5), 5),
+                    "p90": round(pct(0.9), 5)},
+        "launches_per_step": 1 if (chunked or ws_bytes == 0) else 2,
+        "kernel_source": kernel_source_hash(),
+    }
+    if args.cpu_budget > 0:
+        del dev, y
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
 def decode_bytes(cfg) -> int:
     """Algorithmic bytes of one decoding step: the fp32 state read and written, every other
     input read once and y written once."""
@@ -364,7 +444,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 skips it)")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--workload", choices=("scan", "decode", "bwd"), default="scan")
+    ap.add_argument("--workload", choices=("scan", "decode", "bwd", "heads"), default="scan")
+    ap.add_argument("--algorithm", choices=("chunked", "recurrent"), default="chunked",
+                    help="--workload heads: the form of the scan")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -400,6 +482,9 @@ def main():
         return
     if args.workload == "bwd":
         run_bwd(args, torch)
+        return
+    if args.workload == "heads":
+        run_heads(args, torch)
         return
 
     import ssmgen
