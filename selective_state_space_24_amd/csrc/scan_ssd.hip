@@ -28,8 +28,16 @@
 //      accumulator layout, and C^T is read in the same order).
 //   3. y = (Y + D x) silu(z), stored as bf16.
 //   4. H = e^{s_Q} H + B (e^{s_Q - s_j} w_j x).
-// The B and C tiles of a chunk are staged in LDS (transposed for the products over n, plain for
-// the product over j) while the next chunk's global loads are in flight; LDS is double buffered.
+//
+// Data movement: the B and C tiles of a chunk (N rows of 64 steps, as they lie in memory) go
+// from global memory straight into LDS (16-byte direct loads, no registers), one chunk ahead, in
+// a double buffer. The products over n need them transposed (step-major); those operands are read
+// with the LDS transpose read ds_read_b64_tr_b16: in each group of 16 lanes, lane i's slot q
+// receives element i % 4 of the 8 bytes that lane 4q + i / 4 addressed. A lane that addresses 4
+// consecutive steps of state row n_q thus hands step (its first step + e) of row n_q to the
+// lanes that own that step. x and z are loaded into registers one chunk ahead (two register sets
+// that the chunks use in turn), delta into a register that a wavefront turns into the chunk's
+// step arrays.
 //
 // Lane layout of v_mfma_f32_16x16x32_bf16 (lane l, g = l / 16, c = l % 16): A operand holds
 // A[c][8g .. 8g+8), B operand holds B[8g .. 8g+8)[c], the accumulator holds D[4g .. 4g+4)[c].
@@ -42,6 +50,9 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kQ = 64;   // steps per chunk
 constexpr int kPB = 64;  // channels per workgroup
@@ -62,41 +73,41 @@ __device__ __forceinline__ u32x2 split2(float a, float b) {
   return u32x2{hi, pack_bf16x2(a - lo_f(hi), b - hi_f(hi))};
 }
 
-// LDS byte offsets. Each swizzle permutes the 16-byte slots within a row so that the eight
-// lanes of one ds_read_b128 / ds_write_b128 phase hit distinct bank groups.
-//   transposed B / C tiles [t][n] (row = 2N bytes): slot ^ ((t ^ t >> 3) & 7)
-//   plain B tile [n][j] (row = 128 bytes):          slot ^ ((n ^ n >> 3) & 7)
-//   Lmat [t][j] (row = 128 bytes):                  slot ^ ((t ^ (t >> 2 & 4)) & 7)
-template <int N>
-__device__ __forceinline__ int off_tr(int t, int slot) {
-  return t * (2 * N) + ((slot ^ ((t ^ (t >> 3)) & 7)) << 4);
-}
-__device__ __forceinline__ int off_bn(int n, int slot) {
-  return n * 128 + ((slot ^ ((n ^ (n >> 3)) & 7)) << 4);
-}
+// LDS layouts (byte offsets). A staged tile is [n][64 steps] bf16, 128 bytes (8 slots of 16
+// bytes) per state row; slot s of row n is stored at slot s ^ sw(n), sw(n) = 2 (n & 3) + bit 2
+// of n. It makes the plain 16-byte reads of 8 consecutive rows and the transpose reads of 4 rows
+// x 32 bytes hit distinct bank groups.
+__device__ __forceinline__ int sw_row(int n) { return ((n & 3) << 1) | ((n >> 2) & 1); }
+__device__ __forceinline__ int off_st(int n, int slot) { return n * 128 + ((slot ^ sw_row(n)) << 4); }
+// Lmat [t][j] (row = 128 bytes): slot ^ ((t ^ (t >> 2 & 4)) & 7)
 __device__ __forceinline__ int off_lm(int t, int slot) {
   return t * 128 + ((slot ^ ((t ^ ((t >> 2) & 4)) & 7)) << 4);
 }
 
-__device__ __forceinline__ u32x4 lds16(const uint8_t* base, int off) {
-  return *reinterpret_cast<const u32x4*>(base + off);
+__device__ __forceinline__ u32x4 lds16(const lds_u8* base, int off) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(base + off);
 }
-__device__ __forceinline__ u32x2 lds8(const uint8_t* base, int off) {
-  return *reinterpret_cast<const u32x2*>(base + off);
+__device__ __forceinline__ void sts16(lds_u8* base, int off, u32x4 v) {
+  *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(base + off) = v;
 }
-__device__ __forceinline__ void sts16(uint8_t* base, int off, u32x4 v) {
-  *reinterpret_cast<u32x4*>(base + off) = v;
+__device__ __forceinline__ void sts8(lds_u8* base, int off, u32x2 v) {
+  *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(base + off) = v;
+}
+// transpose read of 4 bf16 (see the header comment for the lane mapping)
+__device__ __forceinline__ u32x2 ldtr(const lds_u8* base, int off) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<lds_s16x4*>(const_cast<lds_u8*>(base) + off));
+  return __builtin_bit_cast(u32x2, v);
 }
 
-// The 16-byte word of a row at [t, t + 8), t a multiple of 8 and the row 16-byte aligned, with
-// one aligned 16-byte load whatever t: a word that reaches past L is still read whole (an
-// aligned 16-byte block that holds a valid element lies in that element's page), and a word
-// wholly past L is replaced by the word that holds element L - 1. Every chunk thus issues the
-// same loads into the same registers, ragged last chunk or not; mask8 zeroes the elements at or
-// past L when the word is used (not here, which would make the load wait for its data).
-template <bool STREAM>
-__device__ __forceinline__ u32x4 load8(const bf16_bits* row, int64_t t, int64_t L) {
-  return load16<STREAM>(row + (t < L ? t : ((L - 1) & ~(int64_t)7)));
+// The element offset of the 16-byte word at [t, t + 8) of a row (t a multiple of 8, the row
+// 16-byte aligned) to read so that a word past L never leaves the data: it reads the word that
+// holds element L - 1 instead. A word that reaches past L is read whole: an aligned 16-byte block
+// that holds a valid element lies in that element's page. The elements at or past L are masked
+// (mask8) or zeroed in LDS when used, never when loaded, so that every chunk issues the same
+// loads and a load never waits for its data where it is issued.
+__device__ __forceinline__ int64_t word_at(int64_t t, int64_t L) {
+  return t < L ? t : ((L - 1) & ~(int64_t)7);
 }
 // w with the elements at index >= nv zeroed (nv = valid elements of the word; <= 0: none)
 __device__ __forceinline__ u32x4 mask8(const u32x4 w, int64_t nv) {
@@ -118,6 +129,35 @@ struct StepArrays {
   float cw[kQ];
 };
 
+// Direct load of 16 bytes per lane from global memory into LDS at lds + 16 * lane (lds is a
+// wave-uniform LDS byte address). Written as an instruction of its own rather than the builtin:
+// the compiler then keeps no account of it, so it never makes other LDS accesses wait for it (it
+// cannot tell which buffer the data go to). The instruction has no register result; the kernel
+// waits for it explicitly (vmcnt(0) and a barrier before the buffer is read, and no direct load
+// into a buffer is issued before a barrier has ended every read of it). Any wait count that the
+// compiler computes for its own loads only over-counts the outstanding operations with these
+// present, so it stays correct.
+// M0 (the LDS base of the load) is named as clobbered; clang warns that M0 is a reserved
+// register, which here only means that nothing else in the kernel may rely on its value across
+// the instruction (nothing does: the kernel has no other M0 user).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt with vmcnt(0) and the other counters left alone
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+// Workgroup barrier for LDS data only: this wavefront's LDS accesses complete, then s_barrier.
+// Unlike __syncthreads it does not wait for global memory operations (the next chunk's loads stay
+// in flight); the memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void sync_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // GATE: y is multiplied by silu(z).
 template <int N, bool GATE>
 __global__ void __launch_bounds__(kThreads, 1)
@@ -128,14 +168,18 @@ __global__ void __launch_bounds__(kThreads, 1)
                    const float* __restrict__ bias_p, const ScanParams p) {
   constexpr int NM = N / 16;           // state tiles of H per wavefront
   constexpr int NK = N / 32;           // k-steps of the products over n
-  constexpr int NB = N / 8;            // 8-state blocks of a staged tile
-  constexpr int kMat = kQ * 2 * N;     // bytes of one staged bf16 tile (N x kQ)
-  constexpr int kBuf = 3 * kMat;       // transposed B, transposed C, plain B
+  constexpr int kTile = N * 128;       // bytes of one staged tile (N rows x 64 bf16)
   constexpr int kLm = kQ * kQ * 2;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kBuf + 2 * kLm];
+  constexpr int kDma = N / 32;         // direct loads per matrix per lane (8 rows per load)
+  // two buffers of (B tile, C tile), Lmat hi and lo parts, step arrays: separate objects, so
+  // that the compiler sees the direct loads into one buffer apart from the reads of the other
+  __shared__ __attribute__((aligned(16))) uint8_t stage0[2 * kTile];
+  __shared__ __attribute__((aligned(16))) uint8_t stage1[2 * kTile];
+  __shared__ __attribute__((aligned(16))) uint8_t lm_hi[kLm];
+  __shared__ __attribute__((aligned(16))) uint8_t lm_lo[kLm];
   __shared__ StepArrays sa[2];
-  uint8_t* const lm = smem + 2 * kBuf;   // Lmat hi parts
-  uint8_t* const lml = lm + kLm;         // Lmat lo parts
+  lds_u8* const lm = (lds_u8*)lm_hi;    // the LDS address space
+  lds_u8* const lml = (lds_u8*)lm_lo;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -171,18 +215,14 @@ __global__ void __launch_bounds__(kThreads, 1)
   const bf16_bits* dlrow = DL + b * p.dl_sb + head * p.dl_sd;
   const float Dp = Dm ? Dm[d] : 0.0f;
 
-  // staging role: thread -> one 8 x 8 block (8 states x 8 steps) of B (mat 0) or C (mat 1).
-  // With N = 64 there are 128 blocks for 256 threads: the upper half of the threads loads the
-  // blocks of the lower half again (L2 hits) and writes nothing, so every load is unconditional.
-  constexpr int kBlocks = 2 * N;
-  const int blk = tid % kBlocks;
-  const bool stager = kBlocks == kThreads || tid < kBlocks;  // uniform per wavefront
-  const int mat = blk / (8 * NB);
-  const int nb = blk % NB;
-  const int tb = (blk % (8 * NB)) / NB;
-  const bf16_bits* bcrow = (mat == 0 ? Bm + b * p.B_sb + grp * p.B_sg + (int64_t)(8 * nb) * p.B_sn
-                                     : Cm + b * p.C_sb + grp * p.C_sg + (int64_t)(8 * nb) * p.C_sn);
-  const int64_t bc_sn = mat == 0 ? p.B_sn : p.C_sn;
+  // direct loads: load k of this wavefront fills state rows [8 (4k + wave), +8) of a tile,
+  // lane l the 16 bytes at row + l / 8, stored slot l % 8, i.e. logical slot (l % 8) ^ sw(row)
+  const int dma_r = lane >> 3;
+  const bf16_bits* Bbase = Bm + b * p.B_sb + grp * p.B_sg;
+  const bf16_bits* Cbase = Cm + b * p.C_sb + grp * p.C_sg;
+  int dma_slot[kDma];
+#pragma unroll
+  for (int k = 0; k < kDma; ++k) dma_slot[k] = (lane & 7) ^ sw_row(8 * (4 * k + wave) + dma_r);
 
   // state accumulators: H[m][q] = H[n = 16m + 4g + q][p = 16 wave + c]
   f32x4 H[NM];
@@ -204,53 +244,33 @@ __global__ void __launch_bounds__(kThreads, 1)
     }
   }
 
-  // Loads of a chunk into registers (load8: the same instructions for every chunk). B/C go to
-  // pbc and delta to pdl, which stage() moves into LDS one chunk later; x and z go to one of two
-  // register sets that the chunks use alternately, so a set is read one chunk after its loads
-  // were issued and never copied.
-  u32x4 pbc[8];
+  // Loads of chunk ch (par = ch & 1, a constant at every call): B and C into LDS buffer par, delta (this lane's step) into pdl, x and
+  // z into the given register set.
   bf16_bits pdl = 0;
-  auto issue_bc = [&](int64_t ch) __attribute__((always_inline)) {
+  auto issue = [&](int64_t ch, const int par, u32x4 (&xr)[2], u32x4 (&zr)[2])
+      __attribute__((always_inline)) {
     const int64_t t0 = ch * kQ;
+    lds_u8* buf = par ? (lds_u8*)stage1 : (lds_u8*)stage0;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) pbc[r] = load8<false>(bcrow + r * bc_sn, t0 + 8 * tb, L);
+    for (int k = 0; k < kDma; ++k) {
+      const int n = 8 * (4 * k + wave) + dma_r;
+      const int64_t tw = word_at(t0 + 8 * dma_slot[k], L);
+      const uint32_t dst = (uint32_t)(uintptr_t)(buf + 8 * (4 * k + wave) * 128);  // wave-uniform
+      dma16(Bbase + n * p.B_sn + tw, dst);
+      dma16(Cbase + n * p.C_sn + tw, dst + kTile);
+    }
     const int64_t t = t0 + lane;
-    pdl = dlrow[t < L ? t : L - 1];  // past L: masked when staged
-  };
-  auto issue_xz = [&](int64_t ch, u32x4 (&xr)[2], u32x4 (&zr)[2]) __attribute__((always_inline)) {
-    const int64_t t = ch * kQ + 16 * g;
+    pdl = dlrow[t < L ? t : L - 1];  // past L: masked when the step arrays are made
+    const int64_t tx = t0 + 16 * g;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) xr[s] = load8<true>(xrow, t + 8 * s, L);
+    for (int s = 0; s < 2; ++s) xr[s] = load16<true>(xrow + word_at(tx + 8 * s, L));
     if constexpr (GATE) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s) zr[s] = load8<true>(zrow, t + 8 * s, L);
+      for (int s = 0; s < 2; ++s) zr[s] = load16<true>(zrow + word_at(tx + 8 * s, L));
     }
   };
-  // pbc / pdl -> LDS buffer `buf`: transposed and plain tiles, and the step arrays
-  auto stage = [&](int buf, int64_t ch) __attribute__((always_inline)) {
-    uint8_t* base = smem + buf * kBuf;
-    const int64_t nv = L - (ch * kQ + 8 * tb);
-#pragma unroll
-    for (int r = 0; r < 8; ++r) pbc[r] = mask8(pbc[r], nv);
-    if (stager) {
-      uint8_t* tr = base + mat * kMat;
-      // transpose the 8x8 block: output row (step) e holds states 8nb .. 8nb+8
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t w[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t r0 = pbc[2 * k][e >> 1], r1 = pbc[2 * k + 1][e >> 1];
-          w[k] = (e & 1) ? ((r0 >> 16) | (r1 & 0xffff0000u)) : ((r0 & 0xffffu) | (r1 << 16));
-        }
-        sts16(tr, off_tr<N>(8 * tb + e, nb), u32x4{w[0], w[1], w[2], w[3]});
-      }
-      if (mat == 0) {
-        uint8_t* bn = base + 2 * kMat;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) sts16(bn, off_bn(8 * nb + r, tb), pbc[r]);
-      }
-    }
+  // step arrays of chunk ch from pdl (wavefront 3), after the loads have landed
+  auto steps = [&](int64_t ch, const int par) __attribute__((always_inline)) {
     if (wave == 3) {
       const int64_t t = ch * kQ + lane;
       const bool valid = t < L;
@@ -268,7 +288,7 @@ __global__ void __launch_bounds__(kThreads, 1)
         if (lane >= k) s2 += o;
       }
       const float sQ = __shfl(s2, 63, 64);
-      StepArrays& A = sa[buf];
+      StepArrays& A = sa[par];
       A.s2[lane] = s2;
       A.w[lane] = w;
       A.es[lane] = __builtin_amdgcn_exp2f(s2);
@@ -294,24 +314,51 @@ __global__ void __launch_bounds__(kThreads, 1)
       v[q] = (j0 + q <= t) ? acc[q] * __builtin_amdgcn_exp2f(st - sj[q]) * wj[q] : 0.0f;
     const u32x2 s01 = split2(v[0], v[1]), s23 = split2(v[2], v[3]);
     const int o = off_lm(t, 2 * jt + (g >> 1)) + 8 * (g & 1);
-    *reinterpret_cast<u32x2*>(lm + o) = u32x2{s01[0], s23[0]};
-    *reinterpret_cast<u32x2*>(lml + o) = u32x2{s01[1], s23[1]};
+    sts8(lm, o, u32x2{s01[0], s23[0]});
+    sts8(lml, o, u32x2{s01[1], s23[1]});
+  };
+  // operands of G^T tile (jt, tt), k-step kk, from the staged tiles: A = B^T rows j, B = C^T
+  // rows t; k-slots (g, 0..7) are states 32kk + 8g + (0..7). Lane 4q + r of group g addresses
+  // row 32kk + 8g + q (+ 4) at steps 16jt + 4r (+ 0..3).
+  const int tr_q = c >> 2, tr_r = c & 3;
+  auto g_operand = [&](const lds_u8* tile, int col_tile, int kk) __attribute__((always_inline)) {
+    const int n = 32 * kk + 8 * g + tr_q;
+    const int slot = 2 * col_tile + (tr_r >> 1);
+    const u32x2 lo = ldtr(tile, off_st(n, slot) + 8 * (tr_r & 1));
+    const u32x2 hi = ldtr(tile, off_st(n + 4, slot) + 8 * (tr_r & 1));
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
   };
 
-  auto chunk = [&](int64_t ch, const int buf, u32x4 (&xr)[2], u32x4 (&zr)[2])
-      __attribute__((always_inline)) {
+  // chunk ch, par = ch & 1 (a constant at both calls)
+  auto chunk = [&](int64_t ch, const int par, u32x4 (&xr)[2], u32x4 (&zr)[2], u32x4 (&xn)[2],
+                   u32x4 (&zn)[2]) __attribute__((always_inline)) {
+    lds_u8* const stg = par ? (lds_u8*)stage1 : (lds_u8*)stage0;
+    const lds_u8* bt = stg;           // B tile [n][j]
+    const lds_u8* ct = stg + kTile;   // C tile [n][t]
+    const StepArrays& A = sa[par];
+    const int64_t t0 = ch * kQ;
+    const bool more = ch + 1 < nchunks;
+    if (more) issue(ch + 1, par ^ 1, xn, zn);
+
     u32x4 xv[2], zv[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      xv[s] = mask8(xr[s], L - (ch * kQ + 16 * g + 8 * s));
-      if constexpr (GATE) zv[s] = mask8(zr[s], L - (ch * kQ + 16 * g + 8 * s));
+      xv[s] = mask8(xr[s], L - (t0 + 16 * g + 8 * s));
+      if constexpr (GATE) zv[s] = mask8(zr[s], L - (t0 + 16 * g + 8 * s));
     }
-    const uint8_t* base = smem + buf * kBuf;
-    const uint8_t* bt = base;
-    const uint8_t* ct = base + kMat;
-    const uint8_t* bn = base + 2 * kMat;
-    const StepArrays& A = sa[buf];
-    const int64_t t0 = ch * kQ;
+    if (t0 + kQ > L) {
+      // last chunk of a ragged sequence: zero the staged B, C words at steps >= L
+      lds_u8* w = stg;
+      for (int i = tid; i < 2 * N * 8; i += kThreads) {
+        const int n = (i >> 3) % N, slot = i & 7;
+        const int64_t nv = L - (t0 + 8 * slot);
+        if (nv < 8) {
+          lds_u8* tile = w + (i >= N * 8 ? kTile : 0);
+          sts16(tile, off_st(n, slot), mask8(lds16(tile, off_st(n, slot)), nv));
+        }
+      }
+      sync_lds();
+    }
 
     // 1. Lmat: tiles wave and wave + 4 for every wavefront, wave + 8 for wavefronts 0 and 1
     {
@@ -320,10 +367,10 @@ __global__ void __launch_bounds__(kThreads, 1)
       u32x4 a0[NK], b0[NK], a1[NK], b1[NK];
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        a0[kk] = lds16(bt, off_tr<N>(16 * jt0 + c, 4 * kk + g));
-        b0[kk] = lds16(ct, off_tr<N>(16 * tt0 + c, 4 * kk + g));
-        a1[kk] = lds16(bt, off_tr<N>(16 * jt1 + c, 4 * kk + g));
-        b1[kk] = lds16(ct, off_tr<N>(16 * tt1 + c, 4 * kk + g));
+        a0[kk] = g_operand(bt, jt0, kk);
+        b0[kk] = g_operand(ct, tt0, kk);
+        a1[kk] = g_operand(bt, jt1, kk);
+        b1[kk] = g_operand(ct, tt1, kk);
       }
       f32x4 g0 = {0.f, 0.f, 0.f, 0.f}, g1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -337,8 +384,8 @@ __global__ void __launch_bounds__(kThreads, 1)
         const int jt2 = tile_jt(wave + 8), tt2 = tile_tt(wave + 8, jt2);
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
-          a0[kk] = lds16(bt, off_tr<N>(16 * jt2 + c, 4 * kk + g));
-          b0[kk] = lds16(ct, off_tr<N>(16 * tt2 + c, 4 * kk + g));
+          a0[kk] = g_operand(bt, jt2, kk);
+          b0[kk] = g_operand(ct, tt2, kk);
         }
         f32x4 g2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -346,18 +393,15 @@ __global__ void __launch_bounds__(kThreads, 1)
         store_lmat(A, jt2, tt2, g2);
       }
     }
-    __syncthreads();
+    sync_lds();
 
     // 2. Y tiles i = 0..3: row r of tile i is step 16 (r / 4) + 4i + r % 4. First the
-    //    inter-chunk part e^{s_t} C^T H, then the intra-chunk part Lmat x.
+    //    inter-chunk part e^{s_t} C^T H, then the intra-chunk part Lmat x. The C^T operand: lane
+    //    4q + r of group g addresses state row 32kk + 4g + q (then + 16) at steps 16r + 4i.
     f32x4 Y[4];
     {
-      int tr[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        tr[i] = 16 * (c >> 2) + 4 * i + (c & 3);
-        Y[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      for (int i = 0; i < 4; ++i) Y[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
         // k-slots: states 32kk + 4g + (0..3), then 32kk + 16 + 4g + (0..3)
@@ -366,12 +410,13 @@ __global__ void __launch_bounds__(kThreads, 1)
         const u32x2 h67 = split2(H[2 * kk + 1][2], H[2 * kk + 1][3]);
         const u32x4 hb = {h01[0], h23[0], h45[0], h67[0]};
         const u32x4 hl = {h01[1], h23[1], h45[1], h67[1]};
+        const int n = 32 * kk + 4 * g + tr_q;
         u32x4 ca[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int slot = 4 * kk + (g >> 1);
-          const u32x2 lo = lds8(ct, off_tr<N>(tr[i], slot) + 8 * (g & 1));
-          const u32x2 hi = lds8(ct, off_tr<N>(tr[i], slot + 2) + 8 * (g & 1));
+          const int slot = 2 * tr_r + (i >> 1);
+          const u32x2 lo = ldtr(ct, off_st(n, slot) + 8 * (i & 1));
+          const u32x2 hi = ldtr(ct, off_st(n + 16, slot) + 8 * (i & 1));
           ca[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
         }
 #pragma unroll
@@ -386,8 +431,9 @@ __global__ void __launch_bounds__(kThreads, 1)
         u32x4 la[4], ll[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          la[i] = lds16(lm, off_lm(tr[i], 2 * g + s));
-          ll[i] = lds16(lml, off_lm(tr[i], 2 * g + s));
+          const int tr = 16 * (c >> 2) + 4 * i + (c & 3);
+          la[i] = lds16(lm, off_lm(tr, 2 * g + s));
+          ll[i] = lds16(lml, off_lm(tr, 2 * g + s));
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) Y[i] = mma(la[i], xv[s], Y[i]);
@@ -452,7 +498,7 @@ __global__ void __launch_bounds__(kThreads, 1)
       for (int s = 0; s < 2; ++s) {
         u32x4 ba[NM];
 #pragma unroll
-        for (int m = 0; m < NM; ++m) ba[m] = lds16(bn, off_bn(16 * m + c, 2 * g + s));
+        for (int m = 0; m < NM; ++m) ba[m] = lds16(bt, off_st(16 * m + c, 2 * g + s));
 #pragma unroll
         for (int m = 0; m < NM; ++m) H[m] = mma(ba[m], xs[s], H[m]);
 #pragma unroll
@@ -460,28 +506,24 @@ __global__ void __launch_bounds__(kThreads, 1)
       }
     }
 
-    // 5. the next chunk's B/C into the other buffer, then this register set's next loads
-    if (ch + 1 < nchunks) stage(buf ^ 1, ch + 1);
-    if (ch + 2 < nchunks) {
-      issue_bc(ch + 2);
-      issue_xz(ch + 2, xr, zr);
-    }
-    __syncthreads();
+    // 5. the next chunk's loads have landed and this chunk's stores have left (every
+    //    wavefront waits for its own; on every path, so that no global operation is in
+    //    flight where the next chunk begins), its step arrays are made, then the workgroup
+    //    moves on
+    wait_vmem_all();
+    if (more) steps(ch + 1, par ^ 1);
+    sync_lds();
   };
 
   u32x4 xa[2], za[2], xb[2], zb[2];
-  issue_bc(0);
-  issue_xz(0, xa, za);
-  stage(0, 0);
-  if (nchunks > 1) {
-    issue_bc(1);
-    issue_xz(1, xb, zb);
-  }
+  issue(0, 0, xa, za);
+  wait_vmem_all();
+  steps(0, 0);
   __syncthreads();
   for (int64_t ch = 0; ch < nchunks; ch += 2) {
-    chunk(ch, 0, xa, za);
+    chunk(ch, 0, xa, za, xb, zb);
     if (ch + 1 >= nchunks) break;
-    chunk(ch + 1, 1, xb, zb);
+    chunk(ch + 1, 1, xb, zb, xa, za);
   }
 
   if (p.hfin) {
