@@ -22,6 +22,12 @@ HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
                "-Wall", "-Wno-unused-command-line-argument"]
 
 
+# Per-source additions. The chunked kernel scales its MFMA accumulators elementwise every chunk;
+# kept in accumulation registers (AGPRs) each such operation needs a copy out and back, so its
+# accumulators are placed in ordinary VGPRs (they fit: one wavefront per SIMD).
+EXTRA_FLAGS = {"scan_ssd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _filtered(out: str) -> str:
     # the host pass does not know the packed-fp32 feature and says so; drop that line only
     return "\n".join(ln for ln in out.splitlines()
@@ -54,7 +60,8 @@ def build(verbose: bool = False, jobs: int = 0, only=None) -> str:
             if not os.path.exists(obj):
                 raise RuntimeError(f"{obj} is missing: run a full build first")
             continue
-        cmd = [hipcc()] + HIPCC_FLAGS + inc + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = ([hipcc()] + HIPCC_FLAGS + EXTRA_FLAGS.get(src, []) + inc
+               + ["-c", os.path.join(CSRC, src), "-o", obj])
         if verbose:
             print(" ".join(cmd), flush=True)
         pending.append((src, cmd))

@@ -29,15 +29,14 @@
 //   3. y = (Y + D x) silu(z), stored as bf16.
 //   4. H = e^{s_Q} H + B (e^{s_Q - s_j} w_j x).
 //
-// Data movement: the B and C tiles of a chunk (N rows of 64 steps, as they lie in memory) go
-// from global memory straight into LDS (16-byte direct loads, no registers), one chunk ahead, in
-// a double buffer. The products over n need them transposed (step-major); those operands are read
-// with the LDS transpose read ds_read_b64_tr_b16: in each group of 16 lanes, lane i's slot q
-// receives element i % 4 of the 8 bytes that lane 4q + i / 4 addressed. A lane that addresses 4
-// consecutive steps of state row n_q thus hands step (its first step + e) of row n_q to the
-// lanes that own that step. x and z are loaded into registers one chunk ahead (two register sets
-// that the chunks use in turn), delta into a register that a wavefront turns into the chunk's
-// step arrays.
+// Data movement: every input of a chunk (the B and C tiles, N rows of 64 steps; the x and z
+// tiles, 64 channel rows of 64 steps; the 64 steps of delta) goes from global memory straight
+// into LDS (16-byte direct loads, no registers), one chunk ahead, into one of two stage buffers.
+// The products over n need B and C transposed (step-major); those operands are read with the LDS
+// transpose read ds_read_b64_tr_b16: in each group of 16 lanes, lane i's slot q receives element
+// i % 4 of the 8 bytes that lane 4q + i / 4 addressed. A lane that addresses 4 consecutive steps
+// of state row n_q thus hands step (its first step + e) of row n_q to the lanes that own that
+// step. The only wait for global memory is at the end of a chunk.
 //
 // Lane layout of v_mfma_f32_16x16x32_bf16 (lane l, g = l / 16, c = l % 16): A operand holds
 // A[c][8g .. 8g+8), B operand holds B[8g .. 8g+8)[c], the accumulator holds D[4g .. 4g+4)[c].
@@ -110,7 +109,7 @@ __device__ __forceinline__ int64_t word_at(int64_t t, int64_t L) {
   return t < L ? t : ((L - 1) & ~(int64_t)7);
 }
 // w with the elements at index >= nv zeroed (nv = valid elements of the word; <= 0: none)
-__device__ __forceinline__ u32x4 mask8(const u32x4 w, int64_t nv) {
+__device__ __forceinline__ u32x4 mask8(const u32x4 w, int nv) {
   u32x4 r;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -171,10 +170,13 @@ __global__ void __launch_bounds__(kThreads, 1)
   constexpr int kTile = N * 128;       // bytes of one staged tile (N rows x 64 bf16)
   constexpr int kLm = kQ * kQ * 2;
   constexpr int kDma = N / 32;         // direct loads per matrix per lane (8 rows per load)
-  // two buffers of (B tile, C tile), Lmat hi and lo parts, step arrays: separate objects, so
-  // that the compiler sees the direct loads into one buffer apart from the reads of the other
-  __shared__ __attribute__((aligned(16))) uint8_t stage0[2 * kTile];
-  __shared__ __attribute__((aligned(16))) uint8_t stage1[2 * kTile];
+  // two stage buffers of (B tile, C tile, x tile, z tile, delta), Lmat hi and lo parts, step
+  // arrays
+  constexpr int kXT = kPB * 128;                       // x or z tile: 64 rows of 64 bf16
+  constexpr int kOffX = 2 * kTile, kOffZ = kOffX + kXT, kOffD = kOffZ + (GATE ? kXT : 0);
+  constexpr int kStage = kOffD + 128;
+  __shared__ __attribute__((aligned(16))) uint8_t stage0[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t stage1[kStage];
   __shared__ __attribute__((aligned(16))) uint8_t lm_hi[kLm];
   __shared__ __attribute__((aligned(16))) uint8_t lm_lo[kLm];
   __shared__ StepArrays sa[2];
@@ -209,8 +211,6 @@ __global__ void __launch_bounds__(kThreads, 1)
   // this lane's channel and rows
   const int pl = 16 * wave + c;
   const int64_t d = d0 + pl;
-  const bf16_bits* xrow = X + b * p.x_sb + d * p.x_sd;
-  const bf16_bits* zrow = GATE ? Z + b * p.z_sb + d * p.z_sd : nullptr;
   bf16_bits* yrow = Yo + b * p.y_sb + d * p.y_sd;
   const bf16_bits* dlrow = DL + b * p.dl_sb + head * p.dl_sd;
   const float Dp = Dm ? Dm[d] : 0.0f;
@@ -223,6 +223,17 @@ __global__ void __launch_bounds__(kThreads, 1)
   int dma_slot[kDma];
 #pragma unroll
   for (int k = 0; k < kDma; ++k) dma_slot[k] = (lane & 7) ^ sw_row(8 * (4 * k + wave) + dma_r);
+  // x and z tiles: load k (0, 1) of this wavefront fills channel rows [8 (4k + wave), +8)
+  const bf16_bits* xz_row[2];
+  const bf16_bits* zz_row[2];
+  int xz_slot[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int r = 8 * (4 * k + wave) + dma_r;
+    xz_row[k] = X + b * p.x_sb + (d0 + r) * p.x_sd;
+    zz_row[k] = GATE ? Z + b * p.z_sb + (d0 + r) * p.z_sd : nullptr;
+    xz_slot[k] = (lane & 7) ^ sw_row(r);
+  }
 
   // state accumulators: H[m][q] = H[n = 16m + 4g + q][p = 16 wave + c]
   f32x4 H[NM];
@@ -244,37 +255,40 @@ __global__ void __launch_bounds__(kThreads, 1)
     }
   }
 
-  // Loads of chunk ch (par = ch & 1, a constant at every call): B and C into LDS buffer par, delta (this lane's step) into pdl, x and
-  // z into the given register set.
-  bf16_bits pdl = 0;
-  auto issue = [&](int64_t ch, const int par, u32x4 (&xr)[2], u32x4 (&zr)[2])
-      __attribute__((always_inline)) {
+  // Direct loads of chunk ch into stage buffer par (= ch & 1, a constant at every call).
+  auto issue = [&](int64_t ch, const int par) __attribute__((always_inline)) {
     const int64_t t0 = ch * kQ;
     lds_u8* buf = par ? (lds_u8*)stage1 : (lds_u8*)stage0;
+    const uint32_t base = (uint32_t)(uintptr_t)buf;
 #pragma unroll
     for (int k = 0; k < kDma; ++k) {
       const int n = 8 * (4 * k + wave) + dma_r;
       const int64_t tw = word_at(t0 + 8 * dma_slot[k], L);
-      const uint32_t dst = (uint32_t)(uintptr_t)(buf + 8 * (4 * k + wave) * 128);  // wave-uniform
+      const uint32_t dst = base + 8 * (4 * k + wave) * 128;  // wave-uniform
       dma16(Bbase + n * p.B_sn + tw, dst);
       dma16(Cbase + n * p.C_sn + tw, dst + kTile);
     }
-    const int64_t t = t0 + lane;
-    pdl = dlrow[t < L ? t : L - 1];  // past L: masked when the step arrays are made
-    const int64_t tx = t0 + 16 * g;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) xr[s] = load16<true>(xrow + word_at(tx + 8 * s, L));
-    if constexpr (GATE) {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) zr[s] = load16<true>(zrow + word_at(tx + 8 * s, L));
+    for (int k = 0; k < 2; ++k) {
+      const int64_t tw = word_at(t0 + 8 * xz_slot[k], L);
+      const uint32_t dst = base + 8 * (4 * k + wave) * 128;
+      dma16(xz_row[k] + tw, dst + kOffX);
+      if constexpr (GATE) dma16(zz_row[k] + tw, dst + kOffZ);
     }
+    // delta: 128 bytes, lanes 0..7 of wavefront 3
+    if (wave == 3 && lane < 8) dma16(dlrow + word_at(t0 + 8 * lane, L), base + kOffD);
   };
-  // step arrays of chunk ch from pdl (wavefront 3), after the loads have landed
+  // step arrays of chunk ch (wavefront 3), after its loads have landed
   auto steps = [&](int64_t ch, const int par) __attribute__((always_inline)) {
     if (wave == 3) {
       const int64_t t = ch * kQ + lane;
       const bool valid = t < L;
-      float dl = to_f32(pdl) + bias;
+      const lds_u8* buf = par ? (const lds_u8*)stage1 : (const lds_u8*)stage0;
+      // steps past L hold other data (a word read in place of one past the end); their
+      // results are replaced below
+      const bf16_bits raw = *reinterpret_cast<const __attribute__((address_space(3))) bf16_bits*>(
+          buf + kOffD + 2 * lane);
+      float dl = to_f32(raw) + bias;
       if (softplus) dl = softplus_f32(dl);
       float a2 = dl * a_log2;  // a_t log2 e
       float w = dl;
@@ -330,28 +344,35 @@ __global__ void __launch_bounds__(kThreads, 1)
   };
 
   // chunk ch, par = ch & 1 (a constant at both calls)
-  auto chunk = [&](int64_t ch, const int par, u32x4 (&xr)[2], u32x4 (&zr)[2], u32x4 (&xn)[2],
-                   u32x4 (&zn)[2]) __attribute__((always_inline)) {
+  auto chunk = [&](int64_t ch, const int par) __attribute__((always_inline)) {
     lds_u8* const stg = par ? (lds_u8*)stage1 : (lds_u8*)stage0;
     const lds_u8* bt = stg;           // B tile [n][j]
     const lds_u8* ct = stg + kTile;   // C tile [n][t]
     const StepArrays& A = sa[par];
     const int64_t t0 = ch * kQ;
     const bool more = ch + 1 < nchunks;
-    if (more) issue(ch + 1, par ^ 1, xn, zn);
+    if (more) issue(ch + 1, par ^ 1);
 
+    // this lane's x and z: steps [16g, 16g + 16) of channel row pl
     u32x4 xv[2], zv[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      xv[s] = mask8(xr[s], L - (t0 + 16 * g + 8 * s));
-      if constexpr (GATE) zv[s] = mask8(zr[s], L - (t0 + 16 * g + 8 * s));
+      xv[s] = lds16(stg + kOffX, off_st(pl, 2 * g + s));
+      if constexpr (GATE) zv[s] = lds16(stg + kOffZ, off_st(pl, 2 * g + s));
     }
     if (t0 + kQ > L) {
-      // last chunk of a ragged sequence: zero the staged B, C words at steps >= L
+      // last chunk of a ragged sequence: mask x and z past L
+      const int lim = (int)(L - t0);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        xv[s] = mask8(xv[s], lim - (16 * g + 8 * s));
+        if constexpr (GATE) zv[s] = mask8(zv[s], lim - (16 * g + 8 * s));
+      }
+      // and zero the staged B, C words at steps >= L
       lds_u8* w = stg;
       for (int i = tid; i < 2 * N * 8; i += kThreads) {
         const int n = (i >> 3) % N, slot = i & 7;
-        const int64_t nv = L - (t0 + 8 * slot);
+        const int nv = (int)(L - t0) - 8 * slot;
         if (nv < 8) {
           lds_u8* tile = w + (i >= N * 8 ? kTile : 0);
           sts16(tile, off_st(n, slot), mask8(lds16(tile, off_st(n, slot)), nv));
@@ -515,15 +536,14 @@ __global__ void __launch_bounds__(kThreads, 1)
     sync_lds();
   };
 
-  u32x4 xa[2], za[2], xb[2], zb[2];
-  issue(0, 0, xa, za);
+  issue(0, 0);
   wait_vmem_all();
   steps(0, 0);
   __syncthreads();
   for (int64_t ch = 0; ch < nchunks; ch += 2) {
-    chunk(ch, 0, xa, za, xb, zb);
+    chunk(ch, 0);
     if (ch + 1 >= nchunks) break;
-    chunk(ch + 1, 1, xb, zb, xa, za);
+    chunk(ch + 1, 1);
   }
 
   if (p.hfin) {
