@@ -255,7 +255,8 @@ __global__ void __launch_bounds__(kThreads, 1)
     }
   }
 
-  // Direct loads of chunk ch into stage buffer par (= ch & 1, a constant at every call).
+  // Direct loads of chunk ch (B, C, x, z) into stage buffer par (= ch & 1, a constant at every
+  // call).
   auto issue = [&](int64_t ch, const int par) __attribute__((always_inline)) {
     const int64_t t0 = ch * kQ;
     lds_u8* buf = par ? (lds_u8*)stage1 : (lds_u8*)stage0;
@@ -275,8 +276,13 @@ __global__ void __launch_bounds__(kThreads, 1)
       dma16(xz_row[k] + tw, dst + kOffX);
       if constexpr (GATE) dma16(zz_row[k] + tw, dst + kOffZ);
     }
-    // delta: 128 bytes, lanes 0..7 of wavefront 3
-    if (wave == 3 && lane < 8) dma16(dlrow + word_at(t0 + 8 * lane, L), base + kOffD);
+  };
+  // Direct load of chunk ch's delta (128 bytes, lanes 0..7 of wavefront 3) into the delta slot of
+  // stage buffer ch & 1. It runs two chunks ahead, so that the step arrays of chunk ch + 1 can
+  // be made while chunk ch computes instead of at the barrier that ends chunk ch.
+  auto issue_delta = [&](int64_t ch, const int par) __attribute__((always_inline)) {
+    const uint32_t base = (uint32_t)(uintptr_t)(par ? (lds_u8*)stage1 : (lds_u8*)stage0);
+    if (wave == 3 && lane < 8) dma16(dlrow + word_at(ch * kQ + 8 * lane, L), base + kOffD);
   };
   // step arrays of chunk ch (wavefront 3), after its loads have landed
   auto steps = [&](int64_t ch, const int par) __attribute__((always_inline)) {
@@ -352,6 +358,9 @@ __global__ void __launch_bounds__(kThreads, 1)
     const int64_t t0 = ch * kQ;
     const bool more = ch + 1 < nchunks;
     if (more) issue(ch + 1, par ^ 1);
+    if (ch + 2 < nchunks) issue_delta(ch + 2, par);
+    // the step arrays of chunk ch + 1 (its delta landed before the barrier that began chunk ch)
+    if (more) steps(ch + 1, par ^ 1);
 
     // this lane's x and z: steps [16g, 16g + 16) of channel row pl
     u32x4 xv[2], zv[2];
@@ -529,14 +538,14 @@ __global__ void __launch_bounds__(kThreads, 1)
 
     // 5. the next chunk's loads have landed and this chunk's stores have left (every
     //    wavefront waits for its own; on every path, so that no global operation is in
-    //    flight where the next chunk begins), its step arrays are made, then the workgroup
-    //    moves on
+    //    flight where the next chunk begins), then the workgroup moves on
     wait_vmem_all();
-    if (more) steps(ch + 1, par ^ 1);
     sync_lds();
   };
 
   issue(0, 0);
+  issue_delta(0, 0);
+  if (nchunks > 1) issue_delta(1, 1);
   wait_vmem_all();
   steps(0, 0);
   __syncthreads();
