@@ -149,26 +149,21 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
     }
     __syncthreads();
 
-    // ---- the states at the sub-tile starts: hs[k] = state before step kSub * k
-    float hs[kSubs][NS];
+    // ---- sub-tiles, last first. The state at a sub-tile's start is recomputed from the tile's
+    // start each time (k * kSub steps): a few more steps than keeping every sub-tile start in
+    // registers, which would not fit beside the sub-tile's states.
+#pragma unroll 1
+    for (int k = kSubs - 1; k >= 0; --k) {
+      const int tb = k * kSub;
+      float hsk[NS];
 #pragma unroll
-    for (int k = 0; k < kSubs; ++k) {
-#pragma unroll
-      for (int j = 0; j < NS; ++j) hs[k][j] = h[j];
-      if (k + 1 == kSubs) break;
-      for (int i = 0; i < kSub; ++i) {
-        const int t = k * kSub + i;
+      for (int j = 0; j < NS; ++j) hsk[j] = h[j];
+      for (int t = 0; t < tb; ++t) {
         const f32x4 in = s_in[lane * kInStride + t];
 #pragma unroll
         for (int j = 0; j < NS; ++j)
-          h[j] = fmaf(__builtin_amdgcn_exp2f(in.x * ap[j]), h[j], in.y * s_B[(n0 + j) * kBT + t]);
+          hsk[j] = fmaf(__builtin_amdgcn_exp2f(in.x * ap[j]), hsk[j], in.y * s_B[(n0 + j) * kBT + t]);
       }
-    }
-
-    // ---- sub-tiles, last first (unrolled: hs is indexed by k)
-#pragma unroll
-    for (int k = kSubs - 1; k >= 0; --k) {
-      const int tb = k * kSub;
       // recompute the sub-tile's states (after each step) and the readout partials
       float hh[kSub][NS];
       float yp[kSub];
@@ -178,7 +173,7 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
         float acc = 0.0f;
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-          const float prev = i == 0 ? hs[k][j] : hh[i - 1][j];
+          const float prev = i == 0 ? hsk[j] : hh[i - 1][j];
           hh[i][j] = fmaf(__builtin_amdgcn_exp2f(in.x * ap[j]), prev,
                           in.y * s_B[(n0 + j) * kBT + tb + i]);
           acc = fmaf(s_C[(n0 + j) * kBT + tb + i], hh[i][j], acc);
@@ -186,12 +181,18 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
         yp[i] = acc;
       }
       // reverse recurrence over the sub-tile
-      float gdel[kSub], gxs[kSub];
+      float gdel[kSub];
       // wavefront w's block of s_red (its three partial arrays) doubles as its private scratch
+      // for the dB/dC lane sums, which use its first 64 (NV + 1) floats: that is within the
+      // first two arrays, so the third (rx, the dx partials) is written as the steps go
       float* scratch = s_red + w * 3 * kChannelsPerGroup * kRedStride;
+      float* rx = s_red + ((w * 3 + 2) * kChannelsPerGroup + lane) * kRedStride;
+      static_assert(kChannelsPerGroup * (NV + 1) <= 2 * kChannelsPerGroup * kRedStride,
+                    "lane-sum scratch must stay clear of the dx partials");
+      // this lane's row of the scratch: [tensor (dC, dB)][state j][step e]
+      float* red = scratch + lane * (NV + 1);
 #pragma unroll
       for (int i4 = kSub - RS; i4 >= 0; i4 -= RS) {
-        float red[NV];  // [tensor (dC, dB)][state j][step e]
 #pragma unroll
         for (int e = RS - 1; e >= 0; --e) {
           const int i = i4 + e;
@@ -206,7 +207,7 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
             gh[j] = fmaf(gy, Cv, gh[j]);
             red[j * RS + e] = gy * hh[i][j];                       // dC
             const float dA = __builtin_amdgcn_exp2f(dl * ap[j]);
-            const float hp = i == 0 ? hs[k][j] : hh[i - 1][j];
+            const float hp = i == 0 ? hsk[j] : hh[i - 1][j];
             const float tmp = hp * dA;
             gd = fmaf(gh[j], fmaf(tmp, an[j], Bv * xx), gd);
             da[j] = fmaf(gh[j] * tmp, dl, da[j]);
@@ -215,11 +216,9 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
             gh[j] *= dA;
           }
           gdel[i] = gd;
-          gxs[i] = gx;
+          rx[i] = gx;
         }
         // sum the RS steps' dC, dB over the wavefront's lanes (channels) via wave-private LDS
-#pragma unroll
-        for (int c = 0; c < NV; ++c) scratch[lane * (NV + 1) + c] = red[c];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -246,12 +245,10 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
       {
         float* ry = s_red + ((w * 3 + 0) * kChannelsPerGroup + lane) * kRedStride;
         float* rg = s_red + ((w * 3 + 1) * kChannelsPerGroup + lane) * kRedStride;
-        float* rx = s_red + ((w * 3 + 2) * kChannelsPerGroup + lane) * kRedStride;
 #pragma unroll
         for (int i = 0; i < kSub; ++i) {
           ry[i] = yp[i];
           rg[i] = gdel[i];
-          rx[i] = gxs[i];
         }
       }
       __syncthreads();
