@@ -73,10 +73,12 @@ __device__ __forceinline__ u32x2 split2(float a, float b) {
 }
 
 // LDS layouts (byte offsets). A staged tile is [n][64 steps] bf16, 128 bytes (8 slots of 16
-// bytes) per state row; slot s of row n is stored at slot s ^ sw(n), sw(n) = 2 (n & 3) + bit 2
-// of n. It makes the plain 16-byte reads of 8 consecutive rows and the transpose reads of 4 rows
-// x 32 bytes hit distinct bank groups.
-__device__ __forceinline__ int sw_row(int n) { return ((n & 3) << 1) | ((n >> 2) & 1); }
+// bytes) per state row; slot s of row n is stored at slot s ^ sw(n), sw(n) = 2 (n & 3) +
+// (bit 0 ^ bit 2 of n). sw is one-to-one on n & 7, so the plain 16-byte reads of 8 consecutive
+// rows hit distinct bank groups; the transpose reads of the C.B tile (4 rows x 32 bytes) get
+// four distinct slot pairs; those of the inter-chunk product (4 rows x 4 slots, one half of
+// each) get 8 distinct slots, i.e. no more than two lanes per bank.
+__device__ __forceinline__ int sw_row(int n) { return ((n & 3) << 1) | ((n ^ (n >> 2)) & 1); }
 __device__ __forceinline__ int off_st(int n, int slot) { return n * 128 + ((slot ^ sw_row(n)) << 4); }
 // Lmat [t][j] (row = 128 bytes): slot ^ ((t ^ (t >> 2 & 4)) & 7)
 __device__ __forceinline__ int off_lm(int t, int slot) {
