@@ -56,6 +56,8 @@ CASES = [
     (2, 256, 128, 64, "head", "bf16", True, True, True, True, 1),
     (1, 128, 64, 2, "head", "f32", True, True, False, True, 2),
     (5, 64, 1, 1, "diag", "f32", True, True, True, True, 1),
+    (11, 72, 32, 1, "diag", "bf16", True, True, True, True, 1),     # 8 lanes per channel, ragged
+    (9, 40, 12, 1, "diag", "f32", True, False, True, False, 1),     # lanes past N, ragged
 ]
 
 
