@@ -693,12 +693,382 @@ __global__ void __launch_bounds__(64 * NW, NS <= 4 ? 2 : 1)
 }
 
 // ---------------------------------------------------------------------------------------------
+// Forward kernel for dstate <= 16 with independent wavefronts.
+//
+// One wavefront = kWaveChannels (16) channels of one batch entry x all 16 (padded) states: lane l
+// holds channel c = l & 15 and states 4q .. 4q+3 with q = l >> 4. A wavefront loads its own
+// rows, computes its own step sizes, keeps its own LDS region (step sizes, the B / C tile and
+// the partial readouts of its four state quads) and never waits at a workgroup barrier, so the
+// two wavefronts on a SIMD overlap each other's phases freely. The arithmetic per state update
+// and its order are those of scan_fwd_kernel, so both kernels give bit-identical results.
+//
+// A workgroup holds kWaveGroupWaves (8) wavefronts = 128 channels, one workgroup per CU: the two
+// wavefronts that share a SIMD (w and w ^ 4) belong to the same workgroup and use the same
+// batch entry's B and C. They publish their progress in LDS after every half tile and the one
+// that is behind takes the higher issue priority, so neither finishes long after the other.
+constexpr int kWaveChannels = 16;
+constexpr int kWaveGroupWaves = 8;
+constexpr int kWaveGroupChannels = kWaveChannels * kWaveGroupWaves;
+constexpr int kWaveDuStride = 2 * kTB + 4;  // floats per channel row of (delta, u)
+constexpr int kWaveRowStride = kTB + 4;     // floats per state row of B / C, per lane row of partials
+
+template <typename IO, bool HEAD, bool GATE, bool ZOH>
+__global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
+    scan_fwd_wave_kernel(const IO* __restrict__ X, const IO* __restrict__ DL,
+                         const IO* __restrict__ Bm, const IO* __restrict__ Cm,
+                         const IO* __restrict__ Z, IO* __restrict__ Y, const float* __restrict__ Am,
+                         const float* __restrict__ Dm, const float* __restrict__ bias_p,
+                         const float* __restrict__ hend, const float* __restrict__ dsum,
+                         const ScanParams p) {
+  constexpr int V = IoTraits<IO>::kVec;
+  constexpr int PPR = kTB / V;                  // 16-byte pieces per row of a half tile
+  constexpr int CPL = kWaveChannels * PPR / 64;  // pieces per lane per half (x, delta, z, y, B, C)
+  static_assert(CPL * 64 == kWaveChannels * PPR, "every lane owns whole pieces");
+  static_assert(kWaveChannels == 16, "B / C pieces cover exactly the 16 padded states");
+  __shared__ __align__(16) float s_du[kWaveGroupWaves][kWaveChannels * kWaveDuStride];
+  __shared__ __align__(16) float s_bc[kWaveGroupWaves][2 * 16 * kWaveRowStride];
+  __shared__ __align__(16) float s_part[kWaveGroupWaves][64 * kWaveRowStride];
+  __shared__ int s_prog[kWaveGroupWaves];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  float* const du = s_du[w];
+  float* const sB = s_bc[w];
+  float* const sC = s_bc[w] + 16 * kWaveRowStride;
+  float* const part = s_part[w];
+  const int c = lane & 15, q = lane >> 4;
+  const int64_t gpb = (p.dim + kWaveGroupChannels - 1) / kWaveGroupChannels;
+  const int64_t b = blockIdx.x / gpb;
+  const int64_t d0 = (blockIdx.x % gpb) * kWaveGroupChannels + w * kWaveChannels;
+  if (lane == 0) s_prog[w] = 0;
+  __syncthreads();
+  if (d0 >= p.dim) return;  // a wavefront past the last channel (its partner keeps going)
+
+  const int seg = blockIdx.y;
+  const int64_t t_begin = (int64_t)seg * p.seg_len;
+  const int64_t t_end = min(p.L, t_begin + p.seg_len);
+  const bool softplus = p.softplus != 0;
+  // 16 channels never straddle a B / C group: dim / ngroups is a multiple of 64 when ngroups > 1
+  const int64_t grp = d0 / (p.dim / p.ngroups);
+  const IO* __restrict__ Bg = Bm + b * p.B_sb + grp * p.B_sg;
+  const IO* __restrict__ Cg = Cm + b * p.C_sb + grp * p.C_sg;
+
+  // ---- recurrence lane: channel d, states 4q .. 4q+3 (states >= N have A = 0 and B = C = 0)
+  const int64_t d = d0 + c;
+  const bool live = d < p.dim;
+  float ap[HEAD ? 1 : 4];
+  if constexpr (HEAD) {
+    ap[0] = live ? Am[d / p.headdim] * kLog2e : 0.0f;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      ap[j] = (live && 4 * q + j < p.N) ? Am[d * p.N + 4 * q + j] * kLog2e : 0.0f;
+  }
+  float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (p.h0 && live) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (4 * q + j < p.N) h[j] = p.h0[(b * p.dim + d) * p.N + 4 * q + j];
+  }
+  if (seg > 0 && live) {
+    // compose the summaries of segments 0 .. seg-1: h <- exp(A * sum delta) h + h_end
+    const int64_t base = (b * p.dim + d) * p.nseg;
+    for (int s = 0; s < seg; ++s) {
+      const float ds = dsum[base + s];
+      const float* he = hend + (base + s) * p.N;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a = HEAD ? ap[0] : ap[j];
+        if (4 * q + j < p.N) h[j] = __builtin_amdgcn_exp2f(a * ds) * h[j] + he[4 * q + j];
+      }
+    }
+  }
+
+  // ---- this lane's io pieces: piece k = lane + 64 i covers row k / PPR (a channel for x,
+  // delta, z and y; a state for B and C) and steps (k % PPR) * V .. + V of a half tile
+  const IO* xr[CPL];
+  const IO* dr[CPL];
+  const IO* zr[CPL];
+  IO* yr[CPL];
+  const IO* br[CPL];
+  const IO* cr[CPL];
+  float pb[CPL], pD[CPL];
+  int prow[CPL], pt[CPL];
+  bool plive[CPL], bvalid[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int k = lane + 64 * i;
+    prow[i] = k / PPR;
+    pt[i] = (k % PPR) * V;
+    const int64_t dd = d0 + prow[i];
+    plive[i] = dd < p.dim;
+    const int64_t dv = min(dd, p.dim - 1);  // rows past dim read a valid row (never stored)
+    const int64_t dh = HEAD ? dv / p.headdim : dv;
+    xr[i] = X + b * p.x_sb + dv * p.x_sd;
+    dr[i] = DL + b * p.dl_sb + dh * p.dl_sd;
+    zr[i] = GATE ? Z + b * p.z_sb + dv * p.z_sd : nullptr;
+    yr[i] = Y + b * p.y_sb + dv * p.y_sd;
+    pb[i] = bias_p ? bias_p[dh] : 0.0f;
+    pD[i] = Dm ? Dm[dv] : 0.0f;
+    bvalid[i] = prow[i] < p.N;
+    const int64_t nn = min<int64_t>(prow[i], p.N - 1);
+    br[i] = Bg + nn * p.B_sn;
+    cr[i] = Cg + nn * p.C_sn;
+  }
+
+  // raw 16-byte words of one full load tile (both halves, every input)
+  struct Raw {
+    u32x4 x[2][CPL], d[2][CPL], z[2][CPL], b[2][CPL], c[2][CPL];
+  };
+  auto fetch = [&](Raw& r, int64_t t0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        r.x[hf][i] = load16<true>(xr[i] + t0 + hf * kTB + pt[i]);
+        r.d[hf][i] = load16<true>(dr[i] + t0 + hf * kTB + pt[i]);
+        if constexpr (GATE) r.z[hf][i] = load16<true>(zr[i] + t0 + hf * kTB + pt[i]);
+        r.b[hf][i] = load16<false>(br[i] + t0 + hf * kTB + pt[i]);
+        r.c[hf][i] = load16<false>(cr[i] + t0 + hf * kTB + pt[i]);
+      }
+    }
+  };
+
+  // delta and u = delta * x of piece i into the channel rows; B and C into the state rows
+  auto put_du = [&](int i, const float (&xv)[V], const float (&dv)[V]) __attribute__((always_inline)) {
+    float o[2 * V];
+    if (softplus) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) o[2 * e] = softplus_f32(dv[e] + pb[i]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < V; ++e) o[2 * e] = dv[e] + pb[i];
+    }
+#pragma unroll
+    for (int e = 0; e < V; ++e) o[2 * e + 1] = o[2 * e] * xv[e];
+    f32x4* dst = reinterpret_cast<f32x4*>(&du[prow[i] * kWaveDuStride + 2 * pt[i]]);
+#pragma unroll
+    for (int k = 0; k < V / 2; ++k) dst[k] = f32x4{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]};
+  };
+  auto put_bc = [&](int i, const float (&bv)[V], const float (&cv)[V]) __attribute__((always_inline)) {
+    f32x4* db = reinterpret_cast<f32x4*>(&sB[prow[i] * kWaveRowStride + pt[i]]);
+    f32x4* dc = reinterpret_cast<f32x4*>(&sC[prow[i] * kWaveRowStride + pt[i]]);
+    const float m = bvalid[i] ? 1.0f : 0.0f;  // padding states: B = C = 0
+#pragma unroll
+    for (int k = 0; k < V / 4; ++k) {
+      db[k] = f32x4{bv[4 * k], bv[4 * k + 1], bv[4 * k + 2], bv[4 * k + 3]} * m;
+      dc[k] = f32x4{cv[4 * k], cv[4 * k + 1], cv[4 * k + 2], cv[4 * k + 3]} * m;
+    }
+  };
+  auto prologue_full = [&](const Raw& r, int hf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      float xv[V], dv[V], bv[V], cv[V];
+      unpack16<IO>(r.x[hf][i], xv);
+      unpack16<IO>(r.d[hf][i], dv);
+      unpack16<IO>(r.b[hf][i], bv);
+      unpack16<IO>(r.c[hf][i], cv);
+      put_du(i, xv, dv);
+      put_bc(i, bv, cv);
+    }
+  };
+  // a partial half (or rows without 16-byte access) with guarded element loads; padding steps
+  // get delta = u = 0 (dA = 1, no input) and B = C = 0
+  float xk[CPL][V], zk[CPL][V];
+  auto prologue_partial = [&](int64_t t0, int len) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int cnt = max(0, min(V, len - pt[i]));
+      const int ccnt = plive[i] ? cnt : 0;
+      float dv[V], bv[V], cv[V];
+      load_chunk<IO, true>(xr[i], t0 + pt[i], ccnt, false, xk[i]);
+      load_chunk<IO, true>(dr[i], t0 + pt[i], ccnt, false, dv);
+      if constexpr (GATE) load_chunk<IO, true>(zr[i], t0 + pt[i], ccnt, false, zk[i]);
+      load_chunk<IO, false>(br[i], t0 + pt[i], bvalid[i] ? cnt : 0, false, bv);
+      load_chunk<IO, false>(cr[i], t0 + pt[i], bvalid[i] ? cnt : 0, false, cv);
+      put_du(i, xk[i], dv);
+      if (cnt < V) {
+        float* row = &du[prow[i] * kWaveDuStride + 2 * pt[i]];
+        for (int e = cnt; e < V; ++e) { row[2 * e] = 0.0f; row[2 * e + 1] = 0.0f; }
+      }
+      put_bc(i, bv, cv);
+    }
+  };
+
+  // the recurrence over one half tile in 4-step blocks, each read from LDS one block ahead.
+  // The LDS rows were written by other lanes of this wavefront: a wavefront's LDS operations
+  // complete in issue order, so no barrier is needed.
+  struct Blk {
+    f32x4 du[2];
+    f32x4 bq[4], cq[4];  // [state j] 4 steps of B and C
+  };
+  auto load_blk = [&](Blk& k, int tt) __attribute__((always_inline)) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(&du[c * kWaveDuStride + 2 * tt]);
+    k.du[0] = src[0];
+    k.du[1] = src[1];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      k.bq[j] = *reinterpret_cast<const f32x4*>(&sB[(4 * q + j) * kWaveRowStride + tt]);
+      k.cq[j] = *reinterpret_cast<const f32x4*>(&sC[(4 * q + j) * kWaveRowStride + tt]);
+    }
+  };
+  auto comp_blk = [&](const Blk& k, int tt) __attribute__((always_inline)) {
+    const float dl[4] = {k.du[0].x, k.du[0].z, k.du[1].x, k.du[1].z};
+    const float u[4] = {k.du[0].y, k.du[0].w, k.du[1].y, k.du[1].w};
+    float dAh[HEAD ? 4 : 1], gh[HEAD && ZOH ? 4 : 1];
+    if constexpr (HEAD) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        dAh[s] = __builtin_amdgcn_exp2f(dl[s] * ap[0]);
+        if constexpr (ZOH) gh[s] = zoh_ratio(dAh[s], dl[s] * ap[0]);
+      }
+    }
+    // the discretised step of all four states first, then the updates step by step: the four
+    // states' multiply-adds of one step are independent of each other
+    float dA[4][4], ub[4][4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (HEAD) dA[j][s] = dAh[s];
+        else dA[j][s] = __builtin_amdgcn_exp2f(dl[s] * ap[j]);
+        ub[j][s] = u[s] * k.bq[j][s];
+        if constexpr (ZOH) ub[j][s] *= HEAD ? gh[s] : zoh_ratio(dA[j][s], dl[s] * ap[j]);
+      }
+    }
+    float acc[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) h[j] = fmaf(dA[j][s], h[j], ub[j][s]);
+      acc[s] = k.cq[0][s] * h[0];
+#pragma unroll
+      for (int j = 1; j < 4; ++j) acc[s] = fmaf(k.cq[j][s], h[j], acc[s]);
+    }
+    *reinterpret_cast<f32x4*>(&part[lane * kWaveRowStride + tt]) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+  };
+  auto recurrence = [&](int len) __attribute__((always_inline)) {
+    if (len == kTB) {
+      Blk cur, nxt;
+      load_blk(cur, 0);
+#pragma unroll
+      for (int tt = 0; tt < kTB; tt += 4) {
+        if (tt + 4 < kTB) load_blk(nxt, tt + 4);
+        __builtin_amdgcn_sched_barrier(0);  // the compiler would otherwise sink the reads
+        comp_blk(cur, tt);
+        if (tt + 4 < kTB) cur = nxt;
+      }
+    } else {
+      // padding steps past len have delta = u = 0: the block's extra steps leave h unchanged
+      for (int tt = 0; tt < len; tt += 4) {
+        Blk k;
+        load_blk(k, tt);
+        comp_blk(k, tt);
+      }
+    }
+  };
+  // y of this lane's pieces: the four state quads' partial readouts, D x and the gate
+  auto epilogue = [&](int64_t t0, int len, const float (&xv)[CPL][V], const float (&zv)[CPL][V],
+                      bool full) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      if (!plive[i]) continue;
+      float yv[V];
+#pragma unroll
+      for (int e4 = 0; e4 < V; e4 += 4) {
+        f32x4 s4 = *reinterpret_cast<const f32x4*>(&part[prow[i] * kWaveRowStride + pt[i] + e4]);
+#pragma unroll
+        for (int qq = 1; qq < 4; ++qq)
+          s4 += *reinterpret_cast<const f32x4*>(&part[(16 * qq + prow[i]) * kWaveRowStride + pt[i] + e4]);
+        yv[e4] = s4.x; yv[e4 + 1] = s4.y; yv[e4 + 2] = s4.z; yv[e4 + 3] = s4.w;
+      }
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        float yy = fmaf(pD[i], xv[i][e], yv[e]);
+        if constexpr (GATE) yy *= silu_f32(zv[i][e]);
+        yv[e] = yy;
+      }
+      if (full) {
+        store_chunk<IO>(yr[i], t0 + pt[i], V, true, yv);
+      } else {
+        const int cnt = max(0, min(V, len - pt[i]));
+        if (cnt > 0) store_chunk<IO>(yr[i], t0 + pt[i], cnt, false, yv);
+      }
+    }
+  };
+
+  // progress of this wavefront in half tiles; the partner on the same SIMD is w ^ 4
+  int halves_done = 0;
+  auto pace = [&]() __attribute__((always_inline)) {
+    ++halves_done;
+    *(volatile int*)&s_prog[w] = halves_done;
+    const int other = __builtin_amdgcn_readfirstlane(*(volatile int*)&s_prog[w ^ 4]);
+    if (halves_done > other) __builtin_amdgcn_s_setprio(0);
+    else __builtin_amdgcn_s_setprio(1);
+  };
+  // a full load tile whose raw words are in cur; the next tile's are fetched into nxt first
+  auto tile_full = [&](const Raw& cur, Raw& nxt, int64_t t0, int64_t t_next) __attribute__((always_inline)) {
+    fetch(nxt, t_next);
+    __builtin_amdgcn_sched_barrier(0);  // keep every load of the next tile ahead of this one
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      prologue_full(cur, hf);
+      recurrence(kTB);
+      float xv[CPL][V], zv[CPL][V];
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        unpack16<IO>(cur.x[hf][i], xv[i]);
+        if constexpr (GATE) unpack16<IO>(cur.z[hf][i], zv[i]);
+      }
+      epilogue(t0 + hf * kTB, kTB, xv, zv, true);
+      pace();
+    }
+  };
+
+  // ---- full load tiles, two per iteration so that the two register sets alternate without
+  // copies (a copy would wait for the loads in flight). The fetch after the last tile re-reads
+  // that tile (in bounds, unused): unconditional loads keep the compiler's wait counts exact.
+  const bool fast_ok = p.vec_io != 0 && p.bc_vec != 0;
+  const int64_t n_full = fast_ok ? (t_end - t_begin) / kLT : 0;
+  if (n_full > 0) {
+    Raw ra, rb;
+    fetch(ra, t_begin);
+    for (int64_t i = 0; i < n_full; i += 2) {
+      const int64_t t0 = t_begin + i * kLT;
+      tile_full(ra, rb, t0, i + 1 < n_full ? t0 + kLT : t0);
+      if (i + 1 >= n_full) break;
+      tile_full(rb, ra, t0 + kLT, i + 2 < n_full ? t0 + 2 * kLT : t0 + kLT);
+    }
+  }
+  // ---- the rest, one half tile at a time
+  for (int64_t t0 = t_begin + n_full * kLT; t0 < t_end; t0 += kTB) {
+    const int len = (int)min<int64_t>(kTB, t_end - t0);
+    prologue_partial(t0, len);
+    recurrence(len);
+    epilogue(t0, len, xk, zk, false);
+  }
+  __builtin_amdgcn_s_setprio(0);
+  if (p.hfin && live && seg == p.nseg - 1) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (4 * q + j < p.N) p.hfin[(b * p.dim + d) * p.N + 4 * q + j] = h[j];
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // host-side launch
 
 #define SCAN_ARGS(p)                                                                         \
   static_cast<const IO*>(p.x), static_cast<const IO*>(p.delta), static_cast<const IO*>(p.B), \
       static_cast<const IO*>(p.C), static_cast<const IO*>(p.z), static_cast<IO*>(p.y), p.A,  \
       p.D, p.delta_bias, p.hend, p.dsum, p
+
+// io types that take the independent-wavefront kernel: bf16 only (with fp32 io a lane's raw
+// words of two tiles do not fit the registers)
+template <typename IO>
+struct WAVE_IO { static constexpr bool value = false; };
+template <>
+struct WAVE_IO<bf16_bits> { static constexpr bool value = true; };
 
 template <typename IO, int NS, int NW, bool HEAD, bool ZOH>
 hipError_t launch_cfg(const ScanParams& p, hipStream_t stream) {
@@ -710,6 +1080,19 @@ hipError_t launch_cfg(const ScanParams& p, hipStream_t stream) {
                        stream, SCAN_ARGS(p));
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  if constexpr (NS == 4 && WAVE_IO<IO>::value) {
+    // 8 < N <= 16: the kernel with independent wavefronts (the summary pass above stays)
+    const dim3 wgrid((unsigned)(p.batch * ((p.dim + kWaveGroupChannels - 1) / kWaveGroupChannels)),
+                     (unsigned)p.nseg);
+    const dim3 wblock(64 * kWaveGroupWaves);
+    if (p.z)
+      hipLaunchKernelGGL((scan_fwd_wave_kernel<IO, HEAD, true, ZOH>), wgrid, wblock, 0, stream,
+                         SCAN_ARGS(p));
+    else
+      hipLaunchKernelGGL((scan_fwd_wave_kernel<IO, HEAD, false, ZOH>), wgrid, wblock, 0, stream,
+                         SCAN_ARGS(p));
+    return hipGetLastError();
   }
   const dim3 grid((unsigned)groups, (unsigned)p.nseg);
   if (p.z)

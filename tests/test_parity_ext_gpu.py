@@ -71,6 +71,7 @@ ZOH_CASES = [
     (2, 256, 200, 64, 64, "head", "f32", True, True),
     (1, 128, 97, 128, 64, "head", "bf16", True, True),
     (1, 64, 4096, 16, 1, "diag", "f32", True, True),      # split along L
+    (1, 128, 190, 16, 32, "head", "bf16", True, True),
 ]
 
 
@@ -109,6 +110,7 @@ STATE_CASES = [
     (1, 130, 77, 8, 1, "diag", "bf16", True),
     (2, 128, 150, 128, 64, "head", "bf16", True),
     (1, 64, 4096, 16, 1, "diag", "bf16", True),       # split along L: h0 enters segment 0 only
+    (1, 144, 333, 13, 1, "diag", "bf16", True),
 ]
 
 

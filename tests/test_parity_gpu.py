@@ -93,6 +93,11 @@ EDGE = [
     (1, 192, 300, 32, 2, "head", "f32", True, True, True, True, 1),
     (1, 128, 2100, 8, 128, "head", "f32", False, True, False, True, 1),   # segments, head mode
     (2, 128, 40, 4, 64, "head", "bf16", True, True, True, False, 2),
+    # 8 < N <= 16 with bf16 io runs the kernel with independent wavefronts (16 channels each)
+    (2, 192, 777, 16, 32, "head", "bf16", False, True, True, True, 1),
+    (1, 200, 300, 12, 1, "diag", "bf16", True, False, True, False, 1),    # padded state quad
+    (2, 256, 130, 9, 1, "diag", "bf16", True, True, False, True, 2),      # two groups, N = 9
+    (3, 48, 64, 16, 1, "diag", "bf16", True, True, True, True, 1),        # one full tile
 ]
 
 
@@ -149,6 +154,27 @@ def test_strided_views_match_contiguous():
     _check(cfg, inputs, y_view)
     # the padding around the output view is untouched
     assert float(y_big[:, :2].abs().sum()) == 0.0 and float(y_big[:, :, :16].abs().sum()) == 0.0
+
+
+def test_unaligned_rows_match_aligned():
+    """Rows that start one element past a 16-byte boundary take the guarded element path of
+    the same kernel; the arithmetic is the same, so the result is bit-identical."""
+    cfg = ssmgen.ScanConfig(name="unaligned", batch=2, dim=80, L=203, N=16, seed=31)
+    inputs = ssmgen.make_inputs(cfg)
+    dev = device_inputs(inputs)
+    shifted = dict(dev)
+    for k in ("x", "delta", "z"):
+        t = dev[k]
+        buf = torch.zeros(t.shape[0], t.shape[1], t.shape[2] + 1, dtype=t.dtype, device="cuda")
+        buf[:, :, 1:] = t
+        shifted[k] = buf[:, :, 1:]
+    y_ref = run_hip(dev)
+    y_buf = torch.zeros(2, 80, 204, dtype=torch.bfloat16, device="cuda")
+    y_view = y_buf[:, :, 1:]
+    run_hip(shifted, out=y_view)
+    torch.cuda.synchronize()
+    assert torch.equal(y_ref, y_view)
+    _check(cfg, inputs, y_view)
 
 
 def test_run_to_run_bitwise_determinism():
