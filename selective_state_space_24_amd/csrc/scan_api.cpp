@@ -91,6 +91,11 @@ Plan plan_segments(const ssm_scan_desc* d) {
   if (groups == 0 || d->seqlen == 0) return p;
   if (waves * 4 >= kTargetWaves * 3) return p;  // enough channel groups: one pass
   int64_t want = (kTargetWaves + waves - 1) / waves;
+  // bf16 io with 8 < N <= 16 runs the kernel with independent wavefronts, one 8-wavefront
+  // workgroup per CU: segments beyond what fills the chip once would start a second round of
+  // workgroups that leaves most CUs idle, so the count is rounded down instead
+  if (d->io_dtype == SSM_DTYPE_BF16 && d->dstate > 8 && d->dstate <= 16)
+    want = kTargetWaves / waves;
   const int64_t tiles = (d->seqlen + tile - 1) / tile;
   const int64_t max_by_len = tiles / kMinSegmentTiles;
   if (want > max_by_len) want = max_by_len;
