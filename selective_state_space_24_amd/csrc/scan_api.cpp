@@ -116,7 +116,7 @@ size_t workspace_bytes_for(const ssm_scan_desc* d, const Plan& p) {
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Workspace of the backward pass: checkpoints (batch, dim, ntiles, N) every kTB steps, the dB
+// Workspace of the backward pass: checkpoints (batch, ntiles, N, dim) every kCkptStep steps, the dB
 // and dC partials
 // (batch, groups_per_batch, N, L), the dA partials (batch, dim, N), dD and dbias partials
 // (batch, dim); fp32, each section 256-byte aligned.
@@ -125,7 +125,7 @@ struct BwdLayout {
 };
 
 BwdLayout bwd_layout(const ssm_scan_desc* d) {
-  const size_t ntiles = (size_t)((d->seqlen + ssm::kTB - 1) / ssm::kTB);
+  const size_t ntiles = (size_t)((d->seqlen + ssm::kCkptStep - 1) / ssm::kCkptStep);
   const size_t gpb = (size_t)((d->dim + ssm::kChannelsPerGroup - 1) / ssm::kChannelsPerGroup);
   const size_t B = (size_t)d->batch, D = (size_t)d->dim, N = (size_t)d->dstate, L = (size_t)d->seqlen;
   BwdLayout l;
@@ -490,7 +490,7 @@ int ssm_selective_scan_bwd(const ssm_scan_desc* desc, const void* x, const void*
   p.seg_len = d.seqlen;
   p.nseg = 1;
   p.softplus = delta_softplus ? 1 : 0;
-  p.ntiles = (d.seqlen + ssm::kTB - 1) / ssm::kTB;
+  p.ntiles = (d.seqlen + ssm::kCkptStep - 1) / ssm::kCkptStep;
   char* ws = static_cast<char*>(workspace);
   p.ckpt = reinterpret_cast<float*>(ws + lay.ckpt);
   // 16-byte rows for x, delta, dy, z (the checkpoint pass and the backward prologue)

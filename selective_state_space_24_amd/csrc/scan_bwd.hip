@@ -2,12 +2,12 @@
 //
 // The pages train the layer end to end and recompute the states in the backward pass rather
 // than storing them (page "NL-345", §1 "Hardware-aware Algorithm"). Here:
-//   1. a checkpoint pass (the forward kernel without readout) stores the state at the start of
-//      every 32-step tile: N fp32 values per channel per tile;
-//   2. the backward kernel walks each channel group's tiles in reverse. A tile is processed in
-//      8-step sub-tiles, last first: the states of the tile's sub-tile starts are recomputed
-//      from the checkpoint, then each sub-tile's 8 states are recomputed into registers and
-//      the reverse recurrence runs over them:
+//   1. a checkpoint pass (the forward kernel without readout) stores the state before every
+//      8th step: N fp32 values per channel per 8 steps;
+//   2. the backward kernel walks each channel group's 32-step tiles in reverse. A tile is
+//      processed in 8-step sub-tiles, last first: a sub-tile starts from its checkpoint (read
+//      one sub-tile ahead), its 8 states are recomputed into registers and the reverse
+//      recurrence runs over them:
 //        gh += gy C;  dC += gy h;  ddelta += gh (a dA h_prev + B x);  da += gh dA h_prev delta;
 //        dB += gh delta x;  dx += gh delta B;  gh *= dA
 //      (gy = dy silu(z) is the gradient of the ungated readout). As in the forward pass, lane =
@@ -23,9 +23,10 @@
 
 namespace ssm {
 
-constexpr int kBT = kTB;            // steps per backward tile (the checkpoint interval)
+constexpr int kBT = kTB;            // steps per backward tile (one load of the per-step inputs)
 constexpr int kSub = 8;             // steps per sub-tile (their states are held in registers)
 constexpr int kSubs = kBT / kSub;   // sub-tiles per tile
+static_assert(kSub == kCkptStep, "every sub-tile starts at a checkpoint");
 constexpr int kInStride = kBT + 1;  // entries per channel row of the per-step LDS arrays
 constexpr int kRedStride = kSub + 1;
 
@@ -96,7 +97,7 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
 #pragma unroll
   for (int j = 0; j < NS; ++j) gh[j] = da[j] = 0.0f;
 
-  for (int64_t tile = p.ntiles - 1; tile >= 0; --tile) {
+  for (int64_t tile = (L + kBT - 1) / kBT - 1; tile >= 0; --tile) {
     const int64_t t0 = tile * kBT;
     const int lt_len = (int)min<int64_t>(kBT, L - t0);
 
@@ -140,30 +141,27 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
       s_B[n * kBT + t] = on ? to_f32(Bg[n * p.B_sn + t0 + t]) : 0.0f;
       s_C[n * kBT + t] = on ? to_f32(Cg[n * p.C_sn + t0 + t]) : 0.0f;
     }
-    // the state at the start of the tile
-    float h[NS];
-    {
-      const float* c = p.ckpt + ((b * p.dim + (live ? d : 0)) * p.ntiles + tile) * p.N + n0;
+    // the checkpoints of the tile's sub-tiles (channel-contiguous); the last sub-tile's is
+    // read now and each earlier one while the sub-tile after it runs. A sub-tile entirely past
+    // L has none: its steps are padding, and it starts from 0.
+    const float* ck = p.ckpt + ((b * p.ntiles + tile * kSubs) * p.N + n0) * p.dim + (live ? d : 0);
+    auto load_ck = [&](int k, float (&hv)[NS]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < NS; ++j) h[j] = (live && n0 + j < p.N) ? c[j] : 0.0f;
-    }
+      for (int j = 0; j < NS; ++j)
+        hv[j] = (live && n0 + j < p.N && t0 + k * kSub < L) ? ck[(k * p.N + j) * p.dim] : 0.0f;
+    };
+    float hnext[NS];
+    load_ck(kSubs - 1, hnext);
     __syncthreads();
 
-    // ---- sub-tiles, last first. The state at a sub-tile's start is recomputed from the tile's
-    // start each time (k * kSub steps): a few more steps than keeping every sub-tile start in
-    // registers, which would not fit beside the sub-tile's states.
+    // ---- sub-tiles, last first
 #pragma unroll 1
     for (int k = kSubs - 1; k >= 0; --k) {
       const int tb = k * kSub;
       float hsk[NS];
 #pragma unroll
-      for (int j = 0; j < NS; ++j) hsk[j] = h[j];
-      for (int t = 0; t < tb; ++t) {
-        const f32x4 in = s_in[lane * kInStride + t];
-#pragma unroll
-        for (int j = 0; j < NS; ++j)
-          hsk[j] = fmaf(__builtin_amdgcn_exp2f(in.x * ap[j]), hsk[j], in.y * s_B[(n0 + j) * kBT + t]);
-      }
+      for (int j = 0; j < NS; ++j) hsk[j] = hnext[j];
+      if (k > 0) load_ck(k - 1, hnext);
       // recompute the sub-tile's states (after each step) and the readout partials
       float hh[kSub][NS];
       float yp[kSub];

@@ -12,6 +12,7 @@ constexpr int kWavesPerGroup = 4;
 constexpr int kTB = 32;       // time steps per compute tile
 constexpr int kLT = 2 * kTB;  // time steps per load tile (128 bytes of bf16 per row); segments
                               // along L start at multiples of it
+constexpr int kCkptStep = 8;  // steps between the states the backward checkpoint pass stores
 
 struct ScanParams {
   // inputs / outputs (device pointers); element type is the io dtype unless noted
@@ -26,9 +27,9 @@ struct ScanParams {
   void* y;
   const float* h0;          // nullable: initial state (batch, dim, N) fp32
   float* hfin;              // nullable: final state (batch, dim, N) fp32
-  float* ckpt;              // backward checkpoints: the state before every kTB-th step,
-                            // ckpt[((b * dim + d) * ntiles + tile) * N + n]
-  int64_t ntiles;           // ceil(L / kTB) (checkpoint pass)
+  float* ckpt;              // backward checkpoints: the state before every kCkptStep-th step,
+                            // ckpt[((b * ntiles + k) * N + n) * dim + d] (channel-contiguous)
+  int64_t ntiles;           // ceil(L / kCkptStep), the number of checkpoints per channel
   // per-segment summaries for sequences split along L (nullable when nseg == 1):
   // hend[((b * dim + d) * nseg + s) * N + n] and dsum[(b * dim + d) * nseg + s]
   float* hend;

@@ -177,8 +177,8 @@ __device__ __forceinline__ float zoh_ratio(float dA, float w) {
 //
 // HEAD: one A and one delta per head; SUMMARY: the segment summary pass (no readout, no y);
 // GATE: y is multiplied by silu(z); ZOH: zero-order-hold B discretisation (else delta * B);
-// CKPT: the checkpoint pass of the backward pass (no readout, no y; the state at the start of
-// every kTB-step half tile is stored).
+// CKPT: the checkpoint pass of the backward pass (no readout, no y; the state before every
+// kCkptStep-th step is stored).
 template <typename IO, int NS, int NW, bool HEAD, bool SUMMARY, bool GATE, bool ZOH,
           bool CKPT = false>
 // At most two workgroups fit a CU's LDS (one once the B/C tile holds more than 16 states), so
@@ -621,14 +621,15 @@ __global__ void __launch_bounds__(64 * NW, NS <= 4 ? 2 : 1)
     }
   };
 
-  // the checkpoint pass stores the state before step t (t a multiple of kTB)
+  // the checkpoint pass stores the state before step t (t a multiple of kCkptStep), channel-
+  // contiguous: the lanes of a wavefront store 256 consecutive bytes per state
   auto store_ckpt = [&](int64_t t) __attribute__((always_inline)) {
     if constexpr (CKPT) {
       if (live) {
-        float* c = p.ckpt + ((b * p.dim + d) * p.ntiles + (t - t_begin) / kTB) * p.N + n0;
+        float* c = p.ckpt + ((b * p.ntiles + (t - t_begin) / kCkptStep) * p.N + n0) * p.dim + d;
 #pragma unroll
         for (int j = 0; j < NS; ++j)
-          if (n0 + j < p.N) c[j] = h[j];
+          if (n0 + j < p.N) c[j * p.dim] = h[j];
       }
     }
   };
@@ -640,8 +641,15 @@ __global__ void __launch_bounds__(64 * NW, NS <= 4 ? 2 : 1)
       const int h0 = hf * kTB;
       if (h0 >= lt_len) break;
       const int tb_len = min(kTB, lt_len - h0);
-      if constexpr (CKPT) store_ckpt(t0 + h0);
-      recurrence(h0, tb_len);
+      if constexpr (CKPT) {
+        static_assert(kCkptStep == 8 && kTB % kCkptStep == 0, "checkpoint blocks are step8 blocks");
+        for (int tt = 0; tt < tb_len; tt += kCkptStep) {
+          store_ckpt(t0 + h0 + tt);
+          step8(h0, tt);
+        }
+      } else {
+        recurrence(h0, tb_len);
+      }
       if constexpr (!NOREAD) {
         __syncthreads();  // partial readouts complete
         epilogue(hf, t0, tb_len, full);
