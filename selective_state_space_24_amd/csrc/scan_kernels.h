@@ -1,7 +1,12 @@
 // gfx950 kernels of the selective-scan forward pass.
 //
-// Work decomposition: one workgroup = 64 channels of one batch entry x one segment of L, in NW
-// wavefronts.
+// Two kernels. scan_fwd_wave_kernel (further down) serves bf16 io with 8 < N <= 16: every
+// wavefront owns 16 channels x all states and runs without workgroup barriers. scan_fwd_kernel,
+// described here, serves every other case (fp32 io, N <= 8 or N > 16) and also runs the segment
+// summaries and the backward pass's checkpoints.
+//
+// Work decomposition of scan_fwd_kernel: one workgroup = 64 channels of one batch entry x one
+// segment of L, in NW wavefronts.
 //   * lane l of every wavefront owns channel d0 + l; wavefront w owns states [w*NS, (w+1)*NS).
 //     The state h (NS fp32 values per lane) lives in VGPRs for the whole segment and is never
 //     written to memory (the pages' hardware-aware scan keeps the expanded state on chip).
@@ -1074,9 +1079,9 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
 // io types that take the independent-wavefront kernel: bf16 only (with fp32 io a lane's raw
 // words of two tiles do not fit the registers)
 template <typename IO>
-struct WAVE_IO { static constexpr bool value = false; };
+struct WaveIo { static constexpr bool value = false; };
 template <>
-struct WAVE_IO<bf16_bits> { static constexpr bool value = true; };
+struct WaveIo<bf16_bits> { static constexpr bool value = true; };
 
 template <typename IO, int NS, int NW, bool HEAD, bool ZOH>
 hipError_t launch_cfg(const ScanParams& p, hipStream_t stream) {
@@ -1089,7 +1094,7 @@ hipError_t launch_cfg(const ScanParams& p, hipStream_t stream) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if constexpr (NS == 4 && WAVE_IO<IO>::value) {
+  if constexpr (NS == 4 && WaveIo<IO>::value) {
     // 8 < N <= 16: the kernel with independent wavefronts (the summary pass above stays)
     const dim3 wgrid((unsigned)(p.batch * ((p.dim + kWaveGroupChannels - 1) / kWaveGroupChannels)),
                      (unsigned)p.nseg);
