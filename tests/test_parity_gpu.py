@@ -177,6 +177,28 @@ def test_unaligned_rows_match_aligned():
     _check(cfg, inputs, y_view)
 
 
+@pytest.mark.parametrize("shape", [(2, 200, 333, 16, 1, "diag"), (1, 128, 320, 12, 1, "diag"),
+                                   (2, 192, 150, 16, 32, "head")],
+                         ids=lambda s: "-".join(map(str, s)))
+def test_bf16_path_equals_f32_path_rounded(shape):
+    """bf16 io with 8 < N <= 16 runs the kernel with independent wavefronts; fp32 io runs the
+    barrier-synchronised kernel. Both compute in fp32 with the same operations in the same
+    order, so on the same (bf16-representable) inputs the fp32 result rounded to bf16 equals
+    the bf16 result bit for bit. Short sequences keep both in one segment."""
+    import torch
+    batch, dim, L, N, hd, mode = shape
+    cfg = ssmgen.ScanConfig(name="paths", batch=batch, dim=dim, L=L, N=N, headdim=hd, a_mode=mode,
+                            io="bf16", seed=4242 + dim)
+    _say(f"[paths] {shape}")
+    dev = device_inputs(ssmgen.make_inputs(cfg))
+    y16 = run_hip(dev)
+    dev32 = {k: (v.float() if v.dtype == torch.bfloat16 else v) for k, v in dev.items()}
+    y32 = run_hip(dev32)
+    torch.cuda.synchronize()
+    assert y16.dtype == torch.bfloat16 and y32.dtype == torch.float32
+    assert torch.equal(y32.to(torch.bfloat16), y16)
+
+
 def test_run_to_run_bitwise_determinism():
     cfg = ssmgen.CONFIGS[1]
     dev = device_inputs(ssmgen.make_inputs(cfg))
