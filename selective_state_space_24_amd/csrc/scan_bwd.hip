@@ -357,13 +357,22 @@ template <typename IO, int NS>
 static hipError_t bwd_cfg(const BwdParams& q, hipStream_t stream) {
   const ScanParams& p = q.f;
   const int64_t groups = p.batch * p.groups_per_batch;
-  // 1. checkpoints
-  hipLaunchKernelGGL((scan_fwd_kernel<IO, NS, kWavesPerGroup, false, false, false, false, true>),
-                     dim3((unsigned)groups, 1), dim3(64 * kWavesPerGroup), 0, stream,
-                     static_cast<const IO*>(p.x), static_cast<const IO*>(p.delta),
-                     static_cast<const IO*>(p.B), static_cast<const IO*>(p.C),
-                     static_cast<const IO*>(nullptr), static_cast<IO*>(nullptr), p.A, p.D,
-                     p.delta_bias, nullptr, nullptr, p);
+  // 1. checkpoints (bf16 io with 8 < N <= 16: the kernel with independent wavefronts)
+  if constexpr (NS == 4 && WaveIo<IO>::value) {
+    const unsigned wg = (unsigned)(p.batch * ((p.dim + kWaveGroupChannels - 1) / kWaveGroupChannels));
+    hipLaunchKernelGGL((scan_fwd_wave_kernel<IO, false, false, false, kWaveCkpt>), dim3(wg, 1),
+                       dim3(64 * kWaveGroupWaves), 0, stream, static_cast<const IO*>(p.x),
+                       static_cast<const IO*>(p.delta), static_cast<const IO*>(p.B),
+                       static_cast<const IO*>(p.C), static_cast<const IO*>(nullptr),
+                       static_cast<IO*>(nullptr), p.A, p.D, p.delta_bias, nullptr, nullptr, p);
+  } else {
+    hipLaunchKernelGGL((scan_fwd_kernel<IO, NS, kWavesPerGroup, false, false, false, false, true>),
+                       dim3((unsigned)groups, 1), dim3(64 * kWavesPerGroup), 0, stream,
+                       static_cast<const IO*>(p.x), static_cast<const IO*>(p.delta),
+                       static_cast<const IO*>(p.B), static_cast<const IO*>(p.C),
+                       static_cast<const IO*>(nullptr), static_cast<IO*>(nullptr), p.A, p.D,
+                       p.delta_bias, nullptr, nullptr, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // 2. the reverse pass

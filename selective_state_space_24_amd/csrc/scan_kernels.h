@@ -725,14 +725,24 @@ constexpr int kWaveGroupChannels = kWaveChannels * kWaveGroupWaves;
 constexpr int kWaveDuStride = 2 * kTB + 4;  // floats per channel row of (delta, u)
 constexpr int kWaveRowStride = kTB + 4;     // floats per state row of B / C, per lane row of partials
 
-template <typename IO, bool HEAD, bool GATE, bool ZOH>
+// MODE: kWaveOut computes y; kWaveSummary is the segment summary pass (the state at the
+// segment's end from a zero start, and the segment's sum of delta); kWaveCkpt is the backward
+// pass's checkpoint pass (the state before every kCkptStep-th step). The last two have no
+// readout and no y.
+constexpr int kWaveOut = 0, kWaveSummary = 1, kWaveCkpt = 2;
+
+template <typename IO, bool HEAD, bool GATE, bool ZOH, int MODE = kWaveOut>
 __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
     scan_fwd_wave_kernel(const IO* __restrict__ X, const IO* __restrict__ DL,
                          const IO* __restrict__ Bm, const IO* __restrict__ Cm,
                          const IO* __restrict__ Z, IO* __restrict__ Y, const float* __restrict__ Am,
                          const float* __restrict__ Dm, const float* __restrict__ bias_p,
-                         const float* __restrict__ hend, const float* __restrict__ dsum,
+                         float* __restrict__ hend, float* __restrict__ dsum,
                          const ScanParams p) {
+  constexpr bool NOREAD = MODE != kWaveOut;
+  static_assert(!(NOREAD && GATE), "the summary and checkpoint passes have no gate");
+  static_assert(MODE != kWaveCkpt || (kCkptStep == 8 && kTB % kCkptStep == 0),
+                "checkpoints fall on every other 4-step block");
   constexpr int V = IoTraits<IO>::kVec;
   constexpr int PPR = kTB / V;                  // 16-byte pieces per row of a half tile
   constexpr int CPL = kWaveChannels * PPR / 64;  // pieces per lane per half (x, delta, z, y, B, C)
@@ -778,12 +788,13 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
       ap[j] = (live && 4 * q + j < p.N) ? Am[d * p.N + 4 * q + j] * kLog2e : 0.0f;
   }
   float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (p.h0 && live) {
+  double dsum_total = 0.0;  // summary pass: the segment's sum of delta
+  if (MODE != kWaveSummary && p.h0 && live) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       if (4 * q + j < p.N) h[j] = p.h0[(b * p.dim + d) * p.N + 4 * q + j];
   }
-  if (seg > 0 && live) {
+  if (MODE == kWaveOut && seg > 0 && live) {
     // compose the summaries of segments 0 .. seg-1: h <- exp(A * sum delta) h + h_end
     const int64_t base = (b * p.dim + d) * p.nseg;
     for (int s = 0; s < seg; ++s) {
@@ -842,7 +853,7 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
         r.d[hf][i] = load16<true>(dr[i] + t0 + hf * kTB + pt[i]);
         if constexpr (GATE) r.z[hf][i] = load16<true>(zr[i] + t0 + hf * kTB + pt[i]);
         r.b[hf][i] = load16<false>(br[i] + t0 + hf * kTB + pt[i]);
-        r.c[hf][i] = load16<false>(cr[i] + t0 + hf * kTB + pt[i]);
+        if constexpr (!NOREAD) r.c[hf][i] = load16<false>(cr[i] + t0 + hf * kTB + pt[i]);
       }
     }
   };
@@ -870,7 +881,8 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
 #pragma unroll
     for (int k = 0; k < V / 4; ++k) {
       db[k] = f32x4{bv[4 * k], bv[4 * k + 1], bv[4 * k + 2], bv[4 * k + 3]} * m;
-      dc[k] = f32x4{cv[4 * k], cv[4 * k + 1], cv[4 * k + 2], cv[4 * k + 3]} * m;
+      if constexpr (!NOREAD)
+        dc[k] = f32x4{cv[4 * k], cv[4 * k + 1], cv[4 * k + 2], cv[4 * k + 3]} * m;
     }
   };
   auto prologue_full = [&](const Raw& r, int hf) __attribute__((always_inline)) {
@@ -880,7 +892,7 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
       unpack16<IO>(r.x[hf][i], xv);
       unpack16<IO>(r.d[hf][i], dv);
       unpack16<IO>(r.b[hf][i], bv);
-      unpack16<IO>(r.c[hf][i], cv);
+      if constexpr (!NOREAD) unpack16<IO>(r.c[hf][i], cv);
       put_du(i, xv, dv);
       put_bc(i, bv, cv);
     }
@@ -898,7 +910,8 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
       load_chunk<IO, true>(dr[i], t0 + pt[i], ccnt, false, dv);
       if constexpr (GATE) load_chunk<IO, true>(zr[i], t0 + pt[i], ccnt, false, zk[i]);
       load_chunk<IO, false>(br[i], t0 + pt[i], bvalid[i] ? cnt : 0, false, bv);
-      load_chunk<IO, false>(cr[i], t0 + pt[i], bvalid[i] ? cnt : 0, false, cv);
+      if constexpr (!NOREAD)
+        load_chunk<IO, false>(cr[i], t0 + pt[i], bvalid[i] ? cnt : 0, false, cv);
       put_du(i, xk[i], dv);
       if (cnt < V) {
         float* row = &du[prow[i] * kWaveDuStride + 2 * pt[i]];
@@ -922,7 +935,8 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       k.bq[j] = *reinterpret_cast<const f32x4*>(&sB[(4 * q + j) * kWaveRowStride + tt]);
-      k.cq[j] = *reinterpret_cast<const f32x4*>(&sC[(4 * q + j) * kWaveRowStride + tt]);
+      if constexpr (!NOREAD)
+        k.cq[j] = *reinterpret_cast<const f32x4*>(&sC[(4 * q + j) * kWaveRowStride + tt]);
     }
   };
   auto comp_blk = [&](const Blk& k, int tt) __attribute__((always_inline)) {
@@ -949,18 +963,43 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
         if constexpr (ZOH) ub[j][s] *= HEAD ? gh[s] : zoh_ratio(dA[j][s], dl[s] * ap[j]);
       }
     }
-    float acc[4];
+    if constexpr (NOREAD) {
+      if constexpr (MODE == kWaveSummary) dsum_total += (double)((dl[0] + dl[1]) + (dl[2] + dl[3]));
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) h[j] = fmaf(dA[j][s], h[j], ub[j][s]);
-      acc[s] = k.cq[0][s] * h[0];
+        for (int j = 0; j < 4; ++j) h[j] = fmaf(dA[j][s], h[j], ub[j][s]);
+      // the state goes to the (otherwise unused) partial row: without a store in every block the
+      // compiler's schedule of these passes spills most of the registers
+      *reinterpret_cast<f32x4*>(&part[lane * kWaveRowStride + tt]) = f32x4{h[0], h[1], h[2], h[3]};
+    } else {
+      float acc[4];
 #pragma unroll
-      for (int j = 1; j < 4; ++j) acc[s] = fmaf(k.cq[j][s], h[j], acc[s]);
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) h[j] = fmaf(dA[j][s], h[j], ub[j][s]);
+        acc[s] = k.cq[0][s] * h[0];
+#pragma unroll
+        for (int j = 1; j < 4; ++j) acc[s] = fmaf(k.cq[j][s], h[j], acc[s]);
+      }
+      *reinterpret_cast<f32x4*>(&part[lane * kWaveRowStride + tt]) = f32x4{acc[0], acc[1], acc[2], acc[3]};
     }
-    *reinterpret_cast<f32x4*>(&part[lane * kWaveRowStride + tt]) = f32x4{acc[0], acc[1], acc[2], acc[3]};
   };
-  auto recurrence = [&](int len) __attribute__((always_inline)) {
+  // checkpoint pass: the state before step t (t - t_begin a multiple of kCkptStep), channel-
+  // contiguous as the backward pass reads it
+  float* const ck_lane =
+      MODE == kWaveCkpt ? p.ckpt + (b * p.ntiles * p.N + 4 * q) * p.dim + min(d, p.dim - 1) : nullptr;
+  auto store_ckpt = [&](int64_t t) __attribute__((always_inline)) {
+    if constexpr (MODE == kWaveCkpt) {
+      if (live) {
+        float* cp = ck_lane + (t - t_begin) / kCkptStep * (p.N * p.dim);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (4 * q + j < p.N) cp[j * p.dim] = h[j];
+      }
+    }
+  };
+  auto recurrence = [&](int64_t th, int len) __attribute__((always_inline)) {
     if (len == kTB) {
       Blk cur, nxt;
       load_blk(cur, 0);
@@ -968,6 +1007,7 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
       for (int tt = 0; tt < kTB; tt += 4) {
         if (tt + 4 < kTB) load_blk(nxt, tt + 4);
         __builtin_amdgcn_sched_barrier(0);  // the compiler would otherwise sink the reads
+        if (tt % kCkptStep == 0) store_ckpt(th + tt);
         comp_blk(cur, tt);
         if (tt + 4 < kTB) cur = nxt;
       }
@@ -976,6 +1016,7 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
       for (int tt = 0; tt < len; tt += 4) {
         Blk k;
         load_blk(k, tt);
+        if (tt % kCkptStep == 0) store_ckpt(th + tt);
         comp_blk(k, tt);
       }
     }
@@ -1026,14 +1067,16 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       prologue_full(cur, hf);
-      recurrence(kTB);
-      float xv[CPL][V], zv[CPL][V];
+      recurrence(t0 + hf * kTB, kTB);
+      if constexpr (!NOREAD) {
+        float xv[CPL][V], zv[CPL][V];
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        unpack16<IO>(cur.x[hf][i], xv[i]);
-        if constexpr (GATE) unpack16<IO>(cur.z[hf][i], zv[i]);
+        for (int i = 0; i < CPL; ++i) {
+          unpack16<IO>(cur.x[hf][i], xv[i]);
+          if constexpr (GATE) unpack16<IO>(cur.z[hf][i], zv[i]);
+        }
+        epilogue(t0 + hf * kTB, kTB, xv, zv, true);
       }
-      epilogue(t0 + hf * kTB, kTB, xv, zv, true);
       pace();
     }
   };
@@ -1057,10 +1100,20 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
   for (int64_t t0 = t_begin + n_full * kLT; t0 < t_end; t0 += kTB) {
     const int len = (int)min<int64_t>(kTB, t_end - t0);
     prologue_partial(t0, len);
-    recurrence(len);
-    epilogue(t0, len, xk, zk, false);
+    recurrence(t0, len);
+    if constexpr (!NOREAD) epilogue(t0, len, xk, zk, false);
   }
   __builtin_amdgcn_s_setprio(0);
+  if constexpr (MODE == kWaveSummary) {
+    if (live) {
+      const int64_t base = (b * p.dim + d) * p.nseg + seg;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (4 * q + j < p.N) hend[base * p.N + 4 * q + j] = h[j];
+      if (q == 0) dsum[base] = (float)dsum_total;
+    }
+  }
+  if constexpr (NOREAD) return;
   if (p.hfin && live && seg == p.nseg - 1) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -1087,18 +1140,24 @@ template <typename IO, int NS, int NW, bool HEAD, bool ZOH>
 hipError_t launch_cfg(const ScanParams& p, hipStream_t stream) {
   const dim3 block(64 * NW);
   const int64_t groups = p.batch * p.groups_per_batch;
-  if (p.nseg > 1) {
-    const dim3 grid_sum((unsigned)groups, (unsigned)(p.nseg - 1));
-    hipLaunchKernelGGL((scan_fwd_kernel<IO, NS, NW, HEAD, true, false, ZOH>), grid_sum, block, 0,
-                       stream, SCAN_ARGS(p));
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   if constexpr (NS == 4 && WaveIo<IO>::value) {
-    // 8 < N <= 16: the kernel with independent wavefronts (the summary pass above stays)
-    const dim3 wgrid((unsigned)(p.batch * ((p.dim + kWaveGroupChannels - 1) / kWaveGroupChannels)),
-                     (unsigned)p.nseg);
+    // 8 < N <= 16: the kernel with independent wavefronts for the output. The summaries take it
+    // too when they fill about three quarters of the chip (1536 wavefronts, 192 CUs); fewer
+    // summary workgroups run faster spread over more CUs in the four-wavefront form.
+    const unsigned wg = (unsigned)(p.batch * ((p.dim + kWaveGroupChannels - 1) / kWaveGroupChannels));
     const dim3 wblock(64 * kWaveGroupWaves);
+    if (p.nseg > 1) {
+      if ((int64_t)wg * (p.nseg - 1) * kWaveGroupWaves >= 1536)
+        hipLaunchKernelGGL((scan_fwd_wave_kernel<IO, HEAD, false, ZOH, kWaveSummary>),
+                           dim3(wg, (unsigned)(p.nseg - 1)), wblock, 0, stream, SCAN_ARGS(p));
+      else
+        hipLaunchKernelGGL((scan_fwd_kernel<IO, NS, NW, HEAD, true, false, ZOH>),
+                           dim3((unsigned)groups, (unsigned)(p.nseg - 1)), block, 0, stream,
+                           SCAN_ARGS(p));
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    const dim3 wgrid(wg, (unsigned)p.nseg);
     if (p.z)
       hipLaunchKernelGGL((scan_fwd_wave_kernel<IO, HEAD, true, ZOH>), wgrid, wblock, 0, stream,
                          SCAN_ARGS(p));
@@ -1106,6 +1165,13 @@ hipError_t launch_cfg(const ScanParams& p, hipStream_t stream) {
       hipLaunchKernelGGL((scan_fwd_wave_kernel<IO, HEAD, false, ZOH>), wgrid, wblock, 0, stream,
                          SCAN_ARGS(p));
     return hipGetLastError();
+  }
+  if (p.nseg > 1) {
+    const dim3 grid_sum((unsigned)groups, (unsigned)(p.nseg - 1));
+    hipLaunchKernelGGL((scan_fwd_kernel<IO, NS, NW, HEAD, true, false, ZOH>), grid_sum, block, 0,
+                       stream, SCAN_ARGS(p));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
   const dim3 grid((unsigned)groups, (unsigned)p.nseg);
   if (p.z)
