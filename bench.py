@@ -80,21 +80,28 @@ def device_inputs(cfg, torch):
     return dev
 
 
+VALU_CYCLES = 4   # SIMD cycles per wavefront-wide unpacked fp32 instruction
+TRANS_CYCLES = 8  # per wavefront-wide exp2 / log2 / rcp
+
+
 def alu_model(cfg):
     """Minimal fp32 instruction stream of the method per token*channel: (flops, SIMD cycles).
 
-    A wavefront-wide (64-lane) fp32 add/mul/fma/max issues every 2 cycles on a SIMD (the
-    157.3 TFLOP/s vector rate: 256 CUs x 4 SIMDs x 64 lanes x 2 flops / 2 cycles x 2.4 GHz);
-    exp2, log2 and rcp issue at quarter rate, every 8 cycles. Flops count an fma as 2 and every
-    other operation, transcendentals included, as 1.
-      per state update (t, channel, n): delta*a, exp2, u*B, h fma, readout fma -> 7 flops, 16 cyc
+    Issue costs of a wavefront-wide (64-lane) instruction on one SIMD: an unpacked fp32
+    add/mul/fma/max takes 4 cycles (16 lanes per cycle, the rate of the 78.6 TFLOP/s vector
+    figure: 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz; the 157.3 TFLOP/s fp32 figure
+    needs the packed two-wide fp32 instructions, which this library's build switches off);
+    exp2, log2 and rcp take 8 cycles. The profiler's VALU-busy counter charges exactly these
+    costs (1 and 2 four-cycle units per instruction). Flops count an fma as 2 and every other
+    operation, transcendentals included, as 1.
+      per state update (t, channel, n): delta*a, exp2, u*B, h fma, readout fma -> 7 flops, 24 cyc
         (head mode: delta*a and exp2 once per (t, head) instead)
-      per (t, channel): bias add (1, 2), softplus (10, 30: |v|*log2e, exp2, 1+e, log2, two
-        subtractions of the log1p correction, fma, max, add), u = delta*x (1, 2), D skip fma
-        (2, 2), silu gate (6, 24: z*log2e, exp2, 1+e, rcp, z*r, y*g)
+      per (t, channel): bias add (1, 4), softplus (10, 44: |v|*log2e, exp2, 1+e, log2, two
+        subtractions of the log1p correction, fma, max, add), u = delta*x (1, 4), D skip fma
+        (2, 4), silu gate (6, 32: z*log2e, exp2, 1+e, rcp, z*r, y*g)
     Unpacking and packing of bf16 are not counted (they are not arithmetic of the method).
     """
-    valu, trans = 2, 8
+    valu, trans = VALU_CYCLES, TRANS_CYCLES
     head = cfg.a_mode == "head"
     rows_per_ch = 1.0 / cfg.headdim if head else 1.0
     fl = cy = 0.0
@@ -163,15 +170,15 @@ def cpu_baseline(cfg, budget_s: float):
 def alu_model_bwd(cfg):
     """Minimal fp32 instruction stream of the gradient per token*channel: (flops, SIMD cycles),
     costs as in ``alu_model`` (diagonal A, delta * B rule).
-      per state update: the states recomputed once (delta*a, exp2, u*B, fma: 5 flops, 14 cyc)
+      per state update: the states recomputed once (delta*a, exp2, u*B, fma: 5 flops, 20 cyc)
         and the reverse step (gh += gy C; gy h for dC; exp2; h_prev dA; a h_prev dA + B x;
         ddelta += gh (.); da += gh h_prev dA delta; gh u for dB; dx += gh delta B; gh *= dA:
-        18 flops, 12 plain ops + 1 transcendental = 32 cyc)
-      per (t, channel): softplus and its derivative sigmoid (14 flops, 44 cyc), u = delta*x,
-        the gate silu and silu' (12 flops, 34 cyc), y = readout + D x and dz (3 flops, 4 cyc),
-        dx += gy D, dD += gy x, dbias += (4 fma/add: 7 flops, 8 cyc)
+        18 flops, 12 plain ops + 1 transcendental = 56 cyc)
+      per (t, channel): softplus and its derivative sigmoid (14 flops, 64 cyc), u = delta*x,
+        the gate silu and silu' (12 flops, 52 cyc), y = readout + D x and dz (3 flops, 8 cyc),
+        dx += gy D, dD += gy x, dbias += (4 fma/add: 7 flops, 16 cyc)
     The sums over lanes for dB and dC and over the batch are not counted."""
-    valu, trans = 2, 8
+    valu, trans = VALU_CYCLES, TRANS_CYCLES
     fl = cfg.N * (5 + 18)
     cy = cfg.N * ((3 * valu + trans) + (12 * valu + trans))
     if cfg.softplus:
