@@ -106,3 +106,45 @@ def test_backward_is_deterministic():
     b = _run(cfg, inputs, dy)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+
+
+def test_backward_full_size_bench_workload():
+    """The Mamba-1.4B layer (batch 8, d_inner 4096, N 16, L 4096, bf16) at full size, in the
+    launch configuration that bench.py --workload bwd times. The oracle runs one batch entry at a
+    time: dx, ddelta, dz, dB and dC of the first and last entries are compared whole, and dA, dD
+    and dbias (sums over the batch) against the sum of all eight entries' oracle gradients."""
+    import selective_state_space_24_amd as ssm
+    cfg = ssmgen.CONFIGS[2]
+    _say(f"[bwd] config 2 {cfg.name}: generating inputs")
+    dev = {}
+    for name in cfg.shapes():
+        dev.update(device_inputs({name: ssmgen.make_tensor(cfg, name)}))
+    dy = _dy(cfg, 2)
+    dyd = to_torch(dy, dy.dtype == np.uint16, "cuda")
+    _say("[bwd] config 2: running")
+    g = ssm.selective_scan_bwd(dev["x"], dev["delta"], dev["A"], dev["B"], dev["C"], dev["D"],
+                               dev["z"], dev["delta_bias"], cfg.softplus, dyd)
+    torch.cuda.synchronize()
+    del dev, dyd
+    summed = {"dA": None, "dD": None, "ddelta_bias": None}
+    one = ssmgen.with_shape(cfg, batch=1)
+    worst = {}
+    for b in range(cfg.batch):
+        ref = oracle.scan_inputs_bwd(ssmgen.make_batch_entry(cfg, b), dy[b:b + 1], one)
+        for k in summed:
+            summed[k] = ref[k] if summed[k] is None else summed[k] + ref[k]
+        if b in (0, cfg.batch - 1):
+            for k in ("dx", "ddelta", "dz", "dB", "dC"):
+                got = y_to_f64(g[k][b:b + 1])
+                assert np.isfinite(got).all(), (k, b)
+                err = oracle.rel_err(got, ref[k])
+                worst[k] = max(worst.get(k, 0.0), err)
+                assert err <= TOL[cfg.io], f"{k} of batch entry {b}: rel err {err:.3e}"
+        del ref
+    for k, v in summed.items():
+        err = oracle.rel_err(y_to_f64(g[k]), v)
+        worst[k] = err
+        assert err <= TOL[cfg.io], f"{k}: rel err {err:.3e}"
+    _say(f"[bwd] config 2 errors {', '.join(f'{k} {e:.2e}' for k, e in worst.items())}")
+    del g
+    torch.cuda.empty_cache()
