@@ -101,3 +101,22 @@ def test_step_loop_equals_scan(io, mode, N, hd):
     assert oracle.rel_err(y_steps, y_to_f64(y_scan)) <= TOL[io]
     assert oracle.rel_err(state.cpu().numpy().astype(np.float64),
                           h_scan.cpu().numpy().astype(np.float64)) <= STATE_TOL
+
+
+@pytest.mark.parametrize("key", ["mamba14b_decode", "heads_decode"])
+def test_decode_full_size(key):
+    """The decode workloads at full size (bench.py --workload decode times the first): one step
+    from a seeded N(0, 1) state, y and the whole updated state against the oracle."""
+    cfg = ssmgen.DECODE_CONFIGS[key]
+    _say(f"[decode] {cfg.name}")
+    inputs = ssmgen.make_inputs(cfg)
+    h0 = np.random.default_rng(7).standard_normal((cfg.batch, cfg.dim, cfg.N)).astype(np.float32)
+    dev = device_inputs(inputs)
+    state = torch.from_numpy(h0).cuda()
+    y = _step(dev, 0, state, cfg)
+    torch.cuda.synchronize()
+    yref, href = oracle.scan_inputs(inputs, cfg, h0=h0.astype(np.float64), return_final_state=True)
+    ey = oracle.rel_err(y_to_f64(y), yref[..., 0])
+    eh = oracle.rel_err(state.cpu().numpy().astype(np.float64), href)
+    _say(f"[decode] {key}: y rel err {ey:.2e}, state rel err {eh:.2e}")
+    assert ey <= TOL[cfg.io] and eh <= STATE_TOL
