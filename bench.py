@@ -171,16 +171,17 @@ def alu_model_bwd(cfg):
     """Minimal fp32 instruction stream of the gradient per token*channel: (flops, SIMD cycles),
     costs as in ``alu_model`` (diagonal A, delta * B rule).
       per state update: the states recomputed once (delta*a, exp2, u*B, fma: 5 flops, 20 cyc)
-        and the reverse step (gh += gy C; gy h for dC; exp2; h_prev dA; a h_prev dA + B x;
-        ddelta += gh (.); da += gh h_prev dA delta; gh u for dB; dx += gh delta B; gh *= dA:
-        18 flops, 12 plain ops + 1 transcendental = 56 cyc)
+        and the reverse step (gh += gy C; gy h for dC; exp2 of delta*a; g = gh (h_prev dA);
+        ddelta part += g a; da += g delta; gh u for dB; sb += gh B; gh *= dA: 15 flops,
+        10 plain ops + 1 transcendental = 48 cyc)
       per (t, channel): softplus and its derivative sigmoid (14 flops, 64 cyc), u = delta*x,
         the gate silu and silu' (12 flops, 52 cyc), y = readout + D x and dz (3 flops, 8 cyc),
-        dx += gy D, dD += gy x, dbias += (4 fma/add: 7 flops, 16 cyc)
+        dx += gy D, dD += gy x, dbias += (4 fma/add: 7 flops, 16 cyc), and the two state sums
+        ddelta part += x sb, dx part = delta sb (3 flops, 8 cyc)
     The sums over lanes for dB and dC and over the batch are not counted."""
     valu, trans = VALU_CYCLES, TRANS_CYCLES
-    fl = cfg.N * (5 + 18)
-    cy = cfg.N * ((3 * valu + trans) + (12 * valu + trans))
+    fl = cfg.N * (5 + 15) + 3
+    cy = cfg.N * ((3 * valu + trans) + (10 * valu + trans)) + 2 * valu
     if cfg.softplus:
         fl += 14
         cy += 10 * valu + 3 * trans

@@ -197,7 +197,9 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
           const int t = tb + i;
           const f32x4 in = s_in[lane * kInStride + t];
           const float dl = in.x, u = in.y, gy = in.z, xx = in.w;
-          float gd = 0.0f, gx = 0.0f;
+          // ddelta and dx need sum_j gh_j (h_prev,j dA_j a_j + B_j x) and sum_j gh_j delta B_j:
+          // both are taken as sum_j gh_j h_prev,j dA_j a_j plus x and delta times sum_j gh_j B_j
+          float gd = 0.0f, sb = 0.0f;
 #pragma unroll
           for (int j = 0; j < NS; ++j) {
             const float Bv = s_B[(n0 + j) * kBT + t];
@@ -206,15 +208,15 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
             red[j * RS + e] = gy * hh[i][j];                       // dC
             const float dA = __builtin_amdgcn_exp2f(dl * ap[j]);
             const float hp = i == 0 ? hsk[j] : hh[i - 1][j];
-            const float tmp = hp * dA;
-            gd = fmaf(gh[j], fmaf(tmp, an[j], Bv * xx), gd);
-            da[j] = fmaf(gh[j] * tmp, dl, da[j]);
+            const float gt = gh[j] * (hp * dA);
+            gd = fmaf(gt, an[j], gd);
+            da[j] = fmaf(gt, dl, da[j]);
             red[RS * NS + j * RS + e] = gh[j] * u;                 // dB
-            gx = fmaf(gh[j], dl * Bv, gx);
+            sb = fmaf(gh[j], Bv, sb);
             gh[j] *= dA;
           }
-          gdel[i] = gd;
-          rx[i] = gx;
+          gdel[i] = fmaf(xx, sb, gd);
+          rx[i] = dl * sb;
         }
         // sum the RS steps' dC, dB over the wavefront's lanes (channels) via wave-private LDS
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
