@@ -29,6 +29,25 @@ constexpr int kSubs = kBT / kSub;   // sub-tiles per tile
 static_assert(kSub == kCkptStep, "every sub-tile starts at a checkpoint");
 constexpr int kInStride = kBT + 1;  // entries per channel row of the per-step LDS arrays
 constexpr int kRedStride = kSub + 1;
+// floats per column of the dB/dC lane-sum scratch (64 lanes, padded so that the 16-byte column
+// reads of consecutive columns start in different bank groups)
+constexpr int kSumStride = 64 + 4;
+
+// v of lane l plus v of lane l ^ off (the same sum in both lanes): off 16 and 32 by the
+// lane-swap instructions, which leave {v(l), v(l ^ off)} in the two results in every lane (no
+// LDS round trip); smaller offsets by a permute
+__device__ __forceinline__ float xor_sum(float v, int off) {
+  const uint32_t u = __float_as_uint(v);
+  if (off == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if (off == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  return v + __shfl_xor(v, off);
+}
 
 // sigmoid(v) from delta = softplus(v): e^delta = 1 + e^v gives sigmoid(v) = 1 - e^-delta. For
 // small delta the series delta (1 - delta/2 + delta^2/6 - delta^3/24) avoids the cancellation
@@ -185,10 +204,11 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
       // first two arrays, so the third (rx, the dx partials) is written as the steps go
       float* scratch = s_red + w * 3 * kChannelsPerGroup * kRedStride;
       float* rx = s_red + ((w * 3 + 2) * kChannelsPerGroup + lane) * kRedStride;
-      static_assert(kChannelsPerGroup * (NV + 1) <= 2 * kChannelsPerGroup * kRedStride,
+      static_assert(NV * kSumStride <= 2 * kChannelsPerGroup * kRedStride,
                     "lane-sum scratch must stay clear of the dx partials");
-      // this lane's row of the scratch: [tensor (dC, dB)][state j][step e]
-      float* red = scratch + lane * (NV + 1);
+      // the scratch is column-major: value v of lane l at scratch[v * kSumStride + l], with v =
+      // [tensor (dC, dB)][state j][step e]
+      float* red = scratch + lane;
 #pragma unroll
       for (int i4 = kSub - RS; i4 >= 0; i4 -= RS) {
 #pragma unroll
@@ -205,13 +225,13 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
             const float Bv = s_B[(n0 + j) * kBT + t];
             const float Cv = s_C[(n0 + j) * kBT + t];
             gh[j] = fmaf(gy, Cv, gh[j]);
-            red[j * RS + e] = gy * hh[i][j];                       // dC
+            red[(j * RS + e) * kSumStride] = gy * hh[i][j];        // dC
             const float dA = __builtin_amdgcn_exp2f(dl * ap[j]);
             const float hp = i == 0 ? hsk[j] : hh[i - 1][j];
             const float gt = gh[j] * (hp * dA);
             gd = fmaf(gt, an[j], gd);
             da[j] = fmaf(gt, dl, da[j]);
-            red[RS * NS + j * RS + e] = gh[j] * u;                 // dB
+            red[(RS * NS + j * RS + e) * kSumStride] = gh[j] * u;  // dB
             sb = fmaf(gh[j], Bv, sb);
             gh[j] *= dA;
           }
@@ -222,13 +242,19 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // lane sums NV rows of column lane % NV; the 64 / NV lanes of a column then combine
+        // lane sums value col = lane % NV of the NV lanes part * NV .. + NV (four 16-byte reads
+        // of one column); the 64 / NV lanes of a column then combine across lanes
         const int col = lane % NV, part = lane / NV;
-        float sum = 0.0f;
+        float sum;
+        {
+          const f32x4* src = reinterpret_cast<const f32x4*>(scratch + col * kSumStride + part * NV);
+          f32x4 acc4 = src[0];
 #pragma unroll
-        for (int r = 0; r < NV; ++r) sum += scratch[(part * NV + r) * (NV + 1) + col];
+          for (int r4 = 1; r4 < NV / 4; ++r4) acc4 += src[r4];
+          sum = (acc4.x + acc4.y) + (acc4.z + acc4.w);
+        }
 #pragma unroll
-        for (int off = NV; off < 64; off <<= 1) sum += __shfl_xor(sum, off);
+        for (int off = NV; off < 64; off <<= 1) sum = xor_sum(sum, off);
         if (lane < NV) {
           const int tensor = col / (RS * NS), j = (col / RS) % NS, e = col % RS;
           const int64_t t = t0 + tb + i4 + e;
