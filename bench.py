@@ -170,8 +170,8 @@ def cpu_baseline(cfg, budget_s: float):
 def alu_model_bwd(cfg):
     """Minimal fp32 instruction stream of the gradient per token*channel: (flops, SIMD cycles),
     costs as in ``alu_model`` (diagonal A, delta * B rule).
-      per state update: the states recomputed once (delta*a, exp2, u*B, fma: 5 flops, 20 cyc)
-        and the reverse step (gh += gy C; gy h for dC; exp2 of delta*a; g = gh (h_prev dA);
+      per state update: the states recomputed once (delta*a, exp2, u*B, fma: 5 flops, 20 cyc),
+        with a gate their readout C h for dz (fma: 2 flops, 4 cyc), and the reverse step (gh += gy C; gy h for dC; exp2 of delta*a; g = gh (h_prev dA);
         ddelta part += g a; da += g delta; gh u for dB; sb += gh B; gh *= dA: 15 flops,
         10 plain ops + 1 transcendental = 48 cyc)
       per (t, channel): softplus and its derivative sigmoid (14 flops, 64 cyc), u = delta*x,
@@ -182,6 +182,9 @@ def alu_model_bwd(cfg):
     valu, trans = VALU_CYCLES, TRANS_CYCLES
     fl = cfg.N * (5 + 15) + 3
     cy = cfg.N * ((3 * valu + trans) + (10 * valu + trans)) + 2 * valu
+    if cfg.gate:
+        fl += cfg.N * 2
+        cy += cfg.N * valu
     if cfg.softplus:
         fl += 14
         cy += 10 * valu + 3 * trans
