@@ -513,6 +513,10 @@ int ssm_selective_scan_bwd(const ssm_scan_desc* desc, const void* x, const void*
   p.bc_vec = bc_vec ? 1 : 0;
 
   q.dy = dy; q.dx = dx; q.ddelta = ddelta; q.dz = dz;
+  // two-element stores of dx, ddelta, dz: their strides are those of x, delta, z, which vec_io
+  // makes multiples of 16 bytes; the bases must hold a pair
+  q.pair_out = (p.vec_io && aligned(dx, 2 * es) && aligned(ddelta, 2 * es) &&
+                (!dz || aligned(dz, 2 * es))) ? 1 : 0;
   q.dA = dA; q.dB = dB; q.dC = dC; q.dD = dD; q.dbias = ddelta_bias; q.dh0 = dh0;
   q.dB_part = reinterpret_cast<float*>(ws + lay.dB);
   q.dC_part = reinterpret_cast<float*>(ws + lay.dC);

@@ -57,6 +57,14 @@ __device__ __forceinline__ float sigmoid_from_softplus(float dl) {
   return dl < 0.1f ? series : 1.0f - __builtin_amdgcn_exp2f(-dl * kLog2e);
 }
 
+// two consecutive elements (a, b) at p, which holds a pair: one 4-byte (bf16) or 8-byte store
+__device__ __forceinline__ void store_pair(bf16_bits* p, float a, float b) {
+  *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(a, b);
+}
+__device__ __forceinline__ void store_pair(float* p, float a, float b) {
+  *reinterpret_cast<float2*>(p) = make_float2(a, b);
+}
+
 template <typename IO, int NS, bool GATE>
 __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
   constexpr int NW = kWavesPerGroup;
@@ -305,12 +313,19 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
           IO* dxr = static_cast<IO*>(q.dx) + b * p.x_sb + ed * p.x_sd;
           IO* ddr = static_cast<IO*>(q.ddelta) + b * p.dl_sb + ed * p.dl_sd;
           IO* dzr = GATE ? static_cast<IO*>(q.dz) + b * p.z_sb + ed * p.z_sd : nullptr;
+          if (q.pair_out && tt + 1 < L) {
+            // tt is even: both steps in one store per tensor
+            store_pair(dxr + tt, vx[0], vx[1]);
+            store_pair(ddr + tt, vd[0], vd[1]);
+            if constexpr (GATE) store_pair(dzr + tt, vz[0], vz[1]);
+          } else {
 #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            if (tt + e < L) {
-              store_elem(dxr + tt + e, vx[e]);
-              store_elem(ddr + tt + e, vd[e]);
-              if constexpr (GATE) store_elem(dzr + tt + e, vz[e]);
+            for (int e = 0; e < 2; ++e) {
+              if (tt + e < L) {
+                store_elem(dxr + tt + e, vx[e]);
+                store_elem(ddr + tt + e, vd[e]);
+                if constexpr (GATE) store_elem(dzr + tt + e, vz[e]);
+              }
             }
           }
         }

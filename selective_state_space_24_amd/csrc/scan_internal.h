@@ -76,6 +76,8 @@ struct BwdParams {
   float* dA_part; // (batch, dim, N)
   float* dD_part; // (batch, dim)
   float* dbias_part;
+  int32_t pair_out;  // dx, ddelta, dz allow stores of two consecutive elements (aligned to 2
+                     // elements, with the strides of x, delta, z)
 };
 hipError_t launch_bwd(const BwdParams& q, bool bf16, hipStream_t stream);
 // Chunked matrix form of the head-mode forward pass (bf16 io, MFMA). ssd_supported checks the
