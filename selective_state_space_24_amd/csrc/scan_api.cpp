@@ -10,6 +10,7 @@
 
 namespace {
 
+constexpr int64_t kCUs = 256;                 // compute units of an MI355X
 constexpr int64_t kTargetWaves = 2048;        // about two resident wavefronts per SIMD (256 CUs)
 constexpr int64_t kMinSegmentTiles = 8;       // shortest segment worth a summary pass, in tiles
 constexpr int64_t kMaxSegments = 65535;       // grid.y limit
@@ -17,6 +18,7 @@ constexpr int64_t kMaxSegments = 65535;       // grid.y limit
 struct Plan {
   int64_t nseg;
   int64_t seg_len;
+  bool four_wave = false;  // bf16 io, 8 < dstate <= 16: the four-wavefront kernel (see below)
 };
 
 bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
@@ -91,11 +93,21 @@ Plan plan_segments(const ssm_scan_desc* d) {
   if (groups == 0 || d->seqlen == 0) return p;
   if (waves * 4 >= kTargetWaves * 3) return p;  // enough channel groups: one pass
   int64_t want = (kTargetWaves + waves - 1) / waves;
-  // bf16 io with 8 < N <= 16 runs the kernel with independent wavefronts, one 8-wavefront
-  // workgroup per CU: segments beyond what fills the chip once would start a second round of
-  // workgroups that leaves most CUs idle, so the count is rounded down instead
-  if (d->io_dtype == SSM_DTYPE_BF16 && d->dstate > 8 && d->dstate <= 16)
+  if (d->io_dtype == SSM_DTYPE_BF16 && d->dstate > 8 && d->dstate <= 16) {
+    // bf16 io with 8 < N <= 16 runs the kernel with independent wavefronts, one 8-wavefront
+    // workgroup (128 channels) per CU. With 64-channel groups for three quarters of the CUs or
+    // more, but too few 128-channel workgroups to fill the chip, the four-wavefront kernel (two
+    // workgroups per CU) runs the whole sequence in one pass instead: no summary pass, and its
+    // workgroups spread over more CUs (measured 183 us against 192-204 us at batch 8,
+    // d_inner 1536, L 2048, and likewise at 8 x 2048 and 4 x 4096 channels)
+    if (groups * 4 >= kCUs * 3) {
+      p.four_wave = true;
+      return p;
+    }
+    // otherwise segments: beyond what fills the chip once they would start a second round of
+    // workgroups that leaves most CUs idle, so the count is rounded down
     want = kTargetWaves / waves;
+  }
   const int64_t tiles = (d->seqlen + tile - 1) / tile;
   const int64_t max_by_len = tiles / kMinSegmentTiles;
   if (want > max_by_len) want = max_by_len;
@@ -277,6 +289,7 @@ int ssm_selective_scan_fwd_ext(const ssm_scan_desc* desc, const void* x, const v
   p.groups_per_batch = (d.dim + ssm::kChannelsPerGroup - 1) / ssm::kChannelsPerGroup;
   p.seg_len = plan.seg_len;
   p.nseg = (int32_t)plan.nseg;
+  p.four_wave = plan.four_wave ? 1 : 0;
   p.softplus = delta_softplus ? 1 : 0;
   p.zoh = disc == SSM_DISC_ZOH ? 1 : 0;
   // 16-byte vector access of x/delta/z/y rows: 16-byte aligned bases, strides multiple of 16 B

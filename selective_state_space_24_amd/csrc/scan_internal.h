@@ -47,6 +47,8 @@ struct ScanParams {
   int32_t zoh;               // zero-order-hold B discretisation instead of delta * B
   int32_t state_vec;         // decode: the state allows 16-byte access (N % 4 == 0, aligned)
   int32_t a_vec;             // decode: rows of A allow 16-byte access
+  int32_t four_wave;         // bf16 io, 8 < N <= 16: run scan_fwd_kernel rather than the kernel
+                             // with independent wavefronts (chosen by the segment planner)
 };
 
 // One launcher per (io dtype, A mode); each is compiled in its own translation unit.

@@ -1141,30 +1141,33 @@ hipError_t launch_cfg(const ScanParams& p, hipStream_t stream) {
   const dim3 block(64 * NW);
   const int64_t groups = p.batch * p.groups_per_batch;
   if constexpr (NS == 4 && WaveIo<IO>::value) {
-    // 8 < N <= 16: the kernel with independent wavefronts for the output. The summaries take it
-    // too when they fill about three quarters of the chip (1536 wavefronts, 192 CUs); fewer
-    // summary workgroups run faster spread over more CUs in the four-wavefront form.
-    const unsigned wg = (unsigned)(p.batch * ((p.dim + kWaveGroupChannels - 1) / kWaveGroupChannels));
-    const dim3 wblock(64 * kWaveGroupWaves);
-    if (p.nseg > 1) {
-      if ((int64_t)wg * (p.nseg - 1) * kWaveGroupWaves >= 1536)
-        hipLaunchKernelGGL((scan_fwd_wave_kernel<IO, HEAD, false, ZOH, kWaveSummary>),
-                           dim3(wg, (unsigned)(p.nseg - 1)), wblock, 0, stream, SCAN_ARGS(p));
-      else
-        hipLaunchKernelGGL((scan_fwd_kernel<IO, NS, NW, HEAD, true, false, ZOH>),
-                           dim3((unsigned)groups, (unsigned)(p.nseg - 1)), block, 0, stream,
+    // (four_wave: the segment planner chose the four-wavefront form below instead)
+    if (!p.four_wave) {
+      // 8 < N <= 16: the kernel with independent wavefronts for the output. The summaries take it
+      // too when they fill about three quarters of the chip (1536 wavefronts, 192 CUs); fewer
+      // summary workgroups run faster spread over more CUs in the four-wavefront form.
+      const unsigned wg = (unsigned)(p.batch * ((p.dim + kWaveGroupChannels - 1) / kWaveGroupChannels));
+      const dim3 wblock(64 * kWaveGroupWaves);
+      if (p.nseg > 1) {
+        if ((int64_t)wg * (p.nseg - 1) * kWaveGroupWaves >= 1536)
+          hipLaunchKernelGGL((scan_fwd_wave_kernel<IO, HEAD, false, ZOH, kWaveSummary>),
+                             dim3(wg, (unsigned)(p.nseg - 1)), wblock, 0, stream, SCAN_ARGS(p));
+        else
+          hipLaunchKernelGGL((scan_fwd_kernel<IO, NS, NW, HEAD, true, false, ZOH>),
+                             dim3((unsigned)groups, (unsigned)(p.nseg - 1)), block, 0, stream,
+                             SCAN_ARGS(p));
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      const dim3 wgrid(wg, (unsigned)p.nseg);
+      if (p.z)
+        hipLaunchKernelGGL((scan_fwd_wave_kernel<IO, HEAD, true, ZOH>), wgrid, wblock, 0, stream,
                            SCAN_ARGS(p));
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
+      else
+        hipLaunchKernelGGL((scan_fwd_wave_kernel<IO, HEAD, false, ZOH>), wgrid, wblock, 0, stream,
+                           SCAN_ARGS(p));
+      return hipGetLastError();
     }
-    const dim3 wgrid(wg, (unsigned)p.nseg);
-    if (p.z)
-      hipLaunchKernelGGL((scan_fwd_wave_kernel<IO, HEAD, true, ZOH>), wgrid, wblock, 0, stream,
-                         SCAN_ARGS(p));
-    else
-      hipLaunchKernelGGL((scan_fwd_wave_kernel<IO, HEAD, false, ZOH>), wgrid, wblock, 0, stream,
-                         SCAN_ARGS(p));
-    return hipGetLastError();
   }
   if (p.nseg > 1) {
     const dim3 grid_sum((unsigned)groups, (unsigned)(p.nseg - 1));
