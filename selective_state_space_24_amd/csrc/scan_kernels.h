@@ -2,8 +2,10 @@
 //
 // Two kernels. scan_fwd_wave_kernel (further down) serves bf16 io with 8 < N <= 16: every
 // wavefront owns 16 channels x all states and runs without workgroup barriers. scan_fwd_kernel,
-// described here, serves every other case (fp32 io, N <= 8 or N > 16) and also runs the segment
-// summaries and the backward pass's checkpoints.
+// described here, serves every other case (fp32 io, N <= 8 or N > 16, and bf16 shapes whose
+// 128-channel workgroups are too few to fill the chip while its 64-channel ones are not: the
+// segment planner's four_wave choice) and also runs some segment summaries and the backward
+// pass's checkpoints.
 //
 // Work decomposition of scan_fwd_kernel: one workgroup = 64 channels of one batch entry x one
 // segment of L, in NW wavefronts.
