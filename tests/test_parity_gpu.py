@@ -98,6 +98,9 @@ EDGE = [
     (1, 200, 300, 12, 1, "diag", "bf16", True, False, True, False, 1),    # padded state quad
     (2, 256, 130, 9, 1, "diag", "bf16", True, True, False, True, 2),      # two groups, N = 9
     (3, 48, 64, 16, 1, "diag", "bf16", True, True, True, True, 1),        # one full tile
+    # 192-383 groups of 64 channels: the four-wavefront kernel in one pass (ragged dim, N = 12)
+    (3, 4100, 100, 16, 1, "diag", "bf16", True, True, True, True, 1),
+    (2, 6200, 40, 12, 1, "diag", "bf16", False, True, True, True, 1),
 ]
 
 
