@@ -400,21 +400,30 @@ template <typename IO, int NS>
 static hipError_t bwd_cfg(const BwdParams& q, hipStream_t stream) {
   const ScanParams& p = q.f;
   const int64_t groups = p.batch * p.groups_per_batch;
-  // 1. checkpoints (bf16 io with 8 < N <= 16: the kernel with independent wavefronts)
-  if constexpr (NS == 4 && WaveIo<IO>::value) {
-    const unsigned wg = (unsigned)(p.batch * ((p.dim + kWaveGroupChannels - 1) / kWaveGroupChannels));
-    hipLaunchKernelGGL((scan_fwd_wave_kernel<IO, false, false, false, kWaveCkpt>), dim3(wg, 1),
-                       dim3(64 * kWaveGroupWaves), 0, stream, static_cast<const IO*>(p.x),
-                       static_cast<const IO*>(p.delta), static_cast<const IO*>(p.B),
-                       static_cast<const IO*>(p.C), static_cast<const IO*>(nullptr),
-                       static_cast<IO*>(nullptr), p.A, p.D, p.delta_bias, nullptr, nullptr, p);
-  } else {
+  // 1. checkpoints (bf16 io with 8 < N <= 16: the kernel with independent wavefronts, except
+  // where the forward's planner takes the four-wavefront kernel: 192 to 383 groups of 64
+  // channels, too few 128-channel workgroups to fill the chip)
+  auto four_wave_ckpt = [&]() {
     hipLaunchKernelGGL((scan_fwd_kernel<IO, NS, kWavesPerGroup, false, false, false, false, true>),
                        dim3((unsigned)groups, 1), dim3(64 * kWavesPerGroup), 0, stream,
                        static_cast<const IO*>(p.x), static_cast<const IO*>(p.delta),
                        static_cast<const IO*>(p.B), static_cast<const IO*>(p.C),
                        static_cast<const IO*>(nullptr), static_cast<IO*>(nullptr), p.A, p.D,
                        p.delta_bias, nullptr, nullptr, p);
+  };
+  if constexpr (NS == 4 && WaveIo<IO>::value) {
+    if (groups < 192 || groups >= 384) {
+      const unsigned wg = (unsigned)(p.batch * ((p.dim + kWaveGroupChannels - 1) / kWaveGroupChannels));
+      hipLaunchKernelGGL((scan_fwd_wave_kernel<IO, false, false, false, kWaveCkpt>), dim3(wg, 1),
+                         dim3(64 * kWaveGroupWaves), 0, stream, static_cast<const IO*>(p.x),
+                         static_cast<const IO*>(p.delta), static_cast<const IO*>(p.B),
+                         static_cast<const IO*>(p.C), static_cast<const IO*>(nullptr),
+                         static_cast<IO*>(nullptr), p.A, p.D, p.delta_bias, nullptr, nullptr, p);
+    } else {
+      four_wave_ckpt();
+    }
+  } else {
+    four_wave_ckpt();
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
