@@ -101,6 +101,7 @@ EDGE = [
     # 192-383 groups of 64 channels: the four-wavefront kernel in one pass (ragged dim, N = 12)
     (3, 4100, 100, 16, 1, "diag", "bf16", True, True, True, True, 1),
     (2, 6200, 40, 12, 1, "diag", "bf16", False, True, True, True, 1),
+    (2, 6400, 48, 16, 64, "head", "bf16", True, True, True, True, 1),   # and in head mode
 ]
 
 
