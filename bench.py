@@ -7,12 +7,13 @@ every stage of the scan runs inside it. Inputs are generated once, copied to HBM
 resident; the timed region covers exactly ``--steps`` calls between two device
 synchronisations, timed with HIP events on the stream the kernels are launched on.
 
-Prints one JSON line: throughput in Gtoken*channel/s; the roofline of the scan kernel, which is
-bound by fp32 VALU and transcendental issue, not by HBM (algorithmic flops per launch / average
-launch time, against the peak of the same instruction mix at full issue, see ``alu_model``); the
-HBM figures beside it (algorithmic bytes and, when a counter profile of the current kernel source
-is committed, counted bytes, against the 8 TB/s peak); and the fp64 CPU oracle timed on the host
-cores over whole batch entries of the same workload.
+Prints one JSON line: throughput in Gtoken*channel/s; the HBM roofline of the scan kernel
+(algorithmic bytes per launch / average launch time against the 8 TB/s peak, with the bytes
+counted by a committed profile of the current kernel source beside them, and the fraction of a
+device copy's bandwidth measured in the same run); the ALU roofline that actually bounds it
+(algorithmic flops per launch / launch time against the peak of the same fp32 instruction mix at
+full issue, see ``alu_model``); and the fp64 CPU oracle timed on the host cores over whole batch
+entries of the same workload.
 
 ``--workload bwd`` measures the backward pass (all input gradients) of the same workload.
 ``--workload heads`` measures the scalar-decay heads scan (batch 4, 64 heads x 64 channels,
@@ -21,8 +22,10 @@ recurrent`` for the step-by-step recurrence instead); its roofline is HBM bandwi
 algorithmic matrix flops reported beside it against the bf16 MFMA peak.
 ``--workload decode`` measures instead one recurrent decoding step (``ssm_selective_state_update``)
 on the Mamba-1.4B layer at batch 1024: a step reads and writes the fp32 state once, so its
-roofline is HBM bandwidth. ``--copy-calibration`` runs only a plain device copy of a known size
-(for scaling the FETCH_SIZE / WRITE_SIZE counters of a profiler run).
+roofline is HBM bandwidth. ``--workload lsweep`` times the scan at a fixed batch x channels
+(1 x 2048, the million-token config's) over L = 2^12 .. 2^20 and fits the slope of log time
+against log L (1 for a linear-time scan). ``--copy-calibration`` runs only a plain device copy of
+a known size (for scaling the FETCH_SIZE / WRITE_SIZE counters of a profiler run).
 """
 from __future__ import annotations
 
@@ -447,6 +450,97 @@ def timed_steps(step, args, torch, stream):
     return ms, pct
 
 
+def measure_copy_GBs(torch, nbytes: int = 1 << 30, reps: int = 20) -> float:
+    """Read + write bandwidth of a plain device-to-device copy of ``nbytes`` (event-timed on the
+    current stream after a short warm-up): the practical ceiling of a streaming kernel."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def run_lsweep(args, torch):
+    """Time per call of the scan over L = 2^12 .. 2^20 at batch 1 x 2048 channels (bf16, N 16,
+    gate and softplus on). Inputs are drawn on the GPU with the workload's distributions from a
+    seeded generator (timing only: the parity tests cover these shapes)."""
+    import math
+    import selective_state_space_24_amd as ssm
+    g = torch.Generator(device="cuda")
+    g.manual_seed(12)
+    batch, dim, N = 1, 2048, 16
+    A = -torch.arange(1, N + 1, dtype=torch.float32, device="cuda").repeat(dim, 1).contiguous()
+    D = torch.randn(dim, generator=g, device="cuda")
+    u = torch.rand(dim, generator=g, device="cuda") * 0.099 + 0.001
+    bias = torch.log(torch.expm1(u))
+    points = []
+    stream = torch.cuda.current_stream()
+    for e in range(12, 21):
+        L = 1 << e
+        bf = torch.bfloat16
+        x = torch.randn(batch, dim, L, generator=g, device="cuda").to(bf)
+        dl = (0.5 * torch.randn(batch, dim, L, generator=g, device="cuda")).to(bf)
+        z = torch.randn(batch, dim, L, generator=g, device="cuda").to(bf)
+        B = torch.randn(batch, 1, N, L, generator=g, device="cuda").to(bf)
+        C = torch.randn(batch, 1, N, L, generator=g, device="cuda").to(bf)
+        y = torch.empty_like(x)
+        desc = ssm.describe(x, dl, A, B, C, z, y)
+        ws_bytes = ssm.workspace_size(desc)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+
+        def step():
+            rc = ssm.fwd_raw(desc, x.data_ptr(), dl.data_ptr(), A.data_ptr(), B.data_ptr(),
+                             C.data_ptr(), D.data_ptr(), z.data_ptr(), bias.data_ptr(), True,
+                             y.data_ptr(), ws.data_ptr() if ws_bytes else None, ws_bytes,
+                             stream.cuda_stream)
+            if rc != 0:
+                raise ssm.ScanError(rc, "ssm_selective_scan_fwd")
+
+        sub = argparse.Namespace(warmup=max(3, min(args.warmup, 20)), steps=max(5, min(args.steps, 20)))
+        ms, pct = timed_steps(step, sub, torch, stream)
+        tokch = batch * dim * L
+        points.append({"L": L, "ms": round(ms, 5), "median_ms": round(pct(0.5), 5),
+                       "Gtokch_s": round(tokch / (ms * 1e-3) / 1e9, 2),
+                       "launches": 1 if ws_bytes == 0 else 2})
+        print(f"[lsweep] L={L}: {ms:.4f} ms", file=sys.stderr, flush=True)
+        del x, dl, z, B, C, y, ws
+        torch.cuda.empty_cache()
+    xs = [math.log(pt["L"]) for pt in points]
+    ys = [math.log(pt["ms"]) for pt in points]
+    n = len(xs)
+    mx, my = sum(xs) / n, sum(ys) / n
+    slope = sum((a - mx) * (b - my) for a, b in zip(xs, ys)) / sum((a - mx) ** 2 for a in xs)
+    # the same fit over the points whose segment plan fills the chip (L >= 2^15)
+    big = [(a, b) for a, b, pt in zip(xs, ys, points) if pt["L"] >= 1 << 15]
+    mbx, mby = sum(a for a, _ in big) / len(big), sum(b for _, b in big) / len(big)
+    slope_big = (sum((a - mbx) * (b - mby) for a, b in big) /
+                 sum((a - mbx) ** 2 for a, _ in big))
+    last = points[-1]
+    out = {
+        "metric": "selective-scan time vs sequence length at fixed batch x channels, 1 MI355X",
+        "value": round(slope, 4), "unit": "d log(time) / d log(L)", "n_gpus": 1,
+        "steps": sub.steps, "warmup": sub.warmup, "ms_per_step": last["ms"],
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 arithmetic and state, bf16 io", "data": "synthetic (seeded, on the GPU)",
+        "config": {"workload": "S6 forward scan, batch 1 x d_inner 2048, N 16, L 2^12..2^20",
+                   "gate": "silu(z)", "delta_softplus": True},
+        "slope_L_ge_32768": round(slope_big, 4),
+        "points": points,
+        "kernel_source": kernel_source_hash(),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -458,7 +552,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 skips it)")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--workload", choices=("scan", "decode", "bwd", "heads"), default="scan")
+    ap.add_argument("--workload", choices=("scan", "decode", "bwd", "heads", "lsweep"),
+                    default="scan")
     ap.add_argument("--algorithm", choices=("chunked", "recurrent"), default="chunked",
                     help="--workload heads: the form of the scan")
     args = ap.parse_args()
@@ -500,6 +595,9 @@ def main():
     if args.workload == "heads":
         run_heads(args, torch)
         return
+    if args.workload == "lsweep":
+        run_lsweep(args, torch)
+        return
 
     import ssmgen
     import selective_state_space_24_amd as ssm
@@ -521,6 +619,7 @@ def main():
             raise ssm.ScanError(rc, "ssm_selective_scan_fwd")
 
     ms, pct = timed_steps(step, args, torch, stream)
+    copy_gbs = measure_copy_GBs(torch)
 
     # one launch per step when the sequence is not split along L (no workspace needed)
     launches = 1 if ws_bytes == 0 else 2
@@ -532,6 +631,7 @@ def main():
     launch_ms = ms if launches == 1 else None
     achieved = alg_flops / (launch_ms * 1e-3) / 1e12 if launch_ms else None
     traffic = traffic_from_profile("mamba14b_layer")
+    hbm_gbs = alg_bytes / (launch_ms * 1e-3) / 1e9 if launch_ms else None
     out = {
         "metric": "selective-scan Gtoken\u00b7channel/s and achieved HBM GB/s vs peak, 1 MI355X",
         "value": round(tokch / (ms * 1e-3) / 1e9, 3),
@@ -543,7 +643,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32 arithmetic and state, bf16 io",
         "data": "synthetic",
         "config": {
             "workload": "Mamba-1.4B layer selective scan (S6 forward)",
@@ -552,20 +652,30 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": {
-            "bound": "alu",
+            "bound": "hbm",
+            "achieved": round(hbm_gbs, 1) if hbm_gbs else None,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(hbm_gbs / HBM_PEAK_GBS, 4) if hbm_gbs else None,
+            "traffic": traffic,
+            "algorithmic_bytes": alg_bytes,
+            "copy_GBs": round(copy_gbs, 1),
+            "frac_of_copy": round(hbm_gbs / copy_gbs, 4) if hbm_gbs else None,
+            "counter_GBs": round(traffic / (launch_ms * 1e-3) / 1e9, 1)
+            if (traffic and launch_ms) else None,
+        },
+        # what actually bounds this kernel: fp32 VALU and transcendental issue. The peak is that
+        # of the method's own instruction mix at full issue on 1024 SIMDs at 2.4 GHz (alu_model)
+        "alu": {
             "achieved": round(achieved, 2) if achieved else None,
             "peak": round(peak, 2),
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4) if achieved else None,
-            "traffic": traffic,
-        },
-        "hbm": {
-            "algorithmic_bytes": alg_bytes,
-            "algorithmic_GBs": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
-            "peak_GBs": HBM_PEAK_GBS,
-            "frac_of_peak": round(alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "counter_GBs": round(traffic / (launch_ms * 1e-3) / 1e9, 1)
-            if (traffic and launch_ms) else None,
+            "frac_of_fp32_vector_peak": round(achieved / 78.6, 4) if achieved else None,
+            "derivation": (f"per 64 token*channels: {cfg.N} state updates x (4 fp32 ops x "
+                           f"{VALU_CYCLES} cycles + 1 exp2 x {TRANS_CYCLES} cycles) + bias, "
+                           f"softplus, delta*x, D skip and silu gate = {alu_model(cfg)[1]:.0f} "
+                           f"SIMD cycles for {fl:.0f} flops; 1024 SIMDs at 2.4 GHz"),
         },
         "step_ms": {"p10": round(pct(0.1), 5), "median": round(pct(0.5), 5),
                     "p90": round(pct(0.9), 5)},

@@ -59,7 +59,10 @@ typedef enum {
                                   dim % headdim, dstate > SSM_MAX_DSTATE (128), or sizes that overflow */
   SSM_ERR_BAD_DTYPE = -3,      /* io_dtype, a_mode, discretization or algorithm not one of the
                                   enums below */
-  SSM_ERR_BAD_STRIDE = -4,     /* a negative stride, or strides that make rows overlap */
+  SSM_ERR_BAD_STRIDE = -4,     /* a negative stride, or strides that make the rows of an output
+                                  overlap (the rows of a tensor are disjoint when, taken by
+                                  increasing stride, each dimension of size > 1 steps past the
+                                  whole extent of the dimensions below it) */
   SSM_ERR_MISALIGNED = -5,     /* a pointer not aligned to its element size */
   SSM_ERR_ALIAS = -6,          /* an output (y, h_final, workspace) overlaps an input or another
                                   output */
@@ -198,7 +201,10 @@ int ssm_selective_scan_bwd_workspace_size(const ssm_scan_desc* desc, size_t* byt
  *   dh0      : nullable, (batch, dim, dstate) fp32: the gradient of the initial state
  *   workspace: at least ssm_selective_scan_bwd_workspace_size bytes, 4-byte aligned
  * Supported: A_DIAG mode with dstate <= 16 (SSM_ERR_UNSUPPORTED otherwise). Outputs must not
- * overlap any input or each other. Results are deterministic (fixed-order reductions). */
+ * overlap any input or each other. Because dx, ddelta, dz, dB and dC are written with the
+ * strides of x, delta, z, B and C, those strides must give disjoint rows (as y's must in the
+ * forward call; a stride-0 broadcast of B, say, returns SSM_ERR_BAD_STRIDE). Results are
+ * deterministic (fixed-order reductions). */
 int ssm_selective_scan_bwd(const ssm_scan_desc* desc, const void* x, const void* delta,
                            const float* A, const void* B, const void* C, const float* D,
                            const void* z, const float* delta_bias, int32_t delta_softplus,

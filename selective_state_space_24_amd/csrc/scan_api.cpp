@@ -10,8 +10,7 @@
 
 namespace {
 
-constexpr int64_t kCUs = 256;                 // compute units of an MI355X
-constexpr int64_t kTargetWaves = 2048;        // about two resident wavefronts per SIMD (256 CUs)
+using ssm::kTargetWaves;
 constexpr int64_t kMinSegmentTiles = 8;       // shortest segment worth a summary pass, in tiles
 constexpr int64_t kMaxSegments = 65535;       // grid.y limit
 
@@ -44,6 +43,35 @@ int64_t extent4(int64_t n0, int64_t n1, int64_t n2, int64_t L, int64_t s0, int64
   return e;
 }
 
+// True when the rows of a tensor with L-contiguous rows, `nd` outer dimensions of sizes n[] and
+// element strides s[] (any order), are pairwise disjoint: taken by increasing stride, every
+// dimension of size > 1 must step past the whole extent of the dimensions below it.
+bool rows_disjoint(int nd, const int64_t* n, const int64_t* s, int64_t L) {
+  if (L <= 0) return true;
+  int idx[4];
+  int k = 0;
+  for (int i = 0; i < nd; ++i)
+    if (n[i] > 1) idx[k++] = i;
+  for (int i = 1; i < k; ++i)  // insertion sort by stride
+    for (int j = i; j > 0 && s[idx[j]] < s[idx[j - 1]]; --j) {
+      const int t = idx[j]; idx[j] = idx[j - 1]; idx[j - 1] = t;
+    }
+  int64_t extent = L;
+  for (int i = 0; i < k; ++i) {
+    const int64_t st = s[idx[i]], cnt = n[idx[i]];
+    if (st < extent) return false;
+    int64_t e;
+    if (!mul_ok(cnt - 1, st, &e) || __builtin_add_overflow(e, extent, &e)) return false;
+    extent = e;
+  }
+  return true;
+}
+
+bool rows_disjoint3(int64_t n0, int64_t n1, int64_t L, int64_t s0, int64_t s1) {
+  const int64_t n[] = {n0, n1}, s[] = {s0, s1};
+  return rows_disjoint(2, n, s, L);
+}
+
 int check_desc(const ssm_scan_desc* d) {
   if (!d) return SSM_ERR_NULL_ARG;
   if (d->io_dtype != SSM_DTYPE_F32 && d->io_dtype != SSM_DTYPE_BF16) return SSM_ERR_BAD_DTYPE;
@@ -64,13 +92,8 @@ int check_desc(const ssm_scan_desc* d) {
   for (int64_t s : strides)
     if (s < 0) return SSM_ERR_BAD_STRIDE;
   // y rows must be disjoint (they are written)
-  if (d->dim > 1 && d->seqlen > 0 && d->y_stride_dim < d->seqlen) return SSM_ERR_BAD_STRIDE;
-  if (d->batch > 1 && d->seqlen > 0) {
-    int64_t last;
-    if (!mul_ok(d->dim - 1, d->y_stride_dim, &last) || __builtin_add_overflow(last, d->seqlen, &last))
-      return SSM_ERR_BAD_STRIDE;
-    if (d->y_stride_batch < last) return SSM_ERR_BAD_STRIDE;
-  }
+  if (!rows_disjoint3(d->batch, d->dim, d->seqlen, d->y_stride_batch, d->y_stride_dim))
+    return SSM_ERR_BAD_STRIDE;
   const int64_t drows = d->a_mode == SSM_A_HEAD ? d->dim / d->headdim : d->dim;
   if (extent3(d->batch, d->dim, d->seqlen, d->x_stride_batch, d->x_stride_dim) < 0 ||
       extent3(d->batch, drows, d->seqlen, d->delta_stride_batch, d->delta_stride_dim) < 0 ||
@@ -91,16 +114,15 @@ Plan plan_segments(const ssm_scan_desc* d) {
   const int64_t waves = groups * ssm::kWavesPerGroup;
   Plan p{1, d->seqlen > 0 ? d->seqlen : 1};
   if (groups == 0 || d->seqlen == 0) return p;
-  if (waves * 4 >= kTargetWaves * 3) return p;  // enough channel groups: one pass
+  if (ssm::groups_fill_chip(groups)) return p;  // enough channel groups: one pass
   int64_t want = (kTargetWaves + waves - 1) / waves;
   if (d->io_dtype == SSM_DTYPE_BF16 && d->dstate > 8 && d->dstate <= 16) {
     // bf16 io with 8 < N <= 16 runs the kernel with independent wavefronts, one 8-wavefront
-    // workgroup (128 channels) per CU. With 64-channel groups for three quarters of the CUs or
-    // more, but too few 128-channel workgroups to fill the chip, the four-wavefront kernel (two
-    // workgroups per CU) runs the whole sequence in one pass instead: no summary pass, and its
-    // workgroups spread over more CUs (measured 183 us against 192-204 us at batch 8,
-    // d_inner 1536, L 2048, and likewise at 8 x 2048 and 4 x 4096 channels)
-    if (groups * 4 >= kCUs * 3) {
+    // workgroup (128 channels) per CU, except where four_wave_one_pass holds: then the
+    // four-wavefront kernel needs no summary pass, and its workgroups spread over more CUs
+    // (measured 183 us against 192-204 us at batch 8, d_inner 1536, L 2048, and likewise at
+    // 8 x 2048 and 4 x 4096 channels)
+    if (ssm::four_wave_one_pass(groups)) {
       p.four_wave = true;
       return p;
     }
@@ -453,6 +475,19 @@ int ssm_selective_scan_bwd(const ssm_scan_desc* desc, const void* x, const void*
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
   }
   if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dB || !dC) return SSM_ERR_NULL_ARG;
+  // dx, ddelta, dz, dB and dC are written with the strides of x, delta, z, B and C: inputs may
+  // overlap themselves (a broadcast B, say), gradients may not
+  {
+    const int64_t drows = d.a_mode == SSM_A_HEAD ? d.dim / d.headdim : d.dim;
+    const int64_t nbc[] = {d.batch, d.ngroups, d.dstate};
+    const int64_t sB[] = {d.B_stride_batch, d.B_stride_group, d.B_stride_state};
+    const int64_t sC[] = {d.C_stride_batch, d.C_stride_group, d.C_stride_state};
+    if (!rows_disjoint3(d.batch, d.dim, d.seqlen, d.x_stride_batch, d.x_stride_dim) ||
+        !rows_disjoint3(d.batch, drows, d.seqlen, d.delta_stride_batch, d.delta_stride_dim) ||
+        (z && !rows_disjoint3(d.batch, d.dim, d.seqlen, d.z_stride_batch, d.z_stride_dim)) ||
+        !rows_disjoint(3, nbc, sB, d.seqlen) || !rows_disjoint(3, nbc, sC, d.seqlen))
+      return SSM_ERR_BAD_STRIDE;
+  }
 
   const void* io_ptrs[] = {x, delta, B, C, z, dy, dx, ddelta, dz};
   for (const void* q : io_ptrs)

@@ -401,8 +401,7 @@ static hipError_t bwd_cfg(const BwdParams& q, hipStream_t stream) {
   const ScanParams& p = q.f;
   const int64_t groups = p.batch * p.groups_per_batch;
   // 1. checkpoints (bf16 io with 8 < N <= 16: the kernel with independent wavefronts, except
-  // where the forward's planner takes the four-wavefront kernel: 192 to 383 groups of 64
-  // channels, too few 128-channel workgroups to fill the chip)
+  // where the forward's planner takes the four-wavefront kernel, four_wave_one_pass)
   auto four_wave_ckpt = [&]() {
     hipLaunchKernelGGL((scan_fwd_kernel<IO, NS, kWavesPerGroup, false, false, false, false, true>),
                        dim3((unsigned)groups, 1), dim3(64 * kWavesPerGroup), 0, stream,
@@ -412,7 +411,7 @@ static hipError_t bwd_cfg(const BwdParams& q, hipStream_t stream) {
                        p.delta_bias, nullptr, nullptr, p);
   };
   if constexpr (NS == 4 && WaveIo<IO>::value) {
-    if (groups < 192 || groups >= 384) {
+    if (!four_wave_one_pass(groups)) {
       const unsigned wg = (unsigned)(p.batch * ((p.dim + kWaveGroupChannels - 1) / kWaveGroupChannels));
       hipLaunchKernelGGL((scan_fwd_wave_kernel<IO, false, false, false, kWaveCkpt>), dim3(wg, 1),
                          dim3(64 * kWaveGroupWaves), 0, stream, static_cast<const IO*>(p.x),

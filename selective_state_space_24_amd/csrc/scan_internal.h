@@ -14,6 +14,24 @@ constexpr int kLT = 2 * kTB;  // time steps per load tile (128 bytes of bf16 per
                               // along L start at multiples of it
 constexpr int kCkptStep = 8;  // steps between the states the backward checkpoint pass stores
 
+constexpr int64_t kCUs = 256;           // compute units of an MI355X
+constexpr int64_t kTargetWaves = 2048;  // about two resident wavefronts per SIMD (256 CUs)
+
+// True when `groups` (batch x 64-channel groups) runs the whole sequence in one pass without
+// further thought: enough four-wavefront workgroups for three quarters of the target waves.
+inline bool groups_fill_chip(int64_t groups) {
+  return groups * kWavesPerGroup * 4 >= kTargetWaves * 3;
+}
+
+// bf16 io with 8 < N <= 16 normally runs the kernel with independent wavefronts (128-channel,
+// 8-wavefront workgroups, one per CU). With 64-channel groups for three quarters of the CUs or
+// more, but too few 128-channel workgroups to fill the chip, the four-wavefront kernel (two
+// workgroups per CU) runs the whole sequence in one pass instead. The forward planner and the
+// backward checkpoint pass both take this choice from here.
+inline bool four_wave_one_pass(int64_t groups) {
+  return groups * 4 >= kCUs * 3 && !groups_fill_chip(groups);
+}
+
 struct ScanParams {
   // inputs / outputs (device pointers); element type is the io dtype unless noted
   const void* x;

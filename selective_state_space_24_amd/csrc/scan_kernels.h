@@ -170,6 +170,16 @@ __device__ __forceinline__ float zoh_ratio(float dA, float w) {
   return dA == 1.0f ? 1.0f : (dA == 0.0f ? g0 : g);
 }
 
+// Orders one wavefront's LDS writes before its later LDS reads of the same locations by other
+// lanes (and reads before later overwrites). The hardware completes a wavefront's LDS operations
+// in issue order; the fences and the barrier keep the compiler from moving them across this
+// point. No instruction is emitted.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // One workgroup = NW wavefronts x 64 channels. Lane l owns channel d0 + l in every wavefront;
 // wavefront w owns states [w*NS, (w+1)*NS), so the B and C values a wavefront needs at a step
 // are the same for all of its lanes: they are read from the LDS tile with wave-uniform
@@ -925,7 +935,8 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
 
   // the recurrence over one half tile in 4-step blocks, each read from LDS one block ahead.
   // The LDS rows were written by other lanes of this wavefront: a wavefront's LDS operations
-  // complete in issue order, so no barrier is needed.
+  // complete in issue order, so no workgroup barrier is needed, only wave_lds_sync between the
+  // phases.
   struct Blk {
     f32x4 du[2];
     f32x4 bq[4], cq[4];  // [state j] 4 steps of B and C
@@ -1069,7 +1080,9 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       prologue_full(cur, hf);
+      wave_lds_sync();  // (delta, u), B and C rows written by other lanes
       recurrence(t0 + hf * kTB, kTB);
+      wave_lds_sync();  // partial readouts written by other lanes; rows free for the next half
       if constexpr (!NOREAD) {
         float xv[CPL][V], zv[CPL][V];
 #pragma unroll
@@ -1078,6 +1091,7 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
           if constexpr (GATE) unpack16<IO>(cur.z[hf][i], zv[i]);
         }
         epilogue(t0 + hf * kTB, kTB, xv, zv, true);
+        wave_lds_sync();  // partials read before the next half overwrites them
       }
       pace();
     }
@@ -1102,8 +1116,13 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
   for (int64_t t0 = t_begin + n_full * kLT; t0 < t_end; t0 += kTB) {
     const int len = (int)min<int64_t>(kTB, t_end - t0);
     prologue_partial(t0, len);
+    wave_lds_sync();
     recurrence(t0, len);
-    if constexpr (!NOREAD) epilogue(t0, len, xk, zk, false);
+    wave_lds_sync();
+    if constexpr (!NOREAD) {
+      epilogue(t0, len, xk, zk, false);
+      wave_lds_sync();
+    }
   }
   __builtin_amdgcn_s_setprio(0);
   if constexpr (MODE == kWaveSummary) {

@@ -263,6 +263,49 @@ def make_batch_entry(cfg: ScanConfig, b: int, nthreads: Optional[int] = None
     return out
 
 
+def make_channel_block(cfg: ScanConfig, b: int, d0: int, d1: int,
+                       nthreads: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Inputs of channels [d0, d1) of batch entry ``b`` alone, regenerated from the streams at
+    their offsets, as the batch-1 problem of ``block_config(cfg, d0, d1)``. The block must lie
+    inside one B/C group and, in head mode, cover whole heads."""
+    gsize = cfg.dim // cfg.ngroups
+    if not (0 <= d0 < d1 <= cfg.dim) or d0 // gsize != (d1 - 1) // gsize:
+        raise ValueError("the channel block must lie inside one B/C group")
+    if cfg.a_mode == "head" and (d0 % cfg.headdim or d1 % cfg.headdim):
+        raise ValueError("the channel block must cover whole heads")
+    L, N, nch = cfg.L, cfg.N, d1 - d0
+    g = d0 // gsize
+    r0, r1 = (d0 // cfg.headdim, d1 // cfg.headdim) if cfg.a_mode == "head" else (d0, d1)
+
+    def part(name, start, count, shape):
+        dd = cfg.dist_of(name)
+        return fill(cfg.seed, TENSOR_IDS[name], dd.kind, dd.p0, dd.p1, count, cfg.dtype_of(name),
+                    start, nthreads).reshape(shape)
+
+    out = {
+        "x": part("x", (b * cfg.dim + d0) * L, nch * L, (1, nch, L)),
+        "delta": part("delta", (b * cfg.delta_rows + r0) * L, (r1 - r0) * L, (1, r1 - r0, L)),
+        "B": part("B", (b * cfg.ngroups + g) * N * L, N * L, (1, 1, N, L)),
+        "C": part("C", (b * cfg.ngroups + g) * N * L, N * L, (1, 1, N, L)),
+    }
+    if cfg.a_mode == "head":
+        out["A"] = part("A", r0, r1 - r0, (r1 - r0,))
+    else:
+        out["A"] = part("A", d0 * N, nch * N, (nch, N))
+    if cfg.has_D:
+        out["D"] = part("D", d0, nch, (nch,))
+    if cfg.gate:
+        out["z"] = part("z", (b * cfg.dim + d0) * L, nch * L, (1, nch, L))
+    if cfg.has_bias:
+        out["delta_bias"] = part("delta_bias", r0, r1 - r0, (r1 - r0,))
+    return out
+
+
+def block_config(cfg: ScanConfig, d0: int, d1: int) -> ScanConfig:
+    """The batch-1, one-group problem that ``make_channel_block`` returns."""
+    return replace(cfg, batch=1, dim=d1 - d0, ngroups=1)
+
+
 def with_shape(cfg: ScanConfig, **kw) -> ScanConfig:
     """A copy of ``cfg`` with some fields replaced (same recipe, different sizes)."""
     return replace(cfg, **kw)

@@ -189,6 +189,43 @@ def test_backward_validation():
     assert call(d, dB=FAKE + (11 << 30)) == -6                                 # dB overlaps dC
     assert call(d, ws=FAKE + (10 << 30)) == -6                                 # workspace overlaps dB
     assert ssm.bwd_workspace_size(ssm.desc_contiguous(2, 64, 0, 16)) == 0
+    # gradients are written with the input strides, so those must give disjoint rows
+    bc = ssm.desc_contiguous(2, 64, 128, 16)
+    bc.B_stride_batch = 0                       # B broadcast over the batch: dB rows collide
+    assert call(bc) == -4
+    bc = ssm.desc_contiguous(2, 64, 128, 16)
+    bc.C_stride_state = 64                      # C rows of consecutive states overlap
+    assert call(bc) == -4
+    ov = ssm.desc_contiguous(2, 64, 128, 16)
+    ov.x_stride_dim = 100                       # overlapping x rows: dx rows collide
+    assert call(ov) == -4
+    ov = ssm.desc_contiguous(2, 64, 128, 16)
+    ov.delta_stride_batch = 0                   # delta broadcast over the batch
+    assert call(ov) == -4
+    ov = ssm.desc_contiguous(2, 64, 128, 16)
+    ov.z_stride_dim = 0
+    assert call(ov, z=FAKE + (12 << 30), dz=FAKE + (13 << 30)) == -4
+    assert call(ov, dx=FAKE + (6 << 30) + 1) == -5  # without z its strides are not checked
+    # the forward call may read such inputs: only y's rows must be disjoint. (A NULL y makes the
+    # call fail after the stride checks, so nothing is launched.)
+    fw = ssm.desc_contiguous(2, 64, 128, 16)
+    fw.B_stride_batch = 0
+    fw.x_stride_dim = 100
+    assert _fwd(fw, y=None) == -1
+
+
+def test_disjoint_rows_accepts_any_dimension_order():
+    """Output rows are checked as a set: a (dim, batch, L) order is as valid as (batch, dim, L),
+    and an interleaving that makes two rows meet is rejected."""
+    d = ssm.desc_contiguous(2, 64, 128, 16)
+    d.y_stride_dim, d.y_stride_batch = 2 * 128, 128      # channel-major rows, disjoint
+    assert _fwd(d, y=None) == -1                         # past the stride checks, no launch
+    d.y_stride_batch = 100                               # batch rows overlap within a channel
+    assert _fwd(d, y=None) == -4
+    d.y_stride_batch, d.y_stride_dim = 64 * 128, 128     # (batch, dim, L) as usual
+    assert _fwd(d, y=None) == -1
+    d.y_stride_batch = 63 * 128 + 127                    # the last row of entry 0 meets entry 1
+    assert _fwd(d, y=None) == -4
 
 
 def test_workspace_size_depends_only_on_shape():

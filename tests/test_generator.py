@@ -2,6 +2,7 @@
 import math
 
 import numpy as np
+import pytest
 
 import ssmgen
 
@@ -110,3 +111,30 @@ def test_batch_entry_is_a_slice_of_the_whole_tensors():
                 assert np.array_equal(arr[0], whole[name][b]), name
             else:
                 assert np.array_equal(arr, whole[name]), name
+
+
+@pytest.mark.parametrize("mode", ["diag", "head"])
+def test_channel_block_equals_slice_of_full_tensors(mode):
+    """A block of channels regenerated alone has exactly the bits of the same slice of the full
+    tensors (the full-size parity tests rely on it)."""
+    cfg = ssmgen.ScanConfig(name="blk", batch=3, dim=256, L=40, N=8, ngroups=2,
+                            headdim=32 if mode == "head" else 1, a_mode=mode, seed=91)
+    full = ssmgen.make_inputs(cfg)
+    b, d0, d1 = 2, 128, 192
+    blk = ssmgen.make_channel_block(cfg, b, d0, d1)
+    sub = ssmgen.block_config(cfg, d0, d1)
+    assert set(blk) == set(sub.shapes())
+    r0, r1 = (d0 // 32, d1 // 32) if mode == "head" else (d0, d1)
+    g = d0 // (cfg.dim // cfg.ngroups)
+    assert np.array_equal(blk["x"][0], full["x"][b, d0:d1])
+    assert np.array_equal(blk["z"][0], full["z"][b, d0:d1])
+    assert np.array_equal(blk["delta"][0], full["delta"][b, r0:r1])
+    assert np.array_equal(blk["B"][0, 0], full["B"][b, g])
+    assert np.array_equal(blk["C"][0, 0], full["C"][b, g])
+    assert np.array_equal(blk["A"], full["A"][r0:r1])
+    assert np.array_equal(blk["D"], full["D"][d0:d1])
+    assert np.array_equal(blk["delta_bias"], full["delta_bias"][r0:r1])
+    for k, shp in sub.shapes().items():
+        assert blk[k].shape == shp, k
+    with pytest.raises(ValueError):
+        ssmgen.make_channel_block(cfg, 0, 100, 140)   # crosses the group boundary at 128

@@ -243,3 +243,54 @@ def test_head_mode_equals_broadcast_channel_mode():
     torch.cuda.synchronize()
     err = oracle.rel_err(yh.cpu().numpy(), yc.cpu().numpy().astype(np.float64))
     assert err < 1e-5
+
+
+LIMITS = [
+    # batch, dim, L, N, headdim, a_mode, io, algorithm
+    (2, 128, 300, 16, 1, "diag", "bf16", "auto"),       # independent-wavefront kernel
+    (2, 128, 300, 16, 1, "diag", "f32", "auto"),        # barrier-synchronised kernel
+    (1, 128, 6000, 16, 1, "diag", "bf16", "auto"),      # split along L into segments
+    (1, 128, 500, 8, 1, "diag", "f32", "auto"),         # two states per wavefront
+    (2, 256, 320, 64, 64, "head", "bf16", "chunked"),   # chunked matrix form (rows of 16 B)
+    (2, 256, 320, 64, 64, "head", "bf16", "recurrent"),
+    (1, 128, 400, 16, 32, "head", "f32", "auto"),
+]
+
+
+@pytest.mark.parametrize("case", LIMITS, ids=lambda c: "-".join(map(str, c)))
+def test_default_rule_limits(case):
+    """The delta * B rule at the method's limits, in one problem: one state (diagonal A) or one
+    head with A = 0, where dA = 1 and the state is a running sum of delta B x; one with
+    A = -400, where exp(delta A) underflows for most steps and the state forgets everything but
+    the current input; B = 0 for every channel of the second group, whose output is then exactly
+    D x silu(z); and raw step sizes drawn over [-30, 30], so that softplus(raw + bias) runs from
+    about 1e-16 (e^v) up to about 28 (v itself), through both branches of its stable form."""
+    batch, dim, L, N, hd, mode, io, algo = case
+    cfg = ssmgen.ScanConfig(name="limits", batch=batch, dim=dim, L=L, N=N, ngroups=2, headdim=hd,
+                            a_mode=mode, io=io, seed=777 + L + N,
+                            dists={"delta": ssmgen.Dist(ssmgen.UNIFORM, -30.0, 30.0)})
+    _say(f"[limits] {case}")
+    inputs = ssmgen.make_inputs(cfg)
+    A = inputs["A"].copy()
+    if mode == "head":
+        A[0], A[1] = 0.0, -400.0
+    else:
+        A[:, 1], A[:, N - 3] = 0.0, -400.0
+    inputs["A"] = A
+    for k in ("B",):
+        arr = inputs[k].copy()
+        arr[:, 1] = 0
+        inputs[k] = arr
+    y = run_hip(device_inputs(inputs), algorithm=algo)
+    torch.cuda.synchronize()
+    yref = oracle_of(cfg, inputs)
+    yg = y_to_f64(y)
+    assert np.isfinite(yg).all()
+    err = oracle.rel_err(yg, yref)
+    _say(f"[limits] {case}: rel err {err:.3e}")
+    assert err <= TOL[cfg.io], f"rel err {err:.3e}"
+    # the second group (B = 0) is the skip path alone; with fp32 io the kernel's D x silu(z)
+    # differs from the oracle's by fp32 rounding only
+    half = dim // 2
+    err_skip = oracle.rel_err(yg[:, half:], yref[:, half:])
+    assert err_skip <= TOL[cfg.io], f"B = 0 group: rel err {err_skip:.3e}"
