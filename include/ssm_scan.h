@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_ABI_VERSION 3
+#define SSM_SCAN_ABI_VERSION 4
 
 typedef enum {
   SSM_OK = 0,
@@ -68,7 +68,9 @@ typedef enum {
                                   output */
   SSM_ERR_WORKSPACE = -7,      /* workspace NULL or smaller than the size query returns */
   SSM_ERR_HIP = -8,            /* the HIP runtime reported an error while enqueueing */
-  SSM_ERR_UNSUPPORTED = -9     /* valid arguments outside what this build implements */
+  SSM_ERR_UNSUPPORTED = -9,    /* valid arguments outside what this build implements */
+  SSM_ERR_SCRATCH_LIMIT = -10  /* ssm_selective_scan_fwd_noalloc: the problem needs more scratch
+                                  than the library's fixed array holds */
 } ssm_status;
 
 typedef enum { SSM_DTYPE_F32 = 0, SSM_DTYPE_BF16 = 1 } ssm_dtype;
@@ -211,6 +213,29 @@ int ssm_selective_scan_bwd(const ssm_scan_desc* desc, const void* x, const void*
                            const float* h0, const void* dy, void* dx, void* ddelta, float* dA,
                            float* dB, float* dC, float* dD, void* dz, float* ddelta_bias,
                            float* dh0, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Size of the fixed device array that ssm_selective_scan_fwd_noalloc uses as its workspace:
+ * 8 MiB, held on every GPU the library runs on until the process ends. Every segment plan with
+ * dstate <= 32 fits it (the million-token scan needs 2.2 MB). */
+#define SSM_NOALLOC_SCRATCH_BYTES (8 << 20)
+
+/* ssm_selective_scan_fwd_ext for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same computation
+ * and results, with the workspace taken from a fixed device array of SSM_NOALLOC_SCRATCH_BYTES
+ * owned by the library instead of a caller buffer. It allocates nothing and calls no
+ * allocating routine. The caller still passes every input and output.
+ *   Arguments, layouts and errors: those of ssm_selective_scan_fwd_ext (`ext` may be NULL).
+ *   Returns SSM_ERR_SCRATCH_LIMIT, before touching the GPU, when
+ *   ssm_selective_scan_workspace_size(desc) exceeds SSM_NOALLOC_SCRATCH_BYTES, and SSM_ERR_HIP
+ *   when the array's device address cannot be found. The first call on a device looks that
+ *   address up (with the stream's device current) and keeps it.
+ *   Every call on a GPU shares that GPU's array and leaves its contents behind; nothing in it
+ *   needs to start at zero. Calls on one stream are ordered; calls whose work overlaps on one
+ *   GPU (two streams, or two host threads without ordering) race on the array. */
+int ssm_selective_scan_fwd_noalloc(const ssm_scan_desc* desc, const void* x, const void* delta,
+                                   const float* A, const void* B, const void* C, const float* D,
+                                   const void* z, const float* delta_bias, int32_t delta_softplus,
+                                   void* y, const ssm_scan_ext* ext, void* stream);
 
 /* SSM_SCAN_ABI_VERSION of the built library. */
 int ssm_abi_version(void);

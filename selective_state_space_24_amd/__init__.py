@@ -27,7 +27,9 @@ STATUS_NAMES = {
     0: "SSM_OK", -1: "SSM_ERR_NULL_ARG", -2: "SSM_ERR_BAD_SHAPE", -3: "SSM_ERR_BAD_DTYPE",
     -4: "SSM_ERR_BAD_STRIDE", -5: "SSM_ERR_MISALIGNED", -6: "SSM_ERR_ALIAS",
     -7: "SSM_ERR_WORKSPACE", -8: "SSM_ERR_HIP", -9: "SSM_ERR_UNSUPPORTED",
+    -10: "SSM_ERR_SCRATCH_LIMIT",
 }
+NOALLOC_SCRATCH_BYTES = 8 << 20  # SSM_NOALLOC_SCRATCH_BYTES
 
 
 class ScanDesc(ctypes.Structure):
@@ -80,6 +82,9 @@ def lib():
         h.ssm_selective_scan_fwd_ext.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
                                                  ctypes.POINTER(ScanExt), vp, sz, vp]
         h.ssm_selective_scan_fwd_ext.restype = ctypes.c_int
+        h.ssm_selective_scan_fwd_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
+                                                     ctypes.POINTER(ScanExt), vp]
+        h.ssm_selective_scan_fwd_noalloc.restype = ctypes.c_int
         h.ssm_selective_state_update.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]
         h.ssm_selective_state_update.restype = ctypes.c_int
         h.ssm_selective_scan_bwd_workspace_size.argtypes = [dp, ctypes.POINTER(sz)]
@@ -135,6 +140,15 @@ def fwd_ext_raw(desc: ScanDesc, x, delta, A, B, C, D, z, delta_bias, delta_softp
     return int(lib().ssm_selective_scan_fwd_ext(
         ctypes.byref(desc), x, delta, A, B, C, D, z, delta_bias, int(bool(delta_softplus)), y,
         ctypes.byref(ext) if ext is not None else None, workspace, int(workspace_bytes), stream))
+
+
+def fwd_noalloc_raw(desc: ScanDesc, x, delta, A, B, C, D, z, delta_bias, delta_softplus: bool,
+                    y, ext: Optional[ScanExt], stream) -> int:
+    """Direct call of ``ssm_selective_scan_fwd_noalloc`` (the workspace is the library's fixed
+    device array); returns the status code without raising."""
+    return int(lib().ssm_selective_scan_fwd_noalloc(
+        ctypes.byref(desc), x, delta, A, B, C, D, z, delta_bias, int(bool(delta_softplus)), y,
+        ctypes.byref(ext) if ext is not None else None, stream))
 
 
 def bwd_workspace_size(desc: ScanDesc) -> int:

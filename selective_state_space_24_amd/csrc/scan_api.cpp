@@ -200,6 +200,7 @@ const char* ssm_status_string(int status) {
     case SSM_ERR_WORKSPACE: return "workspace missing or smaller than the queried size";
     case SSM_ERR_HIP: return "the HIP runtime reported an error";
     case SSM_ERR_UNSUPPORTED: return "valid arguments outside what this build implements";
+    case SSM_ERR_SCRATCH_LIMIT: return "the problem needs more scratch than the fixed array of the allocation-free entry point holds";
     default: return "unknown status";
   }
 }

@@ -33,8 +33,8 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert ssm.abi_version() == 3
-    for code in range(-9, 1):
+    assert ssm.abi_version() == 4
+    for code in range(-10, 1):
         s = ssm.status_string(code)
         assert s and s != "unknown status"
     assert ssm.status_string(-100) == "unknown status"
@@ -258,3 +258,19 @@ def test_torch_front_end_checks_shapes():
         ssm.describe(x.transpose(1, 2).contiguous().transpose(1, 2), x, A, B, B)
     d = ssm.describe(x, torch.zeros(2, 2, 16, dtype=torch.bfloat16), torch.zeros(2), B, B)
     assert d.a_mode == ssm.SSM_A_HEAD and d.headdim == 4
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch_on_the_host():
+    """The allocation-free entry point checks its fixed array's size before touching the GPU:
+    512 segments x 64 channels x 129 floats (dstate 128, L = 2^18) exceed its 8 MiB."""
+    d = ssm.desc_contiguous(1, 64, 1 << 18, 128, headdim=64, io_dtype=ssm.SSM_DTYPE_F32,
+                            a_mode=ssm.SSM_A_HEAD)
+    assert ssm.workspace_size(d) > ssm.NOALLOC_SCRATCH_BYTES
+    args = (FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), FAKE + (4 << 30), None,
+            None, None, True, FAKE + (8 << 30), None, None)
+    assert ssm.fwd_noalloc_raw(d, *args) == -10
+    bad = ssm.desc_contiguous(1, 64, 128, 200)      # argument errors come first
+    assert ssm.fwd_noalloc_raw(bad, *args) == -2
+    # every segment plan with dstate <= 32 fits
+    for (b, dim, L, N) in [(1, 2048, 1 << 20, 16), (1, 64, 1 << 22, 32), (3, 64, 1 << 20, 32)]:
+        assert ssm.workspace_size(ssm.desc_contiguous(b, dim, L, N)) <= ssm.NOALLOC_SCRATCH_BYTES
