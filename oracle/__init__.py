@@ -45,7 +45,7 @@ def load_library(path: str):
     i64, ci = ctypes.c_int64, ctypes.c_int
     lib.ssm_oracle_scan.argtypes = [i64, i64, i64, i64, i64, i64, ci, ci, ci] + [_dp] * 11 + [ci]
     lib.ssm_oracle_scan.restype = ci
-    lib.ssm_oracle_scan_bwd.argtypes = [i64, i64, i64, i64, i64, i64, ci, ci, ci] + [_dp] * 19 + [ci]
+    lib.ssm_oracle_scan_bwd.argtypes = [i64, i64, i64, i64, i64, i64, ci, ci, ci] + [_dp] * 20 + [ci]
     lib.ssm_oracle_scan_bwd.restype = ci
     return lib
 
@@ -121,12 +121,15 @@ def selective_scan(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_sof
 
 def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
                        dy=None, *, headdim: int = 1, head_mode: bool = False, zoh: bool = False,
-                       h0=None, nthreads: Optional[int] = None, lib=None) -> dict:
+                       h0=None, dh_final=None, want_dh0: bool = False,
+                       nthreads: Optional[int] = None, lib=None) -> dict:
     """fp64 gradients of ``selective_scan`` with respect to every input, given ``dy`` (the
-    gradient of y, shaped like x). Returns a dict with dx, ddelta, dA, dB, dC, and dD, dz,
-    ddelta_bias, dh0 for the optional inputs that were given."""
+    gradient of y, shaped like x) and optionally ``dh_final`` (the gradient of the final state,
+    (batch, dim, N)). Returns a dict with dx, ddelta, dA, dB, dC, and dD, dz, ddelta_bias for the
+    optional inputs that were given, and dh0 when h0 was given or ``want_dh0``."""
     x, delta, A, B, C = (as_f64(t) for t in (x, delta, A, B, C))
     D, z, delta_bias, h0, dy = (as_f64(t) for t in (D, z, delta_bias, h0, dy))
+    dh_final = as_f64(dh_final)
     batch, dim, L = x.shape
     _, ngroups, N, _ = B.shape
     out = {"dx": np.empty_like(x), "ddelta": np.empty_like(delta), "dA": np.empty_like(A),
@@ -137,12 +140,12 @@ def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta
         out["dz"] = np.empty_like(z)
     if delta_bias is not None:
         out["ddelta_bias"] = np.empty_like(delta_bias)
-    if h0 is not None:
-        out["dh0"] = np.empty_like(h0)
+    if h0 is not None or want_dh0:
+        out["dh0"] = np.empty((batch, dim, N), dtype=np.float64)
     rc = (lib or _load()).ssm_oracle_scan_bwd(
         batch, dim, L, N, ngroups, headdim, int(head_mode), int(bool(delta_softplus)), int(zoh),
         _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-        _ptr(h0), _ptr(dy), _ptr(out["dx"]), _ptr(out["ddelta"]), _ptr(out["dA"]),
+        _ptr(h0), _ptr(dy), _ptr(dh_final), _ptr(out["dx"]), _ptr(out["ddelta"]), _ptr(out["dA"]),
         _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out.get("dD")), _ptr(out.get("dz")),
         _ptr(out.get("ddelta_bias")), _ptr(out.get("dh0")), nthreads or cpu_threads())
     if rc != 0:

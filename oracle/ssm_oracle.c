@@ -169,13 +169,16 @@ int ssm_oracle_scan(int64_t batch, int64_t dim, int64_t L, int64_t N, int64_t ng
  * The states h_t are recomputed by a forward pass and kept for the whole sequence.
  * Layouts as for the forward; dB, dC are [batch][ngroups][N][L], dA is [dim][N] (or [nheads]),
  * dD [dim], ddelta_bias [dim] (or [nheads]), dh0 [batch][dim][N]. Any of dD, dz, ddelta_bias,
- * dh0 may be NULL (not wanted). Gradients of values shared by several channels (B, C, and
+ * dh0 may be NULL (not wanted). dh_final [batch][dim][N], the gradient of the state after the
+ * last step (nonzero when the sequence continues in a later call), may be NULL (zero); dh0 is
+ * the gradient of the initial state. Gradients of values shared by several channels (B, C, and
  * delta, A, bias in head mode, A, D, bias across the batch) are sums over those channels; the
  * sums over the batch run in batch order, so results do not depend on the thread count.
  * ------------------------------------------------------------------------------------------ */
 typedef struct {
   const oracle_problem* p;
   const double* dy;
+  const double* dh_final;  /* gradient of the state after the last step, or NULL (zero) */
   double *dx, *ddelta, *dB, *dC, *dz, *dh0;
   double *dA_b, *dD_b, *dbias_b;  /* per batch entry: [batch][dim*N or nheads], [batch][dim], ... */
 } bwd_problem;
@@ -217,8 +220,10 @@ static void bwd_channel(const bwd_problem* q, int64_t b, int64_t d, double* hist
     }
   }
 
-  /* reverse pass */
-  for (int64_t n = 0; n < N; ++n) gh[n] = 0.0;
+  /* reverse pass: gh starts as dL/dh_{L-1}, the gradient of the final state (the recurrence
+   * goes on across a call boundary, so a later piece of the sequence hands it back) */
+  for (int64_t n = 0; n < N; ++n)
+    gh[n] = q->dh_final ? q->dh_final[(b * p->dim + d) * N + n] : 0.0;
   double dD = 0.0, dbias = 0.0;
   for (int64_t t = L - 1; t >= 0; --t) {
     const double v = dr[t] + bias;
@@ -300,8 +305,9 @@ int ssm_oracle_scan_bwd(int64_t batch, int64_t dim, int64_t L, int64_t N, int64_
                         const double* x, const double* delta, const double* A, const double* B,
                         const double* C, const double* D, const double* z,
                         const double* delta_bias, const double* h0, const double* dy,
-                        double* dx, double* ddelta, double* dA, double* dB, double* dC,
-                        double* dD, double* dz, double* ddelta_bias, double* dh0, int nthreads) {
+                        const double* dh_final, double* dx, double* ddelta, double* dA,
+                        double* dB, double* dC, double* dD, double* dz, double* ddelta_bias,
+                        double* dh0, int nthreads) {
   if (batch < 0 || dim < 1 || L < 0 || N < 1 || N > 1024 || ngroups < 1 || headdim < 1) return -1;
   if (dim % ngroups || dim % headdim) return -1;
   if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dA || !dB || !dC) return -1;
@@ -317,7 +323,7 @@ int ssm_oracle_scan_bwd(int64_t batch, int64_t dim, int64_t L, int64_t N, int64_
   double* dD_b = calloc((size_t)(batch * dim + 1), sizeof(double));
   double* dbias_b = calloc((size_t)(batch * drows + 1), sizeof(double));
   if (!dA_b || !dD_b || !dbias_b) { free(dA_b); free(dD_b); free(dbias_b); return -1; }
-  bwd_problem q = {&p, dy, dx, ddelta, dB, dC, dz, dh0, dA_b, dD_b, dbias_b};
+  bwd_problem q = {&p, dy, dh_final, dx, ddelta, dB, dC, dz, dh0, dA_b, dD_b, dbias_b};
   if (nthreads < 1) nthreads = 1;
   if (nthreads > 256) nthreads = 256;
   if ((int64_t)nthreads > batch) nthreads = (int)(batch > 0 ? batch : 1);

@@ -7,6 +7,11 @@ than the backward code itself.
                        by torch.autograd
   dx_closed_form       without a gate y = (M + diag D) x with the materialised semiseparable
                        matrix M (Transformers-are-SSMs review page), so dx = (M + diag D)^T dy
+  final_state_fd       central differences of f = sum(dy * y) + sum(dhf * h_final): the gradient
+                       that enters through the final state (a sequence scanned in pieces)
+  two_pieces           a sequence split at step m: the second piece's backward from the state
+                       the forward oracle reaches at m gives dh0, which fed as the first piece's
+                       final-state gradient must reproduce the whole sequence's gradients
 
 Every pin takes ``bwd`` with the signature of ``oracle.selective_scan_bwd`` (and the finite
 differences also ``fwd`` = ``oracle.selective_scan``), so the same pins can run against broken
@@ -165,3 +170,67 @@ def dx_closed_form(bwd, seed=3):
             M += np.diag(np.full(L, p["D"][di]))
             ref[bi, di] = M.T @ dy[bi, di]
     return float(np.max(np.abs(g["dx"] - ref)) / np.max(np.abs(ref)))
+
+
+def final_state_fd(bwd, fwd, seed=5, head_mode=False, zoh=False):
+    """Like finite_differences, with a random gradient of the final state as well."""
+    headdim = 2 if head_mode else 1
+    p = problem(seed, headdim=headdim, head_mode=head_mode, gate=True)
+    r = np.random.default_rng(seed + 200)
+    dy = r.normal(size=p["x"].shape)
+    dhf = r.normal(size=p["h0"].shape)
+    g = bwd(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["delta_bias"], True,
+            dy, headdim=headdim, head_mode=head_mode, zoh=zoh, h0=p["h0"], dh_final=dhf)
+
+    def f(q):
+        y, hT = fwd(q["x"], q["delta"], q["A"], q["B"], q["C"], q["D"], q["z"], q["delta_bias"],
+                    True, headdim=headdim, head_mode=head_mode, zoh=zoh, h0=q["h0"],
+                    return_final_state=True)
+        return float(np.sum(dy * y) + np.sum(dhf * hT))
+    worst = 0.0
+    for name in GRAD_NAMES:
+        base = p[name]
+        fd = np.empty_like(base)
+        for idx in np.ndindex(base.shape):
+            eps = 1e-6 * max(1.0, abs(base[idx]))
+            q = dict(p)
+            up = base.copy(); up[idx] += eps
+            dn = base.copy(); dn[idx] -= eps
+            q[name] = up
+            fu = f(q)
+            q[name] = dn
+            fd[idx] = (fu - f(q)) / (2 * eps)
+        scale = max(1.0, float(np.max(np.abs(fd))))
+        worst = max(worst, float(np.max(np.abs(g["d" + name] - fd))) / scale)
+    return worst
+
+
+def two_pieces(bwd, fwd, seed=6, head_mode=False, zoh=False, m=11):
+    """max relative difference between the whole sequence's gradients and the two pieces'."""
+    headdim = 2 if head_mode else 1
+    p = problem(seed, b=2, d=4, L=25, N=3, headdim=headdim, head_mode=head_mode)
+    dy = np.random.default_rng(seed + 300).normal(size=p["x"].shape)
+    kw = dict(headdim=headdim, head_mode=head_mode, zoh=zoh)
+    cut = lambda a, lo, hi: None if a is None else a[..., lo:hi].copy()
+
+    def piece(lo, hi, h0, dhf):
+        return bwd(cut(p["x"], lo, hi), cut(p["delta"], lo, hi), p["A"], cut(p["B"], lo, hi),
+                   cut(p["C"], lo, hi), p["D"], cut(p["z"], lo, hi), p["delta_bias"], True,
+                   cut(dy, lo, hi), h0=h0, dh_final=dhf, want_dh0=True, **kw)
+    whole = piece(0, 25, p["h0"], None)
+    _, hm = fwd(cut(p["x"], 0, m), cut(p["delta"], 0, m), p["A"], cut(p["B"], 0, m),
+                cut(p["C"], 0, m), p["D"], cut(p["z"], 0, m), p["delta_bias"], True, h0=p["h0"],
+                return_final_state=True, **kw)
+    second = piece(m, 25, hm, None)
+    first = piece(0, m, p["h0"], second["dh0"])
+    worst = 0.0
+    for k in whole:
+        if k in ("dx", "ddelta", "dB", "dC", "dz"):
+            ref = np.concatenate([first[k], second[k]], axis=-1)
+        elif k == "dh0":
+            ref = first[k]
+        else:
+            ref = first[k] + second[k]
+        scale = max(1e-300, float(np.max(np.abs(whole[k]))))
+        worst = max(worst, float(np.max(np.abs(whole[k] - ref))) / scale)
+    return worst

@@ -2,7 +2,8 @@
 import pytest
 
 import oracle
-from oracle_bwd_pins import dx_closed_form, finite_differences, torch_autograd
+from oracle_bwd_pins import (dx_closed_form, final_state_fd, finite_differences,
+                             torch_autograd, two_pieces)
 
 FD_TOL = 2e-6      # central differences with eps = 1e-6 relative: O(eps^2) + rounding / eps
 AUTOGRAD_TOL = 1e-11
@@ -40,3 +41,16 @@ def test_backward_does_not_depend_on_thread_count():
     g3 = oracle.selective_scan_bwd(*args, h0=p["h0"], nthreads=3)
     for k in g1:
         assert np.array_equal(g1[k], g3[k]), k
+
+
+@pytest.mark.parametrize("head_mode,zoh", [(False, False), (True, True)])
+def test_final_state_gradient_matches_finite_differences(head_mode, zoh):
+    err = final_state_fd(oracle.selective_scan_bwd, oracle.selective_scan, head_mode=head_mode,
+                         zoh=zoh)
+    assert err <= FD_TOL, err
+
+
+@pytest.mark.parametrize("head_mode,zoh", [(False, False), (False, True), (True, False)])
+def test_two_pieces_reproduce_the_whole_sequence(head_mode, zoh):
+    assert two_pieces(oracle.selective_scan_bwd, oracle.selective_scan, head_mode=head_mode,
+                      zoh=zoh) <= 1e-12

@@ -46,6 +46,8 @@ BWD_MUTANTS = {
     "bwd_zoh_dBbar_ddelta": ("df_ddelta = Abar;", "df_ddelta = 1.0;"),
     "bwd_dB_without_factor": ("dBg[n * L + t] += gh[n] * xt * f;", "dBg[n * L + t] += gh[n] * xt;"),
     "bwd_gate_not_applied": ("gy = gyr[t] * zr[t] * s;", "gy = gyr[t];"),
+    "bwd_final_state_gradient_dropped": ("gh[n] = q->dh_final ? q->dh_final[(b * p->dim + d) * N + n] : 0.0;",
+                                         "gh[n] = 0.0;"),
 }
 
 
@@ -86,6 +88,8 @@ def test_backward_mutant_is_caught(name, src, tmp_path):
             for (h, z, sp, g) in [(False, False, True, True), (False, True, True, True),
                                   (True, False, True, True)]]
     errs.append(BP.dx_closed_form(bwd))
+    errs.append(BP.final_state_fd(bwd, fwd))
+    errs.append(BP.two_pieces(bwd, fwd))
     assert max(errs) > 1e-4, f"backward mutant {name} passed every pin: {errs}"
 
 
