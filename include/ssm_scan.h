@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_ABI_VERSION 4
+#define SSM_SCAN_ABI_VERSION 5
 
 typedef enum {
   SSM_OK = 0,
@@ -188,31 +188,55 @@ int ssm_selective_state_update(const ssm_scan_desc* desc, float* state, const vo
  * seqlen is 0). The value depends only on the descriptor. */
 int ssm_selective_scan_bwd_workspace_size(const ssm_scan_desc* desc, size_t* bytes);
 
-/* Gradients of ssm_selective_scan_fwd (delta * B discretisation) with respect to every input,
- * given dy, the gradient of its output y: the backward half of training the layer (page
- * "NL-345", §1 "Hardware-aware Algorithm": the states are recomputed, not stored).
+/* Gradients of ssm_selective_scan_fwd with respect to every input, given dy, the gradient of its
+ * output y: the backward half of training the layer (page "NL-345", §1 "Hardware-aware
+ * Algorithm": the states are recomputed from sparse checkpoints, not stored).
  *   inputs   : the forward call's desc, x, delta, A, B, C, D, z, delta_bias, delta_softplus and
  *              h0 (nullable initial state, (batch, dim, dstate) fp32 contiguous)
  *   dy       : io dtype with the strides of y
  *   dx       : io dtype, strides of x;  ddelta: io dtype, strides of delta (gradient of the raw
- *              delta, before bias and softplus);  dz: io dtype, strides of z (required when z is
- *              given, ignored otherwise)
+ *              delta, before bias and softplus; (batch, nheads, L) in A_HEAD mode);  dz: io
+ *              dtype, strides of z (required when z is given, ignored otherwise)
  *   dB, dC   : fp32 with the element strides of B and C (summed over the channels of a group)
- *   dA       : (dim, dstate) fp32;  dD, ddelta_bias: (dim,) fp32, nullable (not computed);
- *              summed over the batch
+ *   dA       : fp32 shaped like A ((dim, dstate), or (nheads,) in A_HEAD mode);  dD (dim,) and
+ *              ddelta_bias (shaped like delta_bias), fp32, nullable (not computed); summed over
+ *              the batch (and over each head's channels in A_HEAD mode)
  *   dh0      : nullable, (batch, dim, dstate) fp32: the gradient of the initial state
  *   workspace: at least ssm_selective_scan_bwd_workspace_size bytes, 4-byte aligned
- * Supported: A_DIAG mode with dstate <= 16 (SSM_ERR_UNSUPPORTED otherwise). Outputs must not
- * overlap any input or each other. Because dx, ddelta, dz, dB and dC are written with the
- * strides of x, delta, z, B and C, those strides must give disjoint rows (as y's must in the
- * forward call; a stride-0 broadcast of B, say, returns SSM_ERR_BAD_STRIDE). Results are
- * deterministic (fixed-order reductions). */
+ * Every a_mode, io dtype and dstate (up to 128) is supported. Outputs must not overlap any input
+ * or each other. Because dx, ddelta, dz, dB and dC are written with the strides of x, delta, z,
+ * B and C, those strides must give disjoint rows (as y's must in the forward call; a stride-0
+ * broadcast of B, say, returns SSM_ERR_BAD_STRIDE). Results are deterministic (fixed-order
+ * reductions). This is the delta * B rule with no final-state gradient; see
+ * ssm_selective_scan_bwd_ext for the others. */
 int ssm_selective_scan_bwd(const ssm_scan_desc* desc, const void* x, const void* delta,
                            const float* A, const void* B, const void* C, const float* D,
                            const void* z, const float* delta_bias, int32_t delta_softplus,
                            const float* h0, const void* dy, void* dx, void* ddelta, float* dA,
                            float* dB, float* dC, float* dD, void* dz, float* ddelta_bias,
                            float* dh0, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Options of ssm_selective_scan_bwd_ext. A zero-filled struct gives ssm_selective_scan_bwd. */
+typedef struct ssm_bwd_ext {
+  int32_t discretization; /* the ssm_discretization of the forward call (the zero-order hold
+                             differentiates B_bar = (exp(delta A) - 1) / A B) */
+  int32_t reserved;       /* 0 */
+  const float* dh_final;  /* nullable: gradient of the forward call's final state (batch, dim,
+                             dstate) fp32 contiguous, for a sequence scanned in pieces; NULL is
+                             a zero gradient */
+} ssm_bwd_ext;
+
+/* ssm_selective_scan_bwd with the options above (`ext` may be NULL): the gradients of
+ * ssm_selective_scan_fwd_ext with the given discretisation, including the gradient that flows
+ * in through its final state. Arguments, layouts and errors as ssm_selective_scan_bwd. With
+ * batch or seqlen 0 the parameter gradients are zero and dh0 receives dh_final (or zeros). */
+int ssm_selective_scan_bwd_ext(const ssm_scan_desc* desc, const void* x, const void* delta,
+                               const float* A, const void* B, const void* C, const float* D,
+                               const void* z, const float* delta_bias, int32_t delta_softplus,
+                               const float* h0, const void* dy, void* dx, void* ddelta,
+                               float* dA, float* dB, float* dC, float* dD, void* dz,
+                               float* ddelta_bias, float* dh0, const ssm_bwd_ext* ext,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Size of the fixed device array that ssm_selective_scan_fwd_noalloc uses as its workspace:
  * 8 MiB, held on every GPU the library runs on until the process ends. Every segment plan with

@@ -55,6 +55,12 @@ class ScanExt(ctypes.Structure):
                 ("h0", ctypes.c_void_p), ("h_final", ctypes.c_void_p)]
 
 
+class BwdExt(ctypes.Structure):
+    """Mirror of ``ssm_bwd_ext``."""
+    _fields_ = [("discretization", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("dh_final", ctypes.c_void_p)]
+
+
 class ScanError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -91,6 +97,9 @@ def lib():
         h.ssm_selective_scan_bwd_workspace_size.restype = ctypes.c_int
         h.ssm_selective_scan_bwd.argtypes = [dp] + [vp] * 8 + [i32] + [vp] * 11 + [vp, sz, vp]
         h.ssm_selective_scan_bwd.restype = ctypes.c_int
+        h.ssm_selective_scan_bwd_ext.argtypes = ([dp] + [vp] * 8 + [i32] + [vp] * 11 +
+                                                 [ctypes.POINTER(BwdExt), vp, sz, vp])
+        h.ssm_selective_scan_bwd_ext.restype = ctypes.c_int
         h.ssm_status_string.argtypes = [ctypes.c_int]
         h.ssm_status_string.restype = ctypes.c_char_p
         h.ssm_abi_version.argtypes = []
@@ -166,6 +175,16 @@ def bwd_raw(desc: ScanDesc, x, delta, A, B, C, D, z, delta_bias, delta_softplus:
     return int(lib().ssm_selective_scan_bwd(
         ctypes.byref(desc), x, delta, A, B, C, D, z, delta_bias, int(bool(delta_softplus)), h0, dy,
         dx, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0, workspace, int(workspace_bytes), stream))
+
+
+def bwd_ext_raw(desc: ScanDesc, x, delta, A, B, C, D, z, delta_bias, delta_softplus: bool, h0,
+                dy, dx, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0, ext: Optional[BwdExt],
+                workspace, workspace_bytes: int, stream) -> int:
+    """Direct call of ``ssm_selective_scan_bwd_ext``; returns the status code without raising."""
+    return int(lib().ssm_selective_scan_bwd_ext(
+        ctypes.byref(desc), x, delta, A, B, C, D, z, delta_bias, int(bool(delta_softplus)), h0, dy,
+        dx, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0,
+        ctypes.byref(ext) if ext is not None else None, workspace, int(workspace_bytes), stream))
 
 
 def state_update_raw(desc: ScanDesc, state, x, delta, A, B, C, D, z, delta_bias,
@@ -329,13 +348,15 @@ def selective_state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=
 
 
 def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
-                       dy=None, *, h0=None, want_dh0=False, workspace=None, stream=None) -> dict:
-    """Gradients of ``selective_scan_fwd`` (delta * B rule) for dy, the gradient of y. Returns a
-    dict: dx, ddelta, dz (io dtype, like x, delta, z), dA, dB, dC, dD, ddelta_bias (float32) and
-    dh0 when ``want_dh0``. See ``ssm_selective_scan_bwd``."""
+                       dy=None, *, h0=None, want_dh0=False, zoh: bool = False, dh_final=None,
+                       workspace=None, stream=None) -> dict:
+    """Gradients of ``selective_scan_fwd`` for dy, the gradient of y (and ``dh_final``, the
+    gradient of its final state, if given). ``zoh`` selects the zero-order-hold rule of the
+    forward call. Returns a dict: dx, ddelta, dz (io dtype, like x, delta, z), dA (like A), dB,
+    dC, dD, ddelta_bias (float32) and dh0 when ``want_dh0``. See ``ssm_selective_scan_bwd_ext``."""
     import torch
     desc = describe(x, delta, A, B, C, z, dy)
-    for name, t in (("D", D), ("delta_bias", delta_bias), ("h0", h0)):
+    for name, t in (("D", D), ("delta_bias", delta_bias), ("h0", h0), ("dh_final", dh_final)):
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
             raise TypeError(f"{name} must be a contiguous float32 tensor")
     g = {"dx": torch.empty_like(x), "ddelta": torch.empty_like(delta),
@@ -363,11 +384,14 @@ def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     sp = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
-    rc = bwd_raw(desc, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                 _ptr(delta_bias), delta_softplus, _ptr(h0), _ptr(dy), _ptr(g["dx"]),
-                 _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g.get("dD")),
-                 _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")), _ptr(g.get("dh0")),
-                 _ptr(workspace) if need else None, need, sp)
+    if dh_final is not None and tuple(dh_final.shape) != (desc.batch, desc.dim, desc.dstate):
+        raise ValueError("dh_final must be (batch, dim, N)")
+    ext = BwdExt(SSM_DISC_ZOH if zoh else SSM_DISC_DELTA_B, 0, _ptr(dh_final))
+    rc = bwd_ext_raw(desc, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                     _ptr(delta_bias), delta_softplus, _ptr(h0), _ptr(dy), _ptr(g["dx"]),
+                     _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+                     _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")),
+                     _ptr(g.get("dh0")), ext, _ptr(workspace) if need else None, need, sp)
     if rc != SSM_OK:
         raise ScanError(rc, "ssm_selective_scan_bwd")
     return g

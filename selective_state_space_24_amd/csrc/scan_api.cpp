@@ -150,19 +150,28 @@ size_t workspace_bytes_for(const ssm_scan_desc* d, const Plan& p) {
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Workspace of the backward pass: checkpoints (batch, ntiles, N, dim) every kCkptStep steps, the dB
-// and dC partials
-// (batch, groups_per_batch, N, L), the dA partials (batch, dim, N), dD and dbias partials
-// (batch, dim); fp32, each section 256-byte aligned.
+// Workspace of the backward pass: checkpoints (batch, ntiles, N, dim) every kCkptStep steps, the
+// dB and dC partials (batch, groups_per_batch, N, L), the dA partials (batch, dim, N), dD and
+// dbias partials (batch, dim); in head mode also ddelta summed over runs of gcd(headdim, 64)
+// channels (batch, dim / span, L) and the bias-gradient partials (nheads, batch, chunks). fp32,
+// each section 256-byte aligned.
 struct BwdLayout {
-  size_t ckpt, dB, dC, dA, dD, dbias, total;
+  size_t ckpt, dB, dC, dA, dD, dbias, ddl, dbh, total;
+  int64_t span;
 };
+
+int64_t gcd64(int64_t a, int64_t b) {
+  while (b) { const int64_t t = a % b; a = b; b = t; }
+  return a;
+}
 
 BwdLayout bwd_layout(const ssm_scan_desc* d) {
   const size_t ntiles = (size_t)((d->seqlen + ssm::kCkptStep - 1) / ssm::kCkptStep);
   const size_t gpb = (size_t)((d->dim + ssm::kChannelsPerGroup - 1) / ssm::kChannelsPerGroup);
   const size_t B = (size_t)d->batch, D = (size_t)d->dim, N = (size_t)d->dstate, L = (size_t)d->seqlen;
+  const bool head = d->a_mode == SSM_A_HEAD;
   BwdLayout l;
+  l.span = head ? gcd64(d->headdim, ssm::kChannelsPerGroup) : 1;
   size_t off = 0;
   l.ckpt = off; off += align256(B * D * ntiles * N * 4);
   l.dB = off; off += align256(B * gpb * N * L * 4);
@@ -170,6 +179,13 @@ BwdLayout bwd_layout(const ssm_scan_desc* d) {
   l.dA = off; off += align256(B * D * N * 4);
   l.dD = off; off += align256(B * D * 4);
   l.dbias = off; off += align256(B * D * 4);
+  l.ddl = off;
+  if (head) off += align256(B * (D / (size_t)l.span) * L * 4);
+  l.dbh = off;
+  if (head) {
+    const size_t chunks = (L + ssm::kHeadDeltaChunk - 1) / ssm::kHeadDeltaChunk;
+    off += align256((D / (size_t)d->headdim) * B * chunks * 4);
+  }
   l.total = (B == 0 || L == 0) ? 0 : off;
   return l;
 }
@@ -446,40 +462,47 @@ int ssm_selective_scan_bwd_workspace_size(const ssm_scan_desc* desc, size_t* byt
   return SSM_OK;
 }
 
-int ssm_selective_scan_bwd(const ssm_scan_desc* desc, const void* x, const void* delta,
-                           const float* A, const void* B, const void* C, const float* D,
-                           const void* z, const float* delta_bias, int32_t delta_softplus,
-                           const float* h0, const void* dy, void* dx, void* ddelta, float* dA,
-                           float* dB, float* dC, float* dD, void* dz, float* ddelta_bias,
-                           float* dh0, void* workspace, size_t workspace_bytes, void* stream) {
+int ssm_selective_scan_bwd_ext(const ssm_scan_desc* desc, const void* x, const void* delta,
+                               const float* A, const void* B, const void* C, const float* D,
+                               const void* z, const float* delta_bias, int32_t delta_softplus,
+                               const float* h0, const void* dy, void* dx, void* ddelta,
+                               float* dA, float* dB, float* dC, float* dD, void* dz,
+                               float* ddelta_bias, float* dh0, const ssm_bwd_ext* ext,
+                               void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_desc(desc);
   if (rc != SSM_OK) return rc;
   const ssm_scan_desc& d = *desc;
-  if (d.a_mode != SSM_A_DIAG || d.dstate > 16) return SSM_ERR_UNSUPPORTED;
+  const int32_t disc = ext ? ext->discretization : SSM_DISC_DELTA_B;
+  if (disc != SSM_DISC_DELTA_B && disc != SSM_DISC_ZOH) return SSM_ERR_BAD_DTYPE;
+  const float* dhfin = ext ? ext->dh_final : nullptr;
+  const bool head = d.a_mode == SSM_A_HEAD;
   const int64_t ch_per_group = d.dim / d.ngroups;
   if (d.ngroups > 1 && ch_per_group % ssm::kChannelsPerGroup != 0) return SSM_ERR_UNSUPPORTED;
   if (!dA) return SSM_ERR_NULL_ARG;
   if (z && !dz) return SSM_ERR_NULL_ARG;
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   const size_t es = d.io_dtype == SSM_DTYPE_BF16 ? 2 : 4;
-  const size_t a_bytes = (size_t)d.dim * d.dstate * 4;
+  const int64_t nheads = d.dim / d.headdim;
+  const int64_t drows = head ? nheads : d.dim;
+  const int64_t a_count = head ? nheads : d.dim * d.dstate;
+  const size_t a_bytes = (size_t)a_count * 4;
   const size_t state_bytes = (size_t)d.batch * d.dim * d.dstate * 4;
   if (d.batch == 0 || d.seqlen == 0) {
-    // nothing depends on the parameters or on h0: their gradients are zero
+    // nothing depends on the parameters; the initial state's gradient is the final state's
     if (!aligned(dA, 4) || (dD && !aligned(dD, 4)) || (ddelta_bias && !aligned(ddelta_bias, 4)) ||
-        (dh0 && !aligned(dh0, 4)))
+        (dh0 && !aligned(dh0, 4)) || (dhfin && !aligned(dhfin, 4)))
       return SSM_ERR_MISALIGNED;
-    hipError_t e = ssm::launch_state_copy(nullptr, dA, d.dim * d.dstate, hs);
+    if (dh0 && dhfin && overlaps(dh0, state_bytes, dhfin, state_bytes)) return SSM_ERR_ALIAS;
+    hipError_t e = ssm::launch_state_copy(nullptr, dA, a_count, hs);
     if (e == hipSuccess && dD) e = ssm::launch_state_copy(nullptr, dD, d.dim, hs);
-    if (e == hipSuccess && ddelta_bias) e = ssm::launch_state_copy(nullptr, ddelta_bias, d.dim, hs);
-    if (e == hipSuccess && dh0) e = ssm::launch_state_copy(nullptr, dh0, (int64_t)(state_bytes / 4), hs);
+    if (e == hipSuccess && ddelta_bias) e = ssm::launch_state_copy(nullptr, ddelta_bias, drows, hs);
+    if (e == hipSuccess && dh0) e = ssm::launch_state_copy(dhfin, dh0, (int64_t)(state_bytes / 4), hs);
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
   }
   if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dB || !dC) return SSM_ERR_NULL_ARG;
   // dx, ddelta, dz, dB and dC are written with the strides of x, delta, z, B and C: inputs may
   // overlap themselves (a broadcast B, say), gradients may not
   {
-    const int64_t drows = d.a_mode == SSM_A_HEAD ? d.dim / d.headdim : d.dim;
     const int64_t nbc[] = {d.batch, d.ngroups, d.dstate};
     const int64_t sB[] = {d.B_stride_batch, d.B_stride_group, d.B_stride_state};
     const int64_t sC[] = {d.C_stride_batch, d.C_stride_group, d.C_stride_state};
@@ -493,12 +516,12 @@ int ssm_selective_scan_bwd(const ssm_scan_desc* desc, const void* x, const void*
   const void* io_ptrs[] = {x, delta, B, C, z, dy, dx, ddelta, dz};
   for (const void* q : io_ptrs)
     if (q && !aligned(q, es)) return SSM_ERR_MISALIGNED;
-  const void* f32_ptrs[] = {A, D, delta_bias, h0, dA, dB, dC, dD, ddelta_bias, dh0, workspace};
+  const void* f32_ptrs[] = {A, D, delta_bias, h0, dA, dB, dC, dD, ddelta_bias, dh0, dhfin, workspace};
   for (const void* q : f32_ptrs)
     if (q && !aligned(q, 4)) return SSM_ERR_MISALIGNED;
 
   const size_t x_bytes = (size_t)extent3(d.batch, d.dim, d.seqlen, d.x_stride_batch, d.x_stride_dim) * es;
-  const size_t dl_bytes = (size_t)extent3(d.batch, d.dim, d.seqlen, d.delta_stride_batch, d.delta_stride_dim) * es;
+  const size_t dl_bytes = (size_t)extent3(d.batch, drows, d.seqlen, d.delta_stride_batch, d.delta_stride_dim) * es;
   const size_t z_bytes = (size_t)extent3(d.batch, d.dim, d.seqlen, d.z_stride_batch, d.z_stride_dim) * es;
   const size_t y_bytes = (size_t)extent3(d.batch, d.dim, d.seqlen, d.y_stride_batch, d.y_stride_dim) * es;
   const int64_t Bext = extent4(d.batch, d.ngroups, d.dstate, d.seqlen, d.B_stride_batch, d.B_stride_group, d.B_stride_state);
@@ -506,19 +529,22 @@ int ssm_selective_scan_bwd(const ssm_scan_desc* desc, const void* x, const void*
   const BwdLayout lay = bwd_layout(desc);
   if (!workspace || workspace_bytes < lay.total) return SSM_ERR_WORKSPACE;
 
-  const void* in_ptrs[] = {x, delta, A, B, C, D, z, delta_bias, h0, dy};
+  const void* in_ptrs[] = {x, delta, A, B, C, D, z, delta_bias, h0, dy, dhfin};
   const size_t in_bytes[] = {x_bytes, dl_bytes, a_bytes, (size_t)Bext * es, (size_t)Cext * es,
                              D ? (size_t)d.dim * 4 : 0, z ? z_bytes : 0,
-                             delta_bias ? (size_t)d.dim * 4 : 0, h0 ? state_bytes : 0, y_bytes};
+                             delta_bias ? (size_t)drows * 4 : 0, h0 ? state_bytes : 0, y_bytes,
+                             dhfin ? state_bytes : 0};
+  constexpr int kIn = 11;
   const void* out_ptrs[] = {dx, ddelta, dz, dA, dB, dC, dD, ddelta_bias, dh0, workspace};
   const size_t out_bytes[] = {x_bytes, dl_bytes, dz ? z_bytes : 0, a_bytes, (size_t)Bext * 4,
                               (size_t)Cext * 4, dD ? (size_t)d.dim * 4 : 0,
-                              ddelta_bias ? (size_t)d.dim * 4 : 0, dh0 ? state_bytes : 0,
+                              ddelta_bias ? (size_t)drows * 4 : 0, dh0 ? state_bytes : 0,
                               lay.total};
-  for (int i = 0; i < 10; ++i) {
-    for (int j = 0; j < 10; ++j)
+  constexpr int kOut = 10;
+  for (int i = 0; i < kOut; ++i) {
+    for (int j = 0; j < kIn; ++j)
       if (overlaps(out_ptrs[i], out_bytes[i], in_ptrs[j], in_bytes[j])) return SSM_ERR_ALIAS;
-    for (int j = i + 1; j < 10; ++j)
+    for (int j = i + 1; j < kOut; ++j)
       if (overlaps(out_ptrs[i], out_bytes[i], out_ptrs[j], out_bytes[j])) return SSM_ERR_ALIAS;
   }
 
@@ -539,6 +565,7 @@ int ssm_selective_scan_bwd(const ssm_scan_desc* desc, const void* x, const void*
   p.seg_len = d.seqlen;
   p.nseg = 1;
   p.softplus = delta_softplus ? 1 : 0;
+  p.zoh = disc == SSM_DISC_ZOH ? 1 : 0;
   p.ntiles = (d.seqlen + ssm::kCkptStep - 1) / ssm::kCkptStep;
   char* ws = static_cast<char*>(workspace);
   p.ckpt = reinterpret_cast<float*>(ws + lay.ckpt);
@@ -567,13 +594,30 @@ int ssm_selective_scan_bwd(const ssm_scan_desc* desc, const void* x, const void*
   q.pair_out = (p.vec_io && aligned(dx, 2 * es) && aligned(ddelta, 2 * es) &&
                 (!dz || aligned(dz, 2 * es))) ? 1 : 0;
   q.dA = dA; q.dB = dB; q.dC = dC; q.dD = dD; q.dbias = ddelta_bias; q.dh0 = dh0;
+  q.dhfin = dhfin;
+  q.head = head ? 1 : 0;
+  q.head_ns = ssm::bwd_wide_states_per_lane(d.dstate);
+  q.span = lay.span;
   q.dB_part = reinterpret_cast<float*>(ws + lay.dB);
   q.dC_part = reinterpret_cast<float*>(ws + lay.dC);
   q.dA_part = reinterpret_cast<float*>(ws + lay.dA);
   q.dD_part = reinterpret_cast<float*>(ws + lay.dD);
   q.dbias_part = reinterpret_cast<float*>(ws + lay.dbias);
+  q.ddl_part = reinterpret_cast<float*>(ws + lay.ddl);
+  q.dbias_hpart = reinterpret_cast<float*>(ws + lay.dbh);
   const hipError_t e = ssm::launch_bwd(q, d.io_dtype == SSM_DTYPE_BF16, hs);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+int ssm_selective_scan_bwd(const ssm_scan_desc* desc, const void* x, const void* delta,
+                           const float* A, const void* B, const void* C, const float* D,
+                           const void* z, const float* delta_bias, int32_t delta_softplus,
+                           const float* h0, const void* dy, void* dx, void* ddelta, float* dA,
+                           float* dB, float* dC, float* dD, void* dz, float* ddelta_bias,
+                           float* dh0, void* workspace, size_t workspace_bytes, void* stream) {
+  return ssm_selective_scan_bwd_ext(desc, x, delta, A, B, C, D, z, delta_bias, delta_softplus, h0,
+                                    dy, dx, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0, nullptr,
+                                    workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

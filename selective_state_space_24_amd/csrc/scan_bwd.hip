@@ -17,9 +17,10 @@
 //      wave-private LDS, giving one partial per workgroup;
 //   3. reduce kernels add the partials: dB, dC over the workgroups of a batch entry's group,
 //      dA, dD, dbias over the batch, in a fixed order (results are deterministic).
-// The LDS use (about 74 KB) lets two workgroups share a CU. Arithmetic: fp32. Supported:
-// diagonal A, dstate <= 16, delta * B discretisation.
-#include "scan_kernels.h"
+// The LDS use (about 74 KB) lets two workgroups share a CU. Arithmetic: fp32. This kernel takes
+// diagonal A, dstate <= 16 and the delta * B rule; scan_bwd_wide.h takes every other case and
+// shares the reductions below.
+#include "scan_bwd_common.h"
 
 namespace ssm {
 
@@ -32,38 +33,6 @@ constexpr int kRedStride = kSub + 1;
 // floats per column of the dB/dC lane-sum scratch (64 lanes, padded so that the 16-byte column
 // reads of consecutive columns start in different bank groups)
 constexpr int kSumStride = 64 + 4;
-
-// v of lane l plus v of lane l ^ off (the same sum in both lanes): off 16 and 32 by the
-// lane-swap instructions, which leave {v(l), v(l ^ off)} in the two results in every lane (no
-// LDS round trip); smaller offsets by a permute
-__device__ __forceinline__ float xor_sum(float v, int off) {
-  const uint32_t u = __float_as_uint(v);
-  if (off == 32) {
-    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  }
-  if (off == 16) {
-    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  }
-  return v + __shfl_xor(v, off);
-}
-
-// sigmoid(v) from delta = softplus(v): e^delta = 1 + e^v gives sigmoid(v) = 1 - e^-delta. For
-// small delta the series delta (1 - delta/2 + delta^2/6 - delta^3/24) avoids the cancellation
-// (its first dropped term is below 1e-7 relative at delta = 0.1).
-__device__ __forceinline__ float sigmoid_from_softplus(float dl) {
-  const float series = dl * fmaf(dl, fmaf(dl, fmaf(dl, -1.0f / 24.0f, 1.0f / 6.0f), -0.5f), 1.0f);
-  return dl < 0.1f ? series : 1.0f - __builtin_amdgcn_exp2f(-dl * kLog2e);
-}
-
-// two consecutive elements (a, b) at p, which holds a pair: one 4-byte (bf16) or 8-byte store
-__device__ __forceinline__ void store_pair(bf16_bits* p, float a, float b) {
-  *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(a, b);
-}
-__device__ __forceinline__ void store_pair(float* p, float a, float b) {
-  *reinterpret_cast<float2*>(p) = make_float2(a, b);
-}
 
 template <typename IO, int NS, bool GATE>
 __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
@@ -122,7 +91,10 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
 
   float gh[NS], da[NS];
 #pragma unroll
-  for (int j = 0; j < NS; ++j) gh[j] = da[j] = 0.0f;
+  for (int j = 0; j < NS; ++j) {
+    gh[j] = (q.dhfin && live && n0 + j < p.N) ? q.dhfin[(b * p.dim + d) * p.N + n0 + j] : 0.0f;
+    da[j] = 0.0f;
+  }
 
   for (int64_t tile = (L + kBT - 1) / kBT - 1; tile >= 0; --tile) {
     const int64_t t0 = tile * kBT;
@@ -396,6 +368,55 @@ __global__ void __launch_bounds__(256) bwd_reduce_params(const BwdParams q) {
   }
 }
 
+// Head mode: dA[h] (sum over batch entries, the head's channels and the wavefronts' state
+// blocks), dbias[h] (sum over batch entries and chunks) and dD[d] (sum over batch entries).
+__global__ void __launch_bounds__(256) bwd_reduce_params_head(const BwdParams q) {
+  const ScanParams& p = q.f;
+  const int64_t nheads = p.dim / p.headdim;
+  const int64_t nchunks = (p.L + kHeadDeltaChunk - 1) / kHeadDeltaChunk;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < p.dim && q.dD) {
+    float s = 0.0f;
+    for (int64_t b = 0; b < p.batch; ++b) s += q.dD_part[b * p.dim + i];
+    q.dD[i] = s;
+  }
+  if (i < nheads) {
+    float sa = 0.0f;
+    for (int64_t b = 0; b < p.batch; ++b)
+      for (int64_t d = i * p.headdim; d < (i + 1) * p.headdim; ++d)
+        for (int64_t n = 0; n < p.N; n += q.head_ns) sa += q.dA_part[(b * p.dim + d) * p.N + n];
+    q.dA[i] = sa;
+    if (q.dbias) {
+      float sb = 0.0f;
+      for (int64_t b = 0; b < p.batch; ++b)
+        for (int64_t c = 0; c < nchunks; ++c) sb += q.dbias_hpart[(i * p.batch + b) * nchunks + c];
+      q.dbias[i] = sb;
+    }
+  }
+}
+
+// dB, dC (over the workgroups of each batch entry's group) and the parameter gradients (over
+// the batch; in head mode also over each head's channels), all in a fixed order
+static hipError_t bwd_reductions(const BwdParams& q, hipStream_t stream) {
+  const ScanParams& p = q.f;
+  const int64_t nbc = p.batch * p.ngroups * p.N * p.L;
+  const int64_t bbc = (nbc + 255) / 256;
+  const unsigned gbc = (unsigned)(bbc < 65536 ? bbc : 65536);
+  hipLaunchKernelGGL(bwd_reduce_bc, dim3(gbc > 0 ? gbc : 1), dim3(256), 0, stream, q);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (q.head) {
+    hipLaunchKernelGGL(bwd_reduce_params_head, dim3((unsigned)((p.dim + 255) / 256)), dim3(256),
+                       0, stream, q);
+    return hipGetLastError();
+  }
+  const int64_t np = p.dim * p.N;
+  const int64_t bp = (np + 255) / 256;
+  hipLaunchKernelGGL(bwd_reduce_params, dim3((unsigned)(bp < 65536 ? bp : 65536)), dim3(256), 0,
+                     stream, q);
+  return hipGetLastError();
+}
+
 template <typename IO, int NS>
 static hipError_t bwd_cfg(const BwdParams& q, hipStream_t stream) {
   const ScanParams& p = q.f;
@@ -434,17 +455,7 @@ static hipError_t bwd_cfg(const BwdParams& q, hipStream_t stream) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // 3. reductions
-  const int64_t nbc = p.batch * p.ngroups * p.N * p.L;
-  const int64_t bbc = (nbc + 255) / 256;
-  const unsigned gbc = (unsigned)(bbc < 65536 ? bbc : 65536);
-  hipLaunchKernelGGL(bwd_reduce_bc, dim3(gbc > 0 ? gbc : 1), dim3(256), 0, stream, q);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t np = p.dim * p.N;
-  const int64_t bp = (np + 255) / 256;
-  hipLaunchKernelGGL(bwd_reduce_params, dim3((unsigned)(bp < 65536 ? bp : 65536)), dim3(256), 0,
-                     stream, q);
-  return hipGetLastError();
+  return bwd_reductions(q, stream);
 }
 
 template <typename IO>
@@ -456,6 +467,12 @@ static hipError_t bwd_n(const BwdParams& q, hipStream_t stream) {
 }
 
 hipError_t launch_bwd(const BwdParams& q, bool bf16, hipStream_t stream) {
+  // one A per head, dstate above 16 or the zero-order hold: the kernel of scan_bwd_wide.h
+  if (q.head || q.f.zoh || q.f.N > 16) {
+    const hipError_t e = bf16 ? launch_bwd_wide_bf16(q, stream) : launch_bwd_wide_f32(q, stream);
+    if (e != hipSuccess) return e;
+    return bwd_reductions(q, stream);
+  }
   return bf16 ? bwd_n<bf16_bits>(q, stream) : bwd_n<float>(q, stream);
 }
 

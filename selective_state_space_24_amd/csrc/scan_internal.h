@@ -13,6 +13,7 @@ constexpr int kTB = 32;       // time steps per compute tile
 constexpr int kLT = 2 * kTB;  // time steps per load tile (128 bytes of bf16 per row); segments
                               // along L start at multiples of it
 constexpr int kCkptStep = 8;  // steps between the states the backward checkpoint pass stores
+constexpr int kHeadDeltaChunk = 1024;  // steps per partial sum of the head-mode bias gradient
 
 constexpr int64_t kCUs = 256;           // compute units of an MI355X
 constexpr int64_t kTargetWaves = 2048;  // about two resident wavefronts per SIMD (256 CUs)
@@ -98,8 +99,22 @@ struct BwdParams {
   float* dbias_part;
   int32_t pair_out;  // dx, ddelta, dz allow stores of two consecutive elements (aligned to 2
                      // elements, with the strides of x, delta, z)
+  int32_t head;      // one A per head (the forward's a_mode SSM_A_HEAD)
+  int32_t head_ns;   // head mode: states per lane of the reverse kernel (dA_part holds one value
+                     // per lane at the first state of each wavefront's block)
+  int64_t span;      // head mode: channels per row of ddl_part (gcd(headdim, 64))
+  const float* dhfin;  // nullable: gradient of the final state (batch, dim, N)
+  float* ddl_part;     // head mode: ddelta before the activation, summed over runs of span
+                       // channels, (batch, dim / span, L)
+  float* dbias_hpart;  // head mode: (nheads, batch, ceil(L / kHeadDeltaChunk)) partial sums
 };
 hipError_t launch_bwd(const BwdParams& q, bool bf16, hipStream_t stream);
+// the reverse kernel of one A per head, dstate > 16 or the zero-order hold (with its checkpoint
+// pass and the head-mode ddelta reduction), per io dtype; launch_bwd adds the reductions
+hipError_t launch_bwd_wide_bf16(const BwdParams& q, hipStream_t stream);
+hipError_t launch_bwd_wide_f32(const BwdParams& q, hipStream_t stream);
+// states per lane of that kernel for dstate N (4, 8 or 16)
+inline int bwd_wide_states_per_lane(int64_t N) { return N <= 16 ? 4 : (N <= 32 ? 8 : 16); }
 // Chunked matrix form of the head-mode forward pass (bf16 io, MFMA). ssd_supported checks the
 // shape and access conditions it needs (dstate 64 or 128, 64-channel blocks within one head and
 // one group, 16-byte vector access of every row); the caller checks h0 / hfin alignment.

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert ssm.abi_version() == 4
+    assert ssm.abi_version() == 5
     for code in range(-10, 1):
         s = ssm.status_string(code)
         assert s and s != "unknown status"
@@ -177,8 +177,6 @@ def test_backward_validation():
                            a["wsb"], None)
     d = ssm.desc_contiguous(2, 64, 128, 16)
     assert ssm.bwd_workspace_size(d) > 0
-    assert call(ssm.desc_contiguous(2, 64, 128, 32)) == -9                     # dstate > 16
-    assert call(ssm.desc_contiguous(2, 64, 128, 16, headdim=64, a_mode=ssm.SSM_A_HEAD)) == -9
     assert call(d, dA=None) == -1
     assert call(d, z=FAKE + (12 << 30)) == -1                                  # z without dz
     assert call(d, dx=None) == -1

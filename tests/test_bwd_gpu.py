@@ -30,14 +30,16 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def _run(cfg, inputs, dy, h0=None):
+def _run(cfg, inputs, dy, h0=None, zoh=False, dhf=None):
     import selective_state_space_24_amd as ssm
     dev = device_inputs(inputs)
     dyd = to_torch(dy, dy.dtype == np.uint16, "cuda")
     h0d = torch.from_numpy(h0).cuda() if h0 is not None else None
+    dhfd = torch.from_numpy(dhf).cuda() if dhf is not None else None
     g = ssm.selective_scan_bwd(dev["x"], dev["delta"], dev["A"], dev["B"], dev["C"], dev.get("D"),
                                dev.get("z"), dev.get("delta_bias"), cfg.softplus, dyd, h0=h0d,
-                               want_dh0=h0 is not None)
+                               want_dh0=h0 is not None or dhf is not None, zoh=zoh,
+                               dh_final=dhfd)
     torch.cuda.synchronize()
     return {k: y_to_f64(v) for k, v in g.items()}
 
@@ -49,9 +51,10 @@ def _dy(cfg, seed):
         cfg.batch, cfg.dim, cfg.L)
 
 
-def _compare(cfg, inputs, dy, h0=None, tol=None):
-    g = _run(cfg, inputs, dy, h0)
-    ref = oracle.scan_inputs_bwd(inputs, dy, cfg, h0=None if h0 is None else h0.astype(np.float64))
+def _compare(cfg, inputs, dy, h0=None, tol=None, zoh=False, dhf=None):
+    g = _run(cfg, inputs, dy, h0, zoh=zoh, dhf=dhf)
+    ref = oracle.scan_inputs_bwd(inputs, dy, cfg, h0=None if h0 is None else h0.astype(np.float64),
+                                 zoh=zoh, dh_final=dhf, want_dh0=dhf is not None)
     tol = tol or TOL[cfg.io]
     errs = {}
     for k, v in ref.items():
@@ -87,6 +90,38 @@ def test_backward_matches_oracle(case):
     inputs = ssmgen.make_inputs(cfg)
     hinit = np.random.default_rng(L).standard_normal((batch, dim, N)).astype(np.float32) if h0 else None
     _compare(cfg, inputs, _dy(cfg, L), hinit)
+
+
+WIDE_CASES = [
+    # batch, dim, L, N, headdim, a_mode, io, gate, zoh, h0, dh_final
+    (2, 128, 100, 32, 64, "head", "bf16", True, False, False, False),
+    (1, 256, 77, 128, 64, "head", "f32", True, False, True, False),     # 8 wavefronts of 16
+    (2, 192, 130, 64, 32, "head", "f32", False, False, False, False),   # two rows per head
+    (1, 64, 50, 8, 2, "head", "f32", True, False, False, True),         # heads of two channels
+    (2, 96, 70, 16, 96, "head", "f32", True, False, True, False),       # a head over two groups
+    (2, 64, 90, 16, 1, "diag", "f32", True, True, False, False),        # zero-order hold
+    (1, 70, 60, 32, 1, "diag", "f32", True, True, True, True),
+    (2, 128, 100, 64, 64, "head", "bf16", True, True, True, False),
+    (1, 64, 40, 64, 1, "diag", "f32", False, False, False, False),      # dstate above 16
+    (1, 64, 33, 128, 1, "diag", "f32", True, False, False, False),
+    (2, 64, 100, 16, 1, "diag", "f32", True, False, True, True),        # four-state kernel
+    (1, 64, 2, 128, 64, "head", "f32", True, True, False, True),        # shorter than a block
+]
+
+
+@pytest.mark.parametrize("case", WIDE_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_backward_head_mode_zoh_and_wide_states(case):
+    """One A per head (dA, ddelta, dbias summed over each head's channels), dstate up to 128,
+    the zero-order hold, and the gradient of the final state."""
+    batch, dim, L, N, hd, mode, io, gate, zoh, h0, dhf = case
+    cfg = ssmgen.ScanConfig(name="bwd-wide", batch=batch, dim=dim, L=L, N=N, headdim=hd,
+                            a_mode=mode, io=io, gate=gate, seed=900 + L + N)
+    _say(f"[bwd-wide] {case}")
+    inputs = ssmgen.make_inputs(cfg)
+    r = np.random.default_rng(L + N)
+    hinit = r.standard_normal((batch, dim, N)).astype(np.float32) if h0 else None
+    dhfin = r.standard_normal((batch, dim, N)).astype(np.float32) if dhf else None
+    _compare(cfg, inputs, _dy(cfg, L), hinit, zoh=zoh, dhf=dhfin)
 
 
 @pytest.mark.parametrize("ci", [0, 1])
@@ -146,5 +181,76 @@ def test_backward_full_size_bench_workload():
         worst[k] = err
         assert err <= TOL[cfg.io], f"{k}: rel err {err:.3e}"
     _say(f"[bwd] config 2 errors {', '.join(f'{k} {e:.2e}' for k, e in worst.items())}")
+    del g
+    torch.cuda.empty_cache()
+
+
+def _oracle_bwd_entry_by_blocks(cfg, b, dy_b, block):
+    """The oracle's gradients of batch entry b, run over channel blocks (whole heads, one B/C
+    group each) on the host's threads at once; dB and dC are the sums over the blocks, in block
+    order."""
+    from concurrent.futures import ThreadPoolExecutor
+    starts = list(range(0, cfg.dim, block))
+
+    def one(d0):
+        d1 = min(cfg.dim, d0 + block)
+        sub = ssmgen.block_config(cfg, d0, d1)
+        return oracle.scan_inputs_bwd(ssmgen.make_channel_block(cfg, b, d0, d1, nthreads=1),
+                                      dy_b[None, d0:d1], sub, nthreads=1)
+    with ThreadPoolExecutor(max_workers=min(16, oracle.cpu_threads())) as ex:
+        parts = list(ex.map(one, starts))
+    rows = lambda d0, d1: ((d0 // cfg.headdim, d1 // cfg.headdim) if cfg.a_mode == "head"
+                           else (d0, d1))
+    out = {k: np.concatenate([g[k] for g in parts], axis=1) for k in ("dx", "dz")}
+    out["ddelta"] = np.concatenate([g["ddelta"] for g in parts], axis=1)
+    for k in ("dA", "dD", "ddelta_bias"):
+        out[k] = np.concatenate([g[k] for g in parts], axis=0)
+    for k in ("dB", "dC"):
+        acc = None
+        for g in parts:
+            acc = g[k] if acc is None else acc + g[k]
+        out[k] = acc
+    assert rows(0, cfg.dim)[1] == out["ddelta"].shape[1]
+    return out
+
+
+@pytest.mark.timeout(900)
+def test_backward_full_size_scalar_decay_heads():
+    """The scalar-decay heads config (batch 4, 64 heads x 64, N 128, L 8192, bf16) at full size:
+    every gradient of every batch entry against the oracle run one entry at a time (over blocks
+    of one head each, in parallel), and dA, dD and dbias against the sum over the four
+    entries."""
+    import selective_state_space_24_amd as ssm
+    cfg = ssmgen.CONFIGS[4]
+    _say(f"[bwd] config 4 {cfg.name}: generating inputs")
+    dev = {}
+    for name in cfg.shapes():
+        dev.update(device_inputs({name: ssmgen.make_tensor(cfg, name)}))
+    dy = _dy(cfg, 4)
+    dyd = to_torch(dy, dy.dtype == np.uint16, "cuda")
+    _say("[bwd] config 4: running")
+    g = ssm.selective_scan_bwd(dev["x"], dev["delta"], dev["A"], dev["B"], dev["C"], dev["D"],
+                               dev["z"], dev["delta_bias"], cfg.softplus, dyd)
+    torch.cuda.synchronize()
+    del dev, dyd
+    summed = {"dA": None, "dD": None, "ddelta_bias": None}
+    worst = {}
+    for b in range(cfg.batch):
+        ref = _oracle_bwd_entry_by_blocks(cfg, b, dy[b], cfg.headdim)
+        for k in summed:
+            summed[k] = ref[k] if summed[k] is None else summed[k] + ref[k]
+        for k in ("dx", "ddelta", "dz", "dB", "dC"):
+            got = y_to_f64(g[k][b:b + 1])
+            assert np.isfinite(got).all(), (k, b)
+            err = oracle.rel_err(got, ref[k])
+            worst[k] = max(worst.get(k, 0.0), err)
+            assert err <= TOL[cfg.io], f"{k} of batch entry {b}: rel err {err:.3e}"
+        del ref
+        _say(f"[bwd] config 4: batch entry {b} done")
+    for k, v in summed.items():
+        err = oracle.rel_err(y_to_f64(g[k]), v)
+        worst[k] = err
+        assert err <= TOL[cfg.io], f"{k}: rel err {err:.3e}"
+    _say(f"[bwd] config 4 errors {', '.join(f'{k} {e:.2e}' for k, e in worst.items())}")
     del g
     torch.cuda.empty_cache()
