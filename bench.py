@@ -15,7 +15,8 @@ device copy's bandwidth measured in the same run); the ALU roofline that actuall
 full issue, see ``alu_model``); and the fp64 CPU oracle timed on the host cores over whole batch
 entries of the same workload.
 
-``--workload bwd`` measures the backward pass (all input gradients) of the same workload.
+``--workload bwd`` measures the backward pass (all input gradients) of the same workload, and
+``--workload bwd-heads`` that of the scalar-decay heads config (recurrent form).
 ``--workload heads`` measures the scalar-decay heads scan (batch 4, 64 heads x 64 channels,
 N 128, L 8192, bf16 I/O) in its chunked matrix form on the matrix cores (``--algorithm
 recurrent`` for the step-by-step recurrence instead); its roofline is HBM bandwidth, with the
@@ -181,8 +182,29 @@ def alu_model_bwd(cfg):
         the gate silu and silu' (12 flops, 52 cyc), y = readout + D x and dz (3 flops, 8 cyc),
         dx += gy D, dD += gy x, dbias += (4 fma/add: 7 flops, 16 cyc), and the two state sums
         ddelta part += x sb, dx part = delta sb (3 flops, 8 cyc)
-    The sums over lanes for dB and dC and over the batch are not counted."""
+    The sums over lanes for dB and dC and over the batch are not counted.
+    With one A per head (``cfg.a_mode == "head"``) the decay and its exp2 are per (t, head): per
+    state update the recompute is u*B and the h fma (3 flops, 8 cyc), the reverse step gh += gy C,
+    gy h, gh h_prev sum, gh u, gh B sum, gh *= dA (9 flops, 24 cyc), and per (t, channel) two
+    exp2 of delta*a (recompute and reverse) with the sums a dA s1 and delta dA s1 (4 flops)."""
     valu, trans = VALU_CYCLES, TRANS_CYCLES
+    if cfg.a_mode == "head":
+        fl = cfg.N * (3 + 9) + 2 + 4
+        cy = cfg.N * (2 * valu + 6 * valu) + 2 * (valu + trans) + 3 * valu
+        if cfg.gate:
+            fl += cfg.N * 2
+            cy += cfg.N * valu
+        if cfg.softplus:
+            fl += 14
+            cy += 10 * valu + 3 * trans
+        fl += 1
+        cy += valu
+        if cfg.gate:
+            fl += 12
+            cy += 9 * valu + 2 * trans
+        fl += 3 + 7
+        cy += 2 * valu + 4 * valu
+        return fl, cy
     fl = cfg.N * (5 + 15) + 3
     cy = cfg.N * ((3 * valu + trans) + (10 * valu + trans)) + 2 * valu
     if cfg.gate:
@@ -213,11 +235,11 @@ def bwd_bytes(cfg) -> int:
     return reads + writes
 
 
-def run_bwd(args, torch):
+def run_bwd(args, torch, heads=False):
     import numpy as np
     import ssmgen
     import selective_state_space_24_amd as ssm
-    cfg = ssmgen.CONFIGS[WORKLOAD]
+    cfg = ssmgen.CONFIGS[HEADS_WORKLOAD if heads else WORKLOAD]
     dev = device_inputs(cfg, torch)
     dy = torch.randn(cfg.batch, cfg.dim, cfg.L, device="cuda").to(dev["x"].dtype)
     stream = torch.cuda.current_stream()
@@ -252,7 +274,9 @@ def run_bwd(args, torch):
         "unit": "Gtoken\u00b7channel/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "Mamba-1.4B layer selective scan backward (all input gradients)",
+        "config": {"workload": ("scalar-decay heads selective scan backward (all input "
+                                "gradients; one A per head, 64 heads x 64)" if heads else
+                                "Mamba-1.4B layer selective scan backward (all input gradients)"),
                    "batch": cfg.batch, "d_inner": cfg.dim, "seq_len": cfg.L, "d_state": cfg.N,
                    "io_dtype": cfg.io, "gate": "silu(z)", "delta_softplus": cfg.softplus},
         "roofline": {"bound": "alu", "achieved": round(achieved, 2), "peak": round(peak, 2),
@@ -262,7 +286,7 @@ def run_bwd(args, torch):
                 "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "step_ms": {"p10": round(pct(0.1), 5), "median": round(pct(0.5), 5),
                     "p90": round(pct(0.9), 5)},
-        "launches_per_step": 4,
+        "launches_per_step": 5 if heads else 4,
         "kernel_source": kernel_source_hash(),
     }
     if args.cpu_budget > 0:
@@ -270,16 +294,43 @@ def run_bwd(args, torch):
         del dev, dy, g, ws
         torch.cuda.empty_cache()
         threads = min(oracle.cpu_threads(), cfg.batch)  # the oracle's backward splits the batch
-        inputs = ssmgen.make_inputs(cfg)
-        dyh = np.random.default_rng(0).standard_normal((cfg.batch, cfg.dim, cfg.L))
-        t0 = time.perf_counter()
-        oracle.scan_inputs_bwd(inputs, dyh, cfg, nthreads=threads)
-        spent = time.perf_counter() - t0
-        out["cpu_baseline"] = {
-            "value": round(cfg.tokch / spent / 1e9, 6), "unit": out["unit"], "cores": threads,
-            "kind": "oracle",
-            "sample": f"the whole workload once ({cfg.batch} batch entries, one thread each) in "
-                      f"{spent:.2f} s; input generation untimed"}
+        if heads:
+            # one batch entry (the oracle's backward runs one thread per entry) is about 40 s of
+            # work: a sample of 8 heads of entry 0 instead, 8 threads at once
+            from concurrent.futures import ThreadPoolExecutor
+            nh = 8
+            dyh = np.random.default_rng(0).standard_normal((cfg.headdim * nh, cfg.L))
+
+            def one(h):
+                d0 = h * cfg.headdim
+                sub = ssmgen.block_config(cfg, d0, d0 + cfg.headdim)
+                inp = ssmgen.make_channel_block(cfg, 0, d0, d0 + cfg.headdim, nthreads=1)
+                return inp, sub
+            blocks = [one(h) for h in range(nh)]
+            t0 = time.perf_counter()
+            with ThreadPoolExecutor(max_workers=nh) as ex:
+                list(ex.map(lambda i: oracle.scan_inputs_bwd(
+                    blocks[i][0], dyh[None, i * cfg.headdim:(i + 1) * cfg.headdim], blocks[i][1],
+                    nthreads=1), range(nh)))
+            spent = time.perf_counter() - t0
+            tok = nh * cfg.headdim * cfg.L
+            out["cpu_baseline"] = {
+                "value": round(tok / spent / 1e9, 6), "unit": out["unit"], "cores": nh,
+                "kind": "oracle",
+                "sample": f"{nh} heads of batch entry 0 ({nh * cfg.headdim} channels x {cfg.L} "
+                          f"steps), one thread per head, in {spent:.2f} s; input generation "
+                          f"untimed"}
+        else:
+            inputs = ssmgen.make_inputs(cfg)
+            dyh = np.random.default_rng(0).standard_normal((cfg.batch, cfg.dim, cfg.L))
+            t0 = time.perf_counter()
+            oracle.scan_inputs_bwd(inputs, dyh, cfg, nthreads=threads)
+            spent = time.perf_counter() - t0
+            out["cpu_baseline"] = {
+                "value": round(cfg.tokch / spent / 1e9, 6), "unit": out["unit"], "cores": threads,
+                "kind": "oracle",
+                "sample": f"the whole workload once ({cfg.batch} batch entries, one thread each) "
+                          f"in {spent:.2f} s; input generation untimed"}
     print(json.dumps(out), flush=True)
 
 
@@ -552,8 +603,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 skips it)")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--workload", choices=("scan", "decode", "bwd", "heads", "lsweep"),
-                    default="scan")
+    ap.add_argument("--workload", choices=("scan", "decode", "bwd", "bwd-heads", "heads",
+                                           "lsweep"), default="scan")
     ap.add_argument("--algorithm", choices=("chunked", "recurrent"), default="chunked",
                     help="--workload heads: the form of the scan")
     args = ap.parse_args()
@@ -589,8 +640,8 @@ def main():
     if args.workload == "decode":
         run_decode(args, torch)
         return
-    if args.workload == "bwd":
-        run_bwd(args, torch)
+    if args.workload in ("bwd", "bwd-heads"):
+        run_bwd(args, torch, heads=args.workload == "bwd-heads")
         return
     if args.workload == "heads":
         run_heads(args, torch)
