@@ -886,15 +886,23 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
 #pragma unroll
     for (int k = 0; k < V / 2; ++k) dst[k] = f32x4{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]};
   };
+  for (int i = lane; i < 16 * kWaveRowStride; i += 64) sB[i] = 0.0f;  // padding states' B rows
+  wave_lds_sync();
   auto put_bc = [&](int i, const float (&bv)[V], const float (&cv)[V]) __attribute__((always_inline)) {
     f32x4* db = reinterpret_cast<f32x4*>(&sB[prow[i] * kWaveRowStride + pt[i]]);
     f32x4* dc = reinterpret_cast<f32x4*>(&sC[prow[i] * kWaveRowStride + pt[i]]);
-    const float m = bvalid[i] ? 1.0f : 0.0f;  // padding states: B = C = 0
+    // padding states (N < 16, their rows read a valid state's) never write their B row, which
+    // stays zero from the start: B = 0 keeps their state at zero, so the C there adds nothing
+    // to the readout
+    if (bvalid[i]) {
 #pragma unroll
-    for (int k = 0; k < V / 4; ++k) {
-      db[k] = f32x4{bv[4 * k], bv[4 * k + 1], bv[4 * k + 2], bv[4 * k + 3]} * m;
-      if constexpr (!NOREAD)
-        dc[k] = f32x4{cv[4 * k], cv[4 * k + 1], cv[4 * k + 2], cv[4 * k + 3]} * m;
+      for (int k = 0; k < V / 4; ++k)
+        db[k] = f32x4{bv[4 * k], bv[4 * k + 1], bv[4 * k + 2], bv[4 * k + 3]};
+    }
+    if constexpr (!NOREAD) {
+#pragma unroll
+      for (int k = 0; k < V / 4; ++k)
+        dc[k] = f32x4{cv[4 * k], cv[4 * k + 1], cv[4 * k + 2], cv[4 * k + 3]};
     }
   };
   auto prologue_full = [&](const Raw& r, int hf) __attribute__((always_inline)) {

@@ -302,6 +302,11 @@ __global__ void __launch_bounds__(kThreads, 1)
       float w = dl;
       if (zoh) w = dl * zoh_ratio(__builtin_amdgcn_exp2f(a2), a2);
       if (!valid) { a2 = 0.0f; w = 0.0f; }
+      // a step whose decay 2^a2 is below the smallest fp32 (a2 < -150) zeroes every product
+      // through it whatever its exact value, so a2 is clamped at -160: the prefix sums then stay
+      // within 64 x 160 of zero, and their differences s_t - s_j keep an absolute error of about
+      // 1e-3 even when single steps decay by far more (large delta times large |A|)
+      a2 = fmaxf(a2, -160.0f);
       // inclusive prefix sum over the 64 steps of the chunk
       float s2 = a2;
 #pragma unroll
