@@ -17,7 +17,7 @@ constexpr int64_t kMaxSegments = 65535;       // grid.y limit
 struct Plan {
   int64_t nseg;
   int64_t seg_len;
-  bool four_wave = false;  // bf16 io, 8 < dstate <= 16: the four-wavefront kernel (see below)
+  bool state_split = false;  // bf16 io, 8 < dstate <= 16: the state-split kernel (see below)
 };
 
 bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
@@ -118,12 +118,13 @@ Plan plan_segments(const ssm_scan_desc* d) {
   int64_t want = (kTargetWaves + waves - 1) / waves;
   if (d->io_dtype == SSM_DTYPE_BF16 && d->dstate > 8 && d->dstate <= 16) {
     // bf16 io with 8 < N <= 16 runs the kernel with independent wavefronts, one 8-wavefront
-    // workgroup (128 channels) per CU, except where four_wave_one_pass holds: then the
-    // four-wavefront kernel needs no summary pass, and its workgroups spread over more CUs
-    // (measured 183 us against 192-204 us at batch 8, d_inner 1536, L 2048, and likewise at
-    // 8 x 2048 and 4 x 4096 channels)
-    if (ssm::four_wave_one_pass(groups)) {
-      p.four_wave = true;
+    // workgroup (128 channels) per CU, except where state_split_one_pass holds: then the
+    // barrier-synchronised kernel whose wavefronts split the states needs no summary pass, and
+    // its 64-channel workgroups spread over more CUs (measured 165 us with eight wavefronts of
+    // two states, 183 us with four of four, against 192-204 us split along L, at batch 8,
+    // d_inner 1536, L 2048, and likewise at 8 x 2048 and 4 x 4096 channels)
+    if (ssm::state_split_one_pass(groups)) {
+      p.state_split = true;
       return p;
     }
     // otherwise segments: beyond what fills the chip once they would start a second round of
@@ -328,7 +329,7 @@ int ssm_selective_scan_fwd_ext(const ssm_scan_desc* desc, const void* x, const v
   p.groups_per_batch = (d.dim + ssm::kChannelsPerGroup - 1) / ssm::kChannelsPerGroup;
   p.seg_len = plan.seg_len;
   p.nseg = (int32_t)plan.nseg;
-  p.four_wave = plan.four_wave ? 1 : 0;
+  p.state_split = plan.state_split ? 1 : 0;
   p.softplus = delta_softplus ? 1 : 0;
   p.zoh = disc == SSM_DISC_ZOH ? 1 : 0;
   // 16-byte vector access of x/delta/z/y rows: 16-byte aligned bases, strides multiple of 16 B

@@ -19,17 +19,18 @@ constexpr int64_t kCUs = 256;           // compute units of an MI355X
 constexpr int64_t kTargetWaves = 2048;  // about two resident wavefronts per SIMD (256 CUs)
 
 // True when `groups` (batch x 64-channel groups) runs the whole sequence in one pass without
-// further thought: enough four-wavefront workgroups for three quarters of the target waves.
+// further thought: enough 64-channel, four-wavefront workgroups for three quarters of the
+// target waves.
 inline bool groups_fill_chip(int64_t groups) {
   return groups * kWavesPerGroup * 4 >= kTargetWaves * 3;
 }
 
 // bf16 io with 8 < N <= 16 normally runs the kernel with independent wavefronts (128-channel,
 // 8-wavefront workgroups, one per CU). With 64-channel groups for three quarters of the CUs or
-// more, but too few 128-channel workgroups to fill the chip, the four-wavefront kernel (two
-// workgroups per CU) runs the whole sequence in one pass instead. The forward planner and the
-// backward checkpoint pass both take this choice from here.
-inline bool four_wave_one_pass(int64_t groups) {
+// more, but too few 128-channel workgroups to fill the chip, the barrier-synchronised kernel
+// whose wavefronts split the states (64-channel workgroups) runs the whole sequence in one pass
+// instead. The forward planner and the backward checkpoint pass both take this choice from here.
+inline bool state_split_one_pass(int64_t groups) {
   return groups * 4 >= kCUs * 3 && !groups_fill_chip(groups);
 }
 
@@ -66,8 +67,9 @@ struct ScanParams {
   int32_t zoh;               // zero-order-hold B discretisation instead of delta * B
   int32_t state_vec;         // decode: the state allows 16-byte access (N % 4 == 0, aligned)
   int32_t a_vec;             // decode: rows of A allow 16-byte access
-  int32_t four_wave;         // bf16 io, 8 < N <= 16: run scan_fwd_kernel rather than the kernel
-                             // with independent wavefronts (chosen by the segment planner)
+  int32_t state_split;       // bf16 io, 8 < N <= 16: run scan_fwd_kernel (eight wavefronts of two
+                             // states) in one pass rather than the kernel with independent
+                             // wavefronts (chosen by the segment planner)
 };
 
 // One launcher per (io dtype, A mode); each is compiled in its own translation unit.

@@ -4,7 +4,7 @@
 // wavefront owns 16 channels x all states and runs without workgroup barriers. scan_fwd_kernel,
 // described here, serves every other case (fp32 io, N <= 8 or N > 16, and bf16 shapes whose
 // 128-channel workgroups are too few to fill the chip while its 64-channel ones are not: the
-// segment planner's four_wave choice) and also runs some segment summaries and the backward
+// segment planner's state_split choice) and also runs some segment summaries and the backward
 // pass's checkpoints.
 //
 // Work decomposition of scan_fwd_kernel: one workgroup = 64 channels of one batch entry x one
@@ -201,7 +201,7 @@ template <typename IO, int NS, int NW, bool HEAD, bool SUMMARY, bool GATE, bool 
 // At most two workgroups fit a CU's LDS (one once the B/C tile holds more than 16 states), so
 // each SIMD holds at most two (one) of these wavefronts: the second launch bound lets the
 // compiler use the registers that this occupancy leaves.
-__global__ void __launch_bounds__(64 * NW, NS <= 4 ? 2 : 1)
+__global__ void __launch_bounds__(64 * NW, (NS <= 4 && NW <= 4) ? 2 : 1)
     scan_fwd_kernel(const IO* __restrict__ X, const IO* __restrict__ DL, const IO* __restrict__ Bm,
                     const IO* __restrict__ Cm, const IO* __restrict__ Z, IO* __restrict__ Y,
                     const float* __restrict__ Am, const float* __restrict__ Dm,
@@ -1170,11 +1170,22 @@ hipError_t launch_cfg(const ScanParams& p, hipStream_t stream) {
   const dim3 block(64 * NW);
   const int64_t groups = p.batch * p.groups_per_batch;
   if constexpr (NS == 4 && WaveIo<IO>::value) {
-    // (four_wave: the segment planner chose the four-wavefront form below instead)
-    if (!p.four_wave) {
+    if (p.state_split) {
+      // the planner's one-pass choice for 64-channel groups too few for the chip's 128-channel
+      // workgroups: eight wavefronts of two states each, two per SIMD of the workgroup's CU
+      // (165 us against 183 us for four of four at batch 8, d_inner 1536, L 2048)
+      const dim3 block8(64 * 8);
+      if (p.z)
+        hipLaunchKernelGGL((scan_fwd_kernel<IO, 2, 8, HEAD, false, true, ZOH>),
+                           dim3((unsigned)groups, 1), block8, 0, stream, SCAN_ARGS(p));
+      else
+        hipLaunchKernelGGL((scan_fwd_kernel<IO, 2, 8, HEAD, false, false, ZOH>),
+                           dim3((unsigned)groups, 1), block8, 0, stream, SCAN_ARGS(p));
+      return hipGetLastError();
+    } else {
       // 8 < N <= 16: the kernel with independent wavefronts for the output. The summaries take it
       // too when they fill about three quarters of the chip (1536 wavefronts, 192 CUs); fewer
-      // summary workgroups run faster spread over more CUs in the four-wavefront form.
+      // summary workgroups run faster spread over more CUs in the barrier-synchronised form.
       const unsigned wg = (unsigned)(p.batch * ((p.dim + kWaveGroupChannels - 1) / kWaveGroupChannels));
       const dim3 wblock(64 * kWaveGroupWaves);
       if (p.nseg > 1) {
