@@ -36,15 +36,20 @@ constexpr int kHeadChunk = kHeadDeltaChunk;  // steps per workgroup of the head-
 static_assert(kT % kCkptStep == 0, "a tile holds whole checkpoint intervals");
 }  // namespace wide
 
-// delta^2 g'(w) for w = delta a, g(w) = expm1(w) / w: g'(w) = (e^w - g) / w, from the series
-// 1/2 + w/3 + w^2/8 + w^3/30 + w^4/144 + w^5/840 where |w| < 0.1 (the closed form cancels
-// there; the first dropped term is below 2e-10). dA = e^w and g are the values already formed.
+// delta^2 g'(w) for w = delta a, g(w) = expm1(w) / w: g'(w) = (e^w - g) / w for |w| >= 1/2
+// (e^w - g >= 0.2 there, so the roundings of dA = e^w and g cost a few 1e-7 relative), else the
+// series 1/2 + w/3 + w^2/8 + w^3/30 + w^4/144 + w^5/840 + w^6/5760 + w^7/45360 (the first
+// dropped term is below 3e-8 relative at |w| = 1/2).
 __device__ __forceinline__ float zoh_dgdw_delta2(float dl, float w, float dA, float g) {
-  const float series =
-      fmaf(w, fmaf(w, fmaf(w, fmaf(w, fmaf(w, 1.0f / 840.0f, 1.0f / 144.0f), 1.0f / 30.0f),
-                             0.125f), 1.0f / 3.0f), 0.5f);
+  float s = fmaf(w, 1.0f / 45360.0f, 1.0f / 5760.0f);
+  s = fmaf(w, s, 1.0f / 840.0f);
+  s = fmaf(w, s, 1.0f / 144.0f);
+  s = fmaf(w, s, 1.0f / 30.0f);
+  s = fmaf(w, s, 0.125f);
+  s = fmaf(w, s, 1.0f / 3.0f);
+  s = fmaf(w, s, 0.5f);
   const float closed = (dA - g) * __builtin_amdgcn_rcpf(w);
-  return dl * dl * (fabsf(w) < 0.1f ? series : closed);
+  return dl * dl * (fabsf(w) < 0.5f ? s : closed);
 }
 
 template <typename IO, int NS, int NW, int SUB, bool HEAD, bool ZOH, bool GATE>

@@ -64,25 +64,46 @@ def test_softplus_values():
         assert abs(y[0, 0, 0] - ref) <= 2e-16 * max(1.0, abs(ref))
 
 
-def test_theorem1_fixture_matches_pages():
-    """The special case named by Theorem 1 (fixture holds the page's parameters)."""
+def test_theorem1_worked_example():
+    """Theorem 1 of the memo page with its parameters (one state, A = -1, B = 1, softplus,
+    zero-order hold) makes the scan the gated RNN h_t = (1 - sigmoid(v_t)) h_{t-1} +
+    sigmoid(v_t) x_t. The fixture holds a worked example computed by hand from that form, with
+    steps whose sigmoid is 1/2 or 3/4, so every expected h_t is an exact binary fraction."""
     import json
     import os
     fx = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "theorem1.json")))
     assert fx["N"] == 1 and fx["A"] == -1.0 and fx["B"] == 1.0 and fx["tau"] == "softplus"
-    assert P.theorem1_gate(scan, zoh=True) < 1e-13
+    ex = fx["worked_example"]
+    v = np.array([math.log(3.0) if s == "ln3" else float(s) for s in ex["v"]])
+    x = np.array(ex["x"])
+    L = len(x)
+    y = scan(x.reshape(1, 1, L), v.reshape(1, 1, L), np.array([[-1.0]]), np.ones((1, 1, 1, L)),
+             np.ones((1, 1, 1, L)), None, None, None, True, zoh=True)
+    assert np.max(np.abs(y[0, 0] - np.array(ex["h_zoh"]))) <= 1e-14
 
 
-def test_golden_regression():
-    """Oracle outputs stored by tests/golden/make_golden.py (which calls only the oracle)."""
+def test_golden_values_match_an_independent_forward():
+    """Oracle outputs stored by tests/golden/make_golden.py (which calls only the oracle): they
+    are still what the oracle computes, and they agree with the forward pass written
+    independently in plain torch fp64 ops (tests/oracle_bwd_pins.py)."""
     import os
     import ssmgen
+    torch = pytest.importorskip("torch")
+    from oracle_bwd_pins import _torch_forward
     path = os.path.join(os.path.dirname(__file__), "golden", "config0_oracle_y.txt")
     rows = [ln.split() for ln in open(path) if ln.strip() and not ln.startswith("#")]
-    inp = ssmgen.make_inputs(ssmgen.CONFIGS[0])
-    y = oracle.scan_inputs(inp, ssmgen.CONFIGS[0])
+    cfg = ssmgen.CONFIGS[0]
+    inp = ssmgen.make_inputs(cfg)
+    y = oracle.scan_inputs(inp, cfg)
+    tp = {k: (torch.tensor(oracle.as_f64(inp[k])) if k in inp else None)
+          for k in ("x", "delta", "A", "B", "C", "D", "z", "delta_bias")}
+    tp["h0"] = None
+    yt = _torch_forward(torch, tp, True, 1, False, False).numpy()
+    scale = float(np.max(np.abs(yt)))
     for b, d, t, val in rows:
-        assert float.fromhex(val) == y[int(b), int(d), int(t)]
+        g = float.fromhex(val)
+        assert g == y[int(b), int(d), int(t)]
+        assert abs(g - yt[int(b), int(d), int(t)]) <= 1e-12 * scale
 
 
 def test_empty_and_degenerate_sizes():
