@@ -590,10 +590,10 @@ int ssm_selective_scan_bwd_ext(const ssm_scan_desc* desc, const void* x, const v
   p.bc_vec = bc_vec ? 1 : 0;
 
   q.dy = dy; q.dx = dx; q.ddelta = ddelta; q.dz = dz;
-  // two-element stores of dx, ddelta, dz: their strides are those of x, delta, z, which vec_io
-  // makes multiples of 16 bytes; the bases must hold a pair
-  q.pair_out = (p.vec_io && aligned(dx, 2 * es) && aligned(ddelta, 2 * es) &&
-                (!dz || aligned(dz, 2 * es))) ? 1 : 0;
+  // 16-byte stores of dx, ddelta, dz: their strides are those of x, delta, z, which vec_io
+  // makes multiples of 16 bytes; the bases must be aligned too
+  q.vec_out = (p.vec_io && aligned(dx, 16) && aligned(ddelta, 16) && (!dz || aligned(dz, 16)))
+                  ? 1 : 0;
   q.dA = dA; q.dB = dB; q.dC = dC; q.dD = dD; q.dbias = ddelta_bias; q.dh0 = dh0;
   q.dhfin = dhfin;
   q.head = head ? 1 : 0;
@@ -606,6 +606,7 @@ int ssm_selective_scan_bwd_ext(const ssm_scan_desc* desc, const void* x, const v
   q.dbias_part = reinterpret_cast<float*>(ws + lay.dbias);
   q.ddl_part = reinterpret_cast<float*>(ws + lay.ddl);
   q.dbias_hpart = reinterpret_cast<float*>(ws + lay.dbh);
+  q.part_vec = (aligned(q.dB_part, 16) && aligned(q.dC_part, 16) && d.seqlen % 4 == 0) ? 1 : 0;
   const hipError_t e = ssm::launch_bwd(q, d.io_dtype == SSM_DTYPE_BF16, hs);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }

@@ -14,10 +14,13 @@
 //      channel and the four wavefronts split the states, so the per-channel sums over states
 //      (ddelta, dx, and the readout needed by dz) are added across wavefronts in LDS, and the
 //      per-(t, n) sums over channels (dB, dC) are added over the lanes of each wavefront in
-//      wave-private LDS, giving one partial per workgroup;
+//      wave-private LDS, giving one partial per workgroup. Outputs wait in LDS until the tile is
+//      done (dx, ddelta, dz in the slots of the consumed inputs, the dB/dC partials in a tile
+//      buffer) and leave in whole 16-byte pieces; for bf16 the next tile's inputs are loaded
+//      while the tile runs;
 //   3. reduce kernels add the partials: dB, dC over the workgroups of a batch entry's group,
 //      dA, dD, dbias over the batch, in a fixed order (results are deterministic).
-// The LDS use (about 74 KB) lets two workgroups share a CU. Arithmetic: fp32. This kernel takes
+// The LDS use (under 80 KB) lets two workgroups share a CU. Arithmetic: fp32. This kernel takes
 // diagonal A, dstate <= 16 and the delta * B rule; scan_bwd_wide.h takes every other case and
 // shares the reductions below.
 #include "scan_bwd_common.h"
@@ -30,9 +33,20 @@ constexpr int kSubs = kBT / kSub;   // sub-tiles per tile
 static_assert(kSub == kCkptStep, "every sub-tile starts at a checkpoint");
 constexpr int kInStride = kBT + 1;  // entries per channel row of the per-step LDS arrays
 constexpr int kRedStride = kSub + 1;
-// floats per column of the dB/dC lane-sum scratch (64 lanes, padded so that the 16-byte column
-// reads of consecutive columns start in different bank groups)
-constexpr int kSumStride = 64 + 4;
+
+// NS consecutive floats of LDS at p (aligned to NS floats) as one read
+template <int NS>
+__device__ __forceinline__ void lds_states(const float* p, float (&v)[NS]) {
+  if constexpr (NS == 4) {
+    const f32x4 q = *reinterpret_cast<const f32x4*>(p);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+  } else if constexpr (NS == 2) {
+    const float2 q = *reinterpret_cast<const float2*>(p);
+    v[0] = q.x; v[1] = q.y;
+  } else {
+    v[0] = p[0];
+  }
+}
 
 template <typename IO, int NS, bool GATE>
 __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
@@ -43,16 +57,19 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
   constexpr int CPT = kBT / V;                      // chunks per channel row of a tile
   constexpr int ITEMS = kChannelsPerGroup * CPT;
   constexpr int IPT = ITEMS / NT;                   // prologue items per thread
-  constexpr int RS = NS >= 4 ? 2 : 4;               // steps per dB/dC lane reduction
-  constexpr int NV = 2 * NS * RS;                   // dB/dC values per lane per reduction
+  constexpr int BCI = (NP * kBT + NT - 1) / NT;     // B (and C) elements per thread per tile
+  // the next tile's inputs are loaded while this tile runs where they take few registers (one
+  // 16-byte chunk per tensor per thread); otherwise right before they are needed
+  constexpr bool PREFETCH = IPT == 1;
+  constexpr int M = 2 * NS;                         // dB/dC values per lane per step
+  constexpr int G = 64 / M;                         // lanes that end up holding each sum
   static_assert(ITEMS % NT == 0, "prologue items must divide evenly");
-  static_assert(NV <= 32 && 64 % NV == 0, "dB/dC reduction layout");
 
-  __shared__ __align__(16) f32x4 s_in[kChannelsPerGroup * kInStride];  // delta, u, gy, x
-  __shared__ float s_gz[kChannelsPerGroup * kInStride];                 // dy silu'(z)
-  __shared__ __align__(16) float s_B[NP * kBT];
-  __shared__ __align__(16) float s_C[NP * kBT];
+  __shared__ __align__(16) f32x4 s_in[kChannelsPerGroup * kInStride];  // delta, gz, gy, x
+  __shared__ __align__(16) float s_B[kBT * NP];  // step-major: a wavefront's NS states of a step
+  __shared__ __align__(16) float s_C[kBT * NP];  // are one aligned vector
   __shared__ __align__(16) float s_red[3 * NW * kChannelsPerGroup * kRedStride];
+  __shared__ __align__(16) float s_dbc[2 * NP * kBT];  // the tile's dC, dB partials, (tensor, n, t)
 
   const ScanParams& p = q.f;
   const int tid = threadIdx.x;
@@ -75,12 +92,9 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
   // this lane's channel and states
   const int64_t d = d0 + lane;
   const bool live = d < p.dim;
-  float ap[NS], an[NS];  // a * log2(e) for exp2, and a itself
+  float ap[NS];  // a * log2(e), for exp2
 #pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    an[j] = (live && n0 + j < p.N) ? p.A[d * p.N + n0 + j] : 0.0f;
-    ap[j] = an[j] * kLog2e;
-  }
+  for (int j = 0; j < NS; ++j) ap[j] = ((live && n0 + j < p.N) ? p.A[d * p.N + n0 + j] : 0.0f) * kLog2e;
 
   // the epilogue's item: channel er, steps [2 * eq, 2 * eq + 2) of each sub-tile
   const int er = tid >> 2, eq = tid & 3;
@@ -96,11 +110,19 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
     da[j] = 0.0f;
   }
 
-  for (int64_t tile = (L + kBT - 1) / kBT - 1; tile >= 0; --tile) {
+  // ---- a tile's per-step inputs: raw 16-byte chunks (x, delta, dy, z) of this thread's prologue
+  // items and its B, C elements; then converted into LDS (padding steps are zero). With the
+  // prefetch, an odd tile's chunks are loaded together with those of the even tile before it
+  // (kept in raw2): the two share each 128-byte line of a bf16 row, which is then read whole.
+  struct Items {
+    u32x4 c[IPT][4];  // per item: x, delta, dy, z
+  };
+  Items raw, raw2;
+  IO rb[BCI], rc[BCI];
+  auto load_items = [&](int64_t tile) __attribute__((always_inline)) {
     const int64_t t0 = tile * kBT;
     const int lt_len = (int)min<int64_t>(kBT, L - t0);
-
-    // ---- prologue: per (channel, step) values of the tile into LDS; padding steps are zero
+    Items o;
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
       const int item = tid + it * NT;
@@ -108,38 +130,82 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
       const int64_t dd = d0 + r;
       const int64_t dv = min(dd, p.dim - 1);
       const int cnt = dd < p.dim ? max(0, min(V, lt_len - tl)) : 0;
-      float xv[V], dv_raw[V], zv[V], gv[V];
-      load_chunk<IO, true>(X + b * p.x_sb + dv * p.x_sd, t0 + tl, cnt, vec, xv);
-      load_chunk<IO, true>(DL + b * p.dl_sb + dv * p.dl_sd, t0 + tl, cnt, vec, dv_raw);
-      load_chunk<IO, true>(DY + b * p.y_sb + dv * p.y_sd, t0 + tl, cnt, vec, gv);
-      if constexpr (GATE) load_chunk<IO, true>(Z + b * p.z_sb + dv * p.z_sd, t0 + tl, cnt, vec, zv);
-      const float bias = (dd < p.dim && p.delta_bias) ? p.delta_bias[dv] : 0.0f;
+      o.c[it][0] = load_raw16<IO>(X + b * p.x_sb + dv * p.x_sd, t0 + tl, cnt, vec);
+      o.c[it][1] = load_raw16<IO>(DL + b * p.dl_sb + dv * p.dl_sd, t0 + tl, cnt, vec);
+      o.c[it][2] = load_raw16<IO>(DY + b * p.y_sb + dv * p.y_sd, t0 + tl, cnt, vec);
+      o.c[it][3] = GATE ? load_raw16<IO>(Z + b * p.z_sb + dv * p.z_sd, t0 + tl, cnt, vec)
+                        : u32x4{0u, 0u, 0u, 0u};
+    }
+    return o;
+  };
+  auto issue = [&](int64_t tile, bool pair) __attribute__((always_inline)) {
+    const int64_t t0 = tile * kBT;
+    const int lt_len = (int)min<int64_t>(kBT, L - t0);
+    if (PREFETCH && pair && (tile & 1) == 0) {
+      raw = raw2;  // loaded with tile + 1
+    } else {
+      raw = load_items(tile);
+      if (PREFETCH && pair && tile > 0) raw2 = load_items(tile - 1);
+    }
+#pragma unroll
+    for (int k = 0; k < BCI; ++k) {
+      const int i = tid + k * NT;
+      const int n = i / kBT, t = i % kBT;
+      const bool on = i < NP * kBT && n < p.N && t < lt_len;
+      rb[k] = on ? Bg[n * p.B_sn + t0 + t] : IO(0);
+      rc[k] = on ? Cg[n * p.C_sn + t0 + t] : IO(0);
+    }
+  };
+  auto fill = [&](int64_t tile) __attribute__((always_inline)) {
+    const int64_t t0 = tile * kBT;
+    const int lt_len = (int)min<int64_t>(kBT, L - t0);
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+      const int item = tid + it * NT;
+      const int r = item / CPT, tl = (item % CPT) * V;
+      const int64_t dd = d0 + r;
+      const int cnt = dd < p.dim ? max(0, min(V, lt_len - tl)) : 0;
+      const float bias = (dd < p.dim && p.delta_bias) ? p.delta_bias[dd] : 0.0f;
+      float xv[V], dv_raw[V], gv[V], zv[V];
+      unpack16<IO>(raw.c[it][0], xv);
+      unpack16<IO>(raw.c[it][1], dv_raw);
+      unpack16<IO>(raw.c[it][2], gv);
+      if constexpr (GATE) unpack16<IO>(raw.c[it][3], zv);
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        float dl = 0.0f, u = 0.0f, gy = 0.0f, xx = 0.0f, gzf = 0.0f;
+        float dl = 0.0f, gy = 0.0f, xx = 0.0f, gzf = 0.0f;
         if (e < cnt) {
           const float v = dv_raw[e] + bias;
           dl = p.softplus ? softplus_f32(v) : v;
           xx = xv[e];
-          u = dl * xx;
           gy = gv[e];
           if constexpr (GATE) {
             const float zz = zv[e];
-            const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zz * kLog2e));
-            gzf = gv[e] * s * fmaf(zz, 1.0f - s, 1.0f);
-            gy = gv[e] * zz * s;
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zz * kLog2e));
+            gzf = gv[e] * sg * fmaf(zz, 1.0f - sg, 1.0f);
+            gy = gv[e] * zz * sg;
           }
         }
-        s_in[r * kInStride + tl + e] = f32x4{dl, u, gy, xx};
-        s_gz[r * kInStride + tl + e] = gzf;
+        s_in[r * kInStride + tl + e] = f32x4{dl, gzf, gy, xx};
       }
     }
-    for (int i = tid; i < NP * kBT; i += NT) {
-      const int n = i / kBT, t = i % kBT;
-      const bool on = n < p.N && t < lt_len;
-      s_B[n * kBT + t] = on ? to_f32(Bg[n * p.B_sn + t0 + t]) : 0.0f;
-      s_C[n * kBT + t] = on ? to_f32(Cg[n * p.C_sn + t0 + t]) : 0.0f;
+#pragma unroll
+    for (int k = 0; k < BCI; ++k) {
+      const int i = tid + k * NT;
+      if (i < NP * kBT) {
+        s_B[(i % kBT) * NP + i / kBT] = to_f32(rb[k]);
+        s_C[(i % kBT) * NP + i / kBT] = to_f32(rc[k]);
+      }
     }
+  };
+
+  const int64_t ntile = (L + kBT - 1) / kBT;
+  // tile pairs (2m, 2m + 1) share their 128-byte lines; the last tile is alone if it is even
+  issue(ntile - 1, (ntile - 1) & 1);
+  for (int64_t tile = ntile - 1; tile >= 0; --tile) {
+    const int64_t t0 = tile * kBT;
+    const int lt_len = (int)min<int64_t>(kBT, L - t0);
+    fill(tile);
     // the checkpoints of the tile's sub-tiles (channel-contiguous); the last sub-tile's is
     // read now and each earlier one while the sub-tile after it runs. A sub-tile entirely past
     // L has none: its steps are padding, and it starts from 0.
@@ -152,6 +218,12 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
     float hnext[NS];
     load_ck(kSubs - 1, hnext);
     __syncthreads();
+    if (PREFETCH && tile > 0) issue(tile - 1, true);
+
+    // wavefront w's per-channel partial sums over its states: readout (ry), ddelta (rg), dx (rx)
+    float* ry = s_red + ((w * 3 + 0) * kChannelsPerGroup + lane) * kRedStride;
+    float* rg = s_red + ((w * 3 + 1) * kChannelsPerGroup + lane) * kRedStride;
+    float* rx = s_red + ((w * 3 + 2) * kChannelsPerGroup + lane) * kRedStride;
 
     // ---- sub-tiles, last first
 #pragma unroll 1
@@ -161,149 +233,133 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
 #pragma unroll
       for (int j = 0; j < NS; ++j) hsk[j] = hnext[j];
       if (k > 0) load_ck(k - 1, hnext);
-      // recompute the sub-tile's states (after each step) and the readout partials
-      float hh[kSub][NS];
-      float yp[kSub];
+      // recompute the sub-tile's states (after each step), their decays and the readout partials
+      float hh[kSub][NS], dAk[kSub][NS];
 #pragma unroll
       for (int i = 0; i < kSub; ++i) {
         const f32x4 in = s_in[lane * kInStride + tb + i];
+        const float u = in.x * in.w;
+        float Bv[NS], Cv[NS];
+        lds_states<NS>(s_B + (tb + i) * NP + n0, Bv);
+        lds_states<NS>(s_C + (tb + i) * NP + n0, Cv);
         float acc = 0.0f;
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
           const float prev = i == 0 ? hsk[j] : hh[i - 1][j];
-          hh[i][j] = fmaf(__builtin_amdgcn_exp2f(in.x * ap[j]), prev,
-                          in.y * s_B[(n0 + j) * kBT + tb + i]);
-          acc = fmaf(s_C[(n0 + j) * kBT + tb + i], hh[i][j], acc);
+          dAk[i][j] = __builtin_amdgcn_exp2f(in.x * ap[j]);
+          hh[i][j] = fmaf(dAk[i][j], prev, u * Bv[j]);
+          acc = fmaf(Cv[j], hh[i][j], acc);
         }
-        yp[i] = acc;
+        ry[i] = acc;
       }
       // reverse recurrence over the sub-tile
-      float gdel[kSub];
-      // wavefront w's block of s_red (its three partial arrays) doubles as its private scratch
-      // for the dB/dC lane sums, which use its first 64 (NV + 1) floats: that is within the
-      // first two arrays, so the third (rx, the dx partials) is written as the steps go
-      float* scratch = s_red + w * 3 * kChannelsPerGroup * kRedStride;
-      float* rx = s_red + ((w * 3 + 2) * kChannelsPerGroup + lane) * kRedStride;
-      static_assert(NV * kSumStride <= 2 * kChannelsPerGroup * kRedStride,
-                    "lane-sum scratch must stay clear of the dx partials");
-      // the scratch is column-major: value v of lane l at scratch[v * kSumStride + l], with v =
-      // [tensor (dC, dB)][state j][step e]
-      float* red = scratch + lane;
 #pragma unroll
-      for (int i4 = kSub - RS; i4 >= 0; i4 -= RS) {
+      for (int i = kSub - 1; i >= 0; --i) {
+        const int t = tb + i;
+        const f32x4 in = s_in[lane * kInStride + t];
+        const float dl = in.x, gy = in.z, xx = in.w;
+        const float u = dl * xx;
+        // ddelta and dx need sum_j gh_j (h_prev,j dA_j a_j + B_j x) and sum_j gh_j delta B_j:
+        // both are taken as sum_j gh_j h_prev,j dA_j a_j plus x and delta times sum_j gh_j B_j;
+        // the first sum is formed with a_j log2(e) and scaled by ln 2 once
+        float gd = 0.0f, sb = 0.0f;
+        float dbc[M];  // this lane's (channel's) terms of dC_j, dB_j at step t
+        float Bv[NS], Cv[NS];
+        lds_states<NS>(s_B + t * NP + n0, Bv);
+        lds_states<NS>(s_C + t * NP + n0, Cv);
 #pragma unroll
-        for (int e = RS - 1; e >= 0; --e) {
-          const int i = i4 + e;
-          const int t = tb + i;
-          const f32x4 in = s_in[lane * kInStride + t];
-          const float dl = in.x, u = in.y, gy = in.z, xx = in.w;
-          // ddelta and dx need sum_j gh_j (h_prev,j dA_j a_j + B_j x) and sum_j gh_j delta B_j:
-          // both are taken as sum_j gh_j h_prev,j dA_j a_j plus x and delta times sum_j gh_j B_j
-          float gd = 0.0f, sb = 0.0f;
-#pragma unroll
-          for (int j = 0; j < NS; ++j) {
-            const float Bv = s_B[(n0 + j) * kBT + t];
-            const float Cv = s_C[(n0 + j) * kBT + t];
-            gh[j] = fmaf(gy, Cv, gh[j]);
-            red[(j * RS + e) * kSumStride] = gy * hh[i][j];        // dC
-            const float dA = __builtin_amdgcn_exp2f(dl * ap[j]);
-            const float hp = i == 0 ? hsk[j] : hh[i - 1][j];
-            const float gt = gh[j] * (hp * dA);
-            gd = fmaf(gt, an[j], gd);
-            da[j] = fmaf(gt, dl, da[j]);
-            red[(RS * NS + j * RS + e) * kSumStride] = gh[j] * u;  // dB
-            sb = fmaf(gh[j], Bv, sb);
-            gh[j] *= dA;
-          }
-          gdel[i] = fmaf(xx, sb, gd);
-          rx[i] = dl * sb;
+        for (int j = 0; j < NS; ++j) {
+          gh[j] = fmaf(gy, Cv[j], gh[j]);
+          dbc[j] = gy * hh[i][j];
+          const float dA = dAk[i][j];
+          const float hp = i == 0 ? hsk[j] : hh[i - 1][j];
+          const float gt = gh[j] * (hp * dA);
+          gd = fmaf(gt, ap[j], gd);
+          da[j] = fmaf(gt, dl, da[j]);
+          dbc[NS + j] = gh[j] * u;
+          sb = fmaf(gh[j], Bv[j], sb);
+          gh[j] *= dA;
         }
-        // sum the RS steps' dC, dB over the wavefront's lanes (channels) via wave-private LDS
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // lane sums value col = lane % NV of the NV lanes part * NV .. + NV (four 16-byte reads
-        // of one column); the 64 / NV lanes of a column then combine across lanes
-        const int col = lane % NV, part = lane / NV;
-        float sum;
-        {
-          const f32x4* src = reinterpret_cast<const f32x4*>(scratch + col * kSumStride + part * NV);
-          f32x4 acc4 = src[0];
-#pragma unroll
-          for (int r4 = 1; r4 < NV / 4; ++r4) acc4 += src[r4];
-          sum = (acc4.x + acc4.y) + (acc4.z + acc4.w);
-        }
-#pragma unroll
-        for (int off = NV; off < 64; off <<= 1) sum = xor_sum(sum, off);
-        if (lane < NV) {
-          const int tensor = col / (RS * NS), j = (col / RS) % NS, e = col % RS;
-          const int64_t t = t0 + tb + i4 + e;
-          if (n0 + j < p.N && t < L) {
-            float* dst = tensor == 0 ? q.dC_part : q.dB_part;
-            dst[((b * p.groups_per_batch + wg) * p.N + n0 + j) * L + t] = sum;
-          }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      }
-      // per-channel partial sums over this wavefront's states
-      {
-        float* ry = s_red + ((w * 3 + 0) * kChannelsPerGroup + lane) * kRedStride;
-        float* rg = s_red + ((w * 3 + 1) * kChannelsPerGroup + lane) * kRedStride;
-#pragma unroll
-        for (int i = 0; i < kSub; ++i) {
-          ry[i] = yp[i];
-          rg[i] = gdel[i];
+        rg[i] = fmaf(xx, sb, gd * kLn2);
+        rx[i] = dl * sb;
+        // dC_j, dB_j summed over the wavefront's channels, in registers
+        const float tot = lane_sums<M>(dbc);
+        if ((lane & (G - 1)) == 0) {
+          const int v = lane / G;
+          s_dbc[((v / NS) * NP + n0 + v % NS) * kBT + t] = tot;
         }
       }
       __syncthreads();
       // epilogue: add the wavefronts' partials; dx, ddelta, dz for 2 steps of one channel
       {
-        float vx[2], vd[2], vz[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int i = eq * 2 + e;
           const int t = tb + i;
-          float ys = 0.0f, gds = 0.0f, gxsum = 0.0f;
+          const float* pr = s_red + er * kRedStride + i;
+          float ys = pr[0], gds = pr[kChannelsPerGroup * kRedStride],
+                gxsum = pr[2 * kChannelsPerGroup * kRedStride];
 #pragma unroll
-          for (int ww = 0; ww < NW; ++ww) {
-            ys += s_red[((ww * 3 + 0) * kChannelsPerGroup + er) * kRedStride + i];
-            gds += s_red[((ww * 3 + 1) * kChannelsPerGroup + er) * kRedStride + i];
-            gxsum += s_red[((ww * 3 + 2) * kChannelsPerGroup + er) * kRedStride + i];
+          for (int ww = 1; ww < NW; ++ww) {
+            ys += pr[(ww * 3 + 0) * kChannelsPerGroup * kRedStride];
+            gds += pr[(ww * 3 + 1) * kChannelsPerGroup * kRedStride];
+            gxsum += pr[(ww * 3 + 2) * kChannelsPerGroup * kRedStride];
           }
           const f32x4 in = s_in[er * kInStride + t];
           const float y = fmaf(eD, in.w, ys);
-          vz[e] = s_gz[er * kInStride + t] * y;
-          vx[e] = fmaf(in.z, eD, gxsum);
-          vd[e] = gds * (p.softplus ? sigmoid_from_softplus(in.x) : 1.0f);
+          const float vz = in.y * y;
+          const float vx = fmaf(in.z, eD, gxsum);
+          const float vd = gds * (p.softplus ? sigmoid_from_softplus(in.x) : 1.0f);
           dD_acc = fmaf(in.z, in.w, dD_acc);
-          dbias_acc += vd[e];
-        }
-        if (elive) {
-          const int64_t tt = t0 + tb + eq * 2;
-          IO* dxr = static_cast<IO*>(q.dx) + b * p.x_sb + ed * p.x_sd;
-          IO* ddr = static_cast<IO*>(q.ddelta) + b * p.dl_sb + ed * p.dl_sd;
-          IO* dzr = GATE ? static_cast<IO*>(q.dz) + b * p.z_sb + ed * p.z_sd : nullptr;
-          if (q.pair_out && tt + 1 < L) {
-            // tt is even: both steps in one store per tensor
-            store_pair(dxr + tt, vx[0], vx[1]);
-            store_pair(ddr + tt, vd[0], vd[1]);
-            if constexpr (GATE) store_pair(dzr + tt, vz[0], vz[1]);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              if (tt + e < L) {
-                store_elem(dxr + tt + e, vx[e]);
-                store_elem(ddr + tt + e, vd[e]);
-                if constexpr (GATE) store_elem(dzr + tt + e, vz[e]);
-              }
-            }
-          }
+          dbias_acc += vd;
+          // the step's inputs are dead now (this thread read them last): the slot holds the
+          // outputs until the tile is written out
+          s_in[er * kInStride + t] = f32x4{vx, vd, vz, 0.0f};
         }
       }
       __syncthreads();  // s_red is reused by the next sub-tile
     }
+
+    // ---- the tile's outputs: dx, ddelta, dz from the s_in slots, 16 bytes per store, by the
+    // thread whose prologue item covers the same slots (no barrier needed before its next
+    // prologue writes them); the dB, dC partials from s_dbc
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+      const int item = tid + it * NT;
+      const int r = item / CPT, tl = (item % CPT) * V;
+      const int64_t dd = d0 + r;
+      const int cnt = dd < p.dim ? max(0, min(V, lt_len - tl)) : 0;
+      if (cnt > 0) {
+        float vx[V], vd[V], vz[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const f32x4 o = s_in[r * kInStride + tl + e];
+          vx[e] = o.x;
+          vd[e] = o.y;
+          vz[e] = o.z;
+        }
+        const bool full = q.vec_out && cnt == V;
+        store_chunk<IO>(static_cast<IO*>(q.dx) + b * p.x_sb + dd * p.x_sd, t0 + tl, cnt, full, vx);
+        store_chunk<IO>(static_cast<IO*>(q.ddelta) + b * p.dl_sb + dd * p.dl_sd, t0 + tl, cnt,
+                        full, vd);
+        if constexpr (GATE)
+          store_chunk<IO>(static_cast<IO*>(q.dz) + b * p.z_sb + dd * p.z_sd, t0 + tl, cnt, full, vz);
+      }
+    }
+    static_assert((2 * NP * kBT / 4) % 64 == 0, "4-float pieces of the partials per wavefront");
+    for (int pc = tid; pc < 2 * NP * kBT / 4; pc += NT) {
+      const int tensor = pc / (NP * kBT / 4), n = (pc / (kBT / 4)) % NP, tq = (pc % (kBT / 4)) * 4;
+      const int cnt = n < p.N ? max(0, min(4, lt_len - tq)) : 0;
+      float* dst = (tensor == 0 ? q.dC_part : q.dB_part) +
+                   ((b * p.groups_per_batch + wg) * p.N + n) * L + t0 + tq;
+      const float* src = s_dbc + (tensor * NP + n) * kBT + tq;
+      if (q.part_vec && cnt == 4) {
+        *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(src);
+      } else {
+        for (int e = 0; e < cnt; ++e) dst[e] = src[e];
+      }
+    }
+    if (!PREFETCH && tile > 0) issue(tile - 1, false);
   }
 
   // ---- per-workgroup partials of the batch-summed gradients, and dh0

@@ -99,8 +99,9 @@ struct BwdParams {
   float* dA_part; // (batch, dim, N)
   float* dD_part; // (batch, dim)
   float* dbias_part;
-  int32_t pair_out;  // dx, ddelta, dz allow stores of two consecutive elements (aligned to 2
-                     // elements, with the strides of x, delta, z)
+  int32_t vec_out;   // dx, ddelta, dz allow 16-byte stores (16-byte aligned bases, with the
+                     // strides of x, delta, z, which vec_io makes multiples of 16 bytes)
+  int32_t part_vec;  // the dB, dC partials allow 16-byte stores (aligned bases, L % 4 == 0)
   int32_t head;      // one A per head (the forward's a_mode SSM_A_HEAD)
   int32_t head_ns;   // head mode: states per lane of the reverse kernel (dA_part holds one value
                      // per lane at the first state of each wavefront's block)

@@ -86,7 +86,7 @@ HOT = [
     ("ssd_fwd_kernelILi128ELb1E", "chunked MFMA form, N 128, gate (scalar-decay heads)", 0,
      160 * 1024),
     ("decode_vec_kernelItLi16ELb0ELb1E", "decode step, bf16, N 16, gate", 0, 0),
-    ("bwd_kernelItLi4ELb1E", "backward reverse kernel, bf16, N <= 16, gate", 2, 80 * 1024),
+    ("bwd_kernelItLi4ELb1E", "backward reverse kernel, bf16, N <= 16, gate", 0, 80 * 1024),
     ("bwd_wide_kernelItLi16ELi8ELi4ELb1ELb0ELb1E",
      "backward reverse kernel, one A per head, N 128, gate", 57, 160 * 1024),
 ]
