@@ -46,10 +46,12 @@ WORKLOAD = 2           # Mamba-1.4B layer scan
 HEADS_WORKLOAD = 4     # scalar-decay heads scan
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(names=None) -> str:
+    """Hash of the library's kernel sources: all of csrc/, or the named files of it (those that
+    define one kernel and its launch)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "selective_state_space_24_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(names if names is not None else os.listdir(csrc)):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -57,14 +59,14 @@ def kernel_source_hash() -> str:
 
 def traffic_from_profile(cfg_key: str):
     """HBM bytes per launch from the committed counter summary, if it was taken on the current
-    kernel source; None otherwise."""
+    source of that kernel (the files the record lists, else all of csrc/); None otherwise."""
     path = os.path.join(ROOT, "profiles", f"traffic_{cfg_key}.json")
     try:
         with open(path) as f:
             rec = json.load(f)
+        if rec.get("source_hash") != kernel_source_hash(rec.get("sources")):
+            return None
     except (OSError, ValueError):
-        return None
-    if rec.get("source_hash") != kernel_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -607,6 +609,8 @@ def main():
                                            "lsweep"), default="scan")
     ap.add_argument("--algorithm", choices=("chunked", "recurrent"), default="chunked",
                     help="--workload heads: the form of the scan")
+    ap.add_argument("--config", type=int, choices=(0, 1, 2, 3, 4), default=WORKLOAD,
+                    help="--workload scan: the config timed (default: the Mamba-1.4B layer)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -653,18 +657,21 @@ def main():
     import ssmgen
     import selective_state_space_24_amd as ssm
 
-    cfg = ssmgen.CONFIGS[WORKLOAD]
+    cfg = ssmgen.CONFIGS[args.config]
     dev = device_inputs(cfg, torch)
     y = torch.empty_like(dev["x"])
     stream = torch.cuda.current_stream()
-    desc = ssm.describe(dev["x"], dev["delta"], dev["A"], dev["B"], dev["C"], dev["z"], y)
+    desc = ssm.describe(dev["x"], dev["delta"], dev["A"], dev["B"], dev["C"], dev.get("z"), y)
     ws_bytes = ssm.workspace_size(desc)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
 
+    def ptr(name):
+        t = dev.get(name)
+        return t.data_ptr() if t is not None else None
+
     def step():
-        rc = ssm.fwd_raw(desc, dev["x"].data_ptr(), dev["delta"].data_ptr(), dev["A"].data_ptr(),
-                         dev["B"].data_ptr(), dev["C"].data_ptr(), dev["D"].data_ptr(),
-                         dev["z"].data_ptr(), dev["delta_bias"].data_ptr(), True, y.data_ptr(),
+        rc = ssm.fwd_raw(desc, ptr("x"), ptr("delta"), ptr("A"), ptr("B"), ptr("C"), ptr("D"),
+                         ptr("z"), ptr("delta_bias"), cfg.softplus, y.data_ptr(),
                          ws.data_ptr() if ws_bytes else None, ws_bytes, stream.cuda_stream)
         if rc != 0:
             raise ssm.ScanError(rc, "ssm_selective_scan_fwd")
@@ -681,7 +688,7 @@ def main():
     peak = alu_peak_tflops(cfg)
     launch_ms = ms if launches == 1 else None
     achieved = alg_flops / (launch_ms * 1e-3) / 1e12 if launch_ms else None
-    traffic = traffic_from_profile("mamba14b_layer")
+    traffic = traffic_from_profile("mamba14b_layer") if args.config == WORKLOAD else None
     hbm_gbs = alg_bytes / (launch_ms * 1e-3) / 1e9 if launch_ms else None
     out = {
         "metric": "selective-scan Gtoken\u00b7channel/s and achieved HBM GB/s vs peak, 1 MI355X",
@@ -694,13 +701,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32 arithmetic and state, bf16 io",
+        "dtype": f"f32 arithmetic and state, {cfg.io} io",
         "data": "synthetic",
         "config": {
-            "workload": "Mamba-1.4B layer selective scan (S6 forward)",
+            "workload": ("Mamba-1.4B layer selective scan (S6 forward)" if args.config == WORKLOAD
+                         else f"selective scan (S6 forward), {cfg.name}"),
             "batch": cfg.batch, "d_inner": cfg.dim, "seq_len": cfg.L, "d_state": cfg.N,
-            "io_dtype": cfg.io, "gate": "silu(z)", "delta_softplus": cfg.softplus,
-            "parallelism": "single GPU",
+            "io_dtype": cfg.io, "gate": "silu(z)" if cfg.gate else None,
+            "delta_softplus": cfg.softplus, "parallelism": "single GPU",
         },
         "roofline": {
             "bound": "hbm",
