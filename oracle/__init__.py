@@ -47,6 +47,8 @@ def load_library(path: str):
     lib.ssm_oracle_scan.restype = ci
     lib.ssm_oracle_scan_bwd.argtypes = [i64, i64, i64, i64, i64, i64, ci, ci, ci] + [_dp] * 20 + [ci]
     lib.ssm_oracle_scan_bwd.restype = ci
+    lib.ssm_oracle_scan_complex.argtypes = [i64, i64, i64, i64, i64, ci] + [_dp] * 12 + [ci]
+    lib.ssm_oracle_scan_complex.restype = ci
     return lib
 
 
@@ -151,6 +153,27 @@ def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta
     if rc != 0:
         raise ValueError("oracle backward rejected the problem sizes")
     return out
+
+
+def selective_scan_complex(x, delta, A, B, C, D=None, z=None, delta_bias=None,
+                           delta_softplus=True, *, nthreads=None, lib=None):
+    """y of the complex-A scan (ssm_oracle.c, complex section): A complex (dim, N); B, C
+    complex (batch, ngroups, N, L); x, delta, z real (batch, dim, L); D, delta_bias (dim,)."""
+    lib = lib or _load()
+    x, delta = as_f64(x), as_f64(delta)
+    A, B, C = (np.ascontiguousarray(np.asarray(v, dtype=np.complex128)) for v in (A, B, C))
+    batch, dim, L = x.shape
+    ngroups, N = B.shape[1], B.shape[2]
+    parts = [np.ascontiguousarray(v) for v in (A.real, A.imag, B.real, B.imag, C.real, C.imag)]
+    D, z, delta_bias = as_f64(D), as_f64(z), as_f64(delta_bias)
+    y = np.empty((batch, dim, L), dtype=np.float64)
+    rc = lib.ssm_oracle_scan_complex(batch, dim, L, N, ngroups, int(bool(delta_softplus)),
+                                     _ptr(x), _ptr(delta), *[_ptr(v) for v in parts], _ptr(D),
+                                     _ptr(z), _ptr(delta_bias), _ptr(y),
+                                     nthreads or cpu_threads())
+    if rc != 0:
+        raise ValueError(f"ssm_oracle_scan_complex: bad sizes (rc {rc})")
+    return y
 
 
 def scan_inputs_bwd(inputs: dict, dy, cfg=None, **kw) -> dict:

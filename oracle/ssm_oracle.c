@@ -371,3 +371,99 @@ int ssm_oracle_scan_bwd(int64_t batch, int64_t dim, int64_t L, int64_t N, int64_
   free(dA_b); free(dD_b); free(dbias_b);
   return rc;
 }
+
+/* ------------------------------------------------------------------------------------------
+ * Complex diagonal A. The memo page's Figure 10 caption compares SSM parameterisations on audio
+ * and stresses that complex-valued parameters matter there; the pages give no formula for that
+ * case. The reading taken here is the recurrence above with complex numbers:
+ *   A_n complex per (channel, state); B_tn, C_tn complex (input-dependent, per group);
+ *   delta, x, z real;  A_bar = exp(delta A) (complex exponential), B_bar = delta B;
+ *   h_t = A_bar_t h_{t-1} + B_bar_t x_t (complex state);  y_t = Re(sum_n C_tn h_tn) + D x_t,
+ *   times silu(z_t).
+ * Layouts (fp64): Ar, Ai [dim][N]; Br, Bi, Cr, Ci [batch][ngroups][N][L]; the rest as above.
+ * -------------------------------------------------------------------------------------------*/
+#include <complex.h>
+
+typedef struct {
+  int64_t batch, dim, L, N, ngroups;
+  int delta_softplus;
+  const double *x, *delta, *Ar, *Ai, *Br, *Bi, *Cr, *Ci, *D, *z, *delta_bias;
+  double* y;
+} complex_problem;
+
+static void scan_channel_complex(const complex_problem* p, int64_t b, int64_t d,
+                                 double complex* h) {
+  const int64_t L = p->L, N = p->N;
+  const int64_t group = d / (p->dim / p->ngroups);
+  const double* xr = p->x + (b * p->dim + d) * L;
+  const double* dr = p->delta + (b * p->dim + d) * L;
+  const int64_t goff = (b * p->ngroups + group) * N * L;
+  const double* zr = p->z ? p->z + (b * p->dim + d) * L : NULL;
+  double* yr = p->y + (b * p->dim + d) * L;
+  const double bias = p->delta_bias ? p->delta_bias[d] : 0.0;
+  const double Dd = p->D ? p->D[d] : 0.0;
+
+  for (int64_t n = 0; n < N; ++n) h[n] = 0.0;
+  for (int64_t t = 0; t < L; ++t) {
+    const double v = dr[t] + bias;
+    const double delta = p->delta_softplus ? softplus(v) : v;
+    const double xt = xr[t];
+    double acc = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+      const double complex a = p->Ar[d * N + n] + I * p->Ai[d * N + n];
+      const double complex Bt = p->Br[goff + n * L + t] + I * p->Bi[goff + n * L + t];
+      const double complex Ct = p->Cr[goff + n * L + t] + I * p->Ci[goff + n * L + t];
+      const double complex Abar = cexp(delta * a);
+      const double complex Bbar = delta * Bt;
+      h[n] = Abar * h[n] + Bbar * xt;
+      acc += creal(Ct * h[n]);
+    }
+    double yt = acc + Dd * xt;
+    if (zr) yt *= silu(zr[t]);
+    yr[t] = yt;
+  }
+}
+
+typedef struct { const complex_problem* p; int64_t lo, hi; } complex_part;
+
+static void* complex_worker(void* arg) {
+  complex_part* w = (complex_part*)arg;
+  double complex hbuf[1024];
+  for (int64_t c = w->lo; c < w->hi; ++c)
+    scan_channel_complex(w->p, c / w->p->dim, c % w->p->dim, hbuf);
+  return NULL;
+}
+
+/* The complex-A scan for every (b, d) channel over nthreads threads; 0, or -1 on bad sizes. */
+int ssm_oracle_scan_complex(int64_t batch, int64_t dim, int64_t L, int64_t N, int64_t ngroups,
+                            int delta_softplus, const double* x, const double* delta,
+                            const double* Ar, const double* Ai, const double* Br,
+                            const double* Bi, const double* Cr, const double* Ci,
+                            const double* D, const double* z, const double* delta_bias, double* y,
+                            int nthreads) {
+  if (batch < 0 || dim < 1 || L < 0 || N < 1 || N > 1024 || ngroups < 1 || dim % ngroups) return -1;
+  if (!x || !delta || !Ar || !Ai || !Br || !Bi || !Cr || !Ci || !y) return -1;
+  complex_problem p = {batch, dim, L, N, ngroups, delta_softplus, x, delta, Ar, Ai, Br, Bi,
+                       Cr, Ci, D, z, delta_bias, y};
+  const int64_t channels = batch * dim;
+  if (channels == 0) return 0;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  if ((int64_t)nthreads > channels) nthreads = (int)channels;
+  pthread_t th[256];
+  complex_part parts[256];
+  int started[256] = {0};
+  const int64_t per = (channels + nthreads - 1) / nthreads;
+  for (int t = 0; t < nthreads; ++t) {
+    parts[t].p = &p;
+    parts[t].lo = per * t;
+    parts[t].hi = per * (t + 1) < channels ? per * (t + 1) : channels;
+    if (parts[t].lo >= parts[t].hi) continue;
+    if (nthreads == 1 || pthread_create(&th[t], NULL, complex_worker, &parts[t]) != 0)
+      complex_worker(&parts[t]);
+    else
+      started[t] = 1;
+  }
+  for (int t = 0; t < nthreads; ++t) if (started[t]) pthread_join(th[t], NULL);
+  return 0;
+}

@@ -2,7 +2,8 @@
 
 Forward mutants edit the forward section of the source (before the backward section's marker)
 and must fail a forward pin; backward mutants edit the backward section and must fail a
-backward pin (finite differences, torch autograd or the transposed-matrix closed form)."""
+backward pin (finite differences, torch autograd or the transposed-matrix closed form); complex
+mutants edit the complex-A section and must fail a complex pin."""
 import os
 import subprocess
 
@@ -10,10 +11,12 @@ import pytest
 
 import oracle
 import oracle_bwd_pins as BP
+import oracle_complex_pins as CP
 import oracle_pins as P
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ssm_oracle.c")
 BWD_MARK = "Gradients of the scan above"
+COMPLEX_MARK = "Complex diagonal A."
 
 MUTANTS = {
     "drop_D": ("double yt = acc + Dd * xt;", "double yt = acc;"),
@@ -48,6 +51,20 @@ BWD_MUTANTS = {
     "bwd_gate_not_applied": ("gy = gyr[t] * zr[t] * s;", "gy = gyr[t];"),
     "bwd_final_state_gradient_dropped": ("gh[n] = q->dh_final ? q->dh_final[(b * p->dim + d) * N + n] : 0.0;",
                                          "gh[n] = 0.0;"),
+}
+
+
+COMPLEX_MUTANTS = {
+    "cplx_conjugated_readout": ("acc += creal(Ct * h[n]);", "acc += creal(conj(Ct) * h[n]);"),
+    "cplx_imaginary_readout": ("acc += creal(Ct * h[n]);", "acc += cimag(Ct * h[n]);"),
+    "cplx_decay_without_rotation": ("cexp(delta * a)", "exp(delta * creal(a))"),
+    "cplx_exp_sign": ("cexp(delta * a)", "cexp(-delta * a)"),
+    "cplx_B_real_part_only": ("const double complex Bbar = delta * Bt;",
+                              "const double complex Bbar = delta * creal(Bt);"),
+    "cplx_A_conjugated": ("p->Ar[d * N + n] + I * p->Ai[d * N + n]",
+                          "p->Ar[d * N + n] - I * p->Ai[d * N + n]"),
+    "cplx_C_imag_sign": ("p->Cr[goff + n * L + t] + I * p->Ci[goff + n * L + t]",
+                         "p->Cr[goff + n * L + t] - I * p->Ci[goff + n * L + t]"),
 }
 
 
@@ -103,3 +120,18 @@ def test_mutant_is_caught(name, src, tmp_path):
     res = P.run_all(scan)
     failed = [k for k, (_, ok) in res.items() if not ok]
     assert failed, f"mutant {name} passed every pin"
+
+
+@pytest.mark.parametrize("name", sorted(COMPLEX_MUTANTS))
+def test_complex_mutant_is_caught(name, src, tmp_path):
+    old, new = COMPLEX_MUTANTS[name]
+    cut = src.index(COMPLEX_MARK)
+    head, tail = src[:cut], src[cut:]
+    assert tail.count(old) == 1, f"mutation site not found exactly once: {old!r}"
+    lib = _build(tmp_path, name, head + tail.replace(old, new))
+
+    def scan(*a, **k):
+        return oracle.selective_scan_complex(*a, lib=lib, **k)
+    res = CP.run_all(scan)
+    failed = [k for k, (_, ok) in res.items() if not ok]
+    assert failed, f"complex mutant {name} passed every pin"
