@@ -21,6 +21,9 @@ entries of the same workload.
 N 128, L 8192, bf16 I/O) in its chunked matrix form on the matrix cores (``--algorithm
 recurrent`` for the step-by-step recurrence instead); its roofline is HBM bandwidth, with the
 algorithmic matrix flops reported beside it against the bf16 MFMA peak.
+``--workload complex`` measures the scan with a complex diagonal A (complex A, B and C; batch 8,
+d_inner 1536, N 16, L 2048, bf16 I/O): its roofline is the fp32 VALU issue of its instruction mix
+(exp2, sin and cos per state update), with the HBM figures beside it.
 ``--workload decode`` measures instead one recurrent decoding step (``ssm_selective_state_update``)
 on the Mamba-1.4B layer at batch 1024: a step reads and writes the fp32 state once, so its
 roofline is HBM bandwidth. ``--workload lsweep`` times the scan at a fixed batch x channels
@@ -101,7 +104,8 @@ def alu_model(cfg):
     costs (1 and 2 four-cycle units per instruction). Flops count an fma as 2 and every other
     operation, transcendentals included, as 1.
       per state update (t, channel, n): delta*a, exp2, u*B, h fma, readout fma -> 7 flops, 24 cyc
-        (head mode: delta*a and exp2 once per (t, head) instead)
+        (head mode: delta*a and exp2 once per (t, head) instead; complex A: 13 fp32 ops and
+        exp2, sin, cos -> 22 flops, 76 cyc)
       per (t, channel): bias add (1, 4), softplus (10, 44: |v|*log2e, exp2, 1+e, log2, two
         subtractions of the log1p correction, fma, max, add), u = delta*x (1, 4), D skip fma
         (2, 4), silu gate (6, 32: z*log2e, exp2, 1+e, rcp, z*r, y*g)
@@ -111,7 +115,12 @@ def alu_model(cfg):
     head = cfg.a_mode == "head"
     rows_per_ch = 1.0 / cfg.headdim if head else 1.0
     fl = cy = 0.0
-    if head:
+    if cfg.a_mode == "complex":
+        # delta*Re(A), exp2, delta*Im(A), whole turns dropped, sin, cos, |Abar| cos, |Abar| sin,
+        # delta*x*B (two parts), the complex update (4 fma), Re(C h) (2 fma)
+        fl += cfg.N * 22
+        cy += cfg.N * (13 * valu + 3 * trans)
+    elif head:
         fl += cfg.N * 5 + 2 * rows_per_ch
         cy += cfg.N * 3 * valu + (valu + trans) * rows_per_ch
     else:
@@ -143,7 +152,7 @@ def alu_peak_tflops(cfg) -> float:
     return fl * 64 / cy * SIMDS * CLOCK_HZ / 1e12
 
 
-def cpu_baseline(cfg, budget_s: float):
+def cpu_baseline(cfg, budget_s: float, scan=None):
     """The fp64 oracle, as it stands, over whole batch entries of the workload (inputs of one
     entry generated untimed, then the oracle timed on them), until every entry is done or the
     time budget is spent."""
@@ -155,7 +164,7 @@ def cpu_baseline(cfg, budget_s: float):
         inputs = ssmgen.make_batch_entry(cfg, b)
         one = ssmgen.with_shape(cfg, batch=1)
         t0 = time.perf_counter()
-        oracle.scan_inputs(inputs, one, nthreads=threads)
+        (scan or oracle.scan_inputs)(inputs, one, nthreads=threads)
         spent += time.perf_counter() - t0
         done += 1
         del inputs
@@ -594,6 +603,65 @@ def run_lsweep(args, torch):
     print(json.dumps(out), flush=True)
 
 
+def run_complex(args, torch):
+    import oracle
+    import ssmgen
+    import selective_state_space_24_amd as ssm
+    cfg = ssmgen.COMPLEX_CONFIG
+    dev = device_inputs(cfg, torch)
+    y = torch.empty_like(dev["x"])
+    stream = torch.cuda.current_stream()
+    desc = ssm.describe(dev["x"], dev["delta"], dev["A"], dev["B"], dev["C"], dev["z"], y)
+
+    def step():
+        rc = ssm.fwd_raw(desc, dev["x"].data_ptr(), dev["delta"].data_ptr(), dev["A"].data_ptr(),
+                         dev["B"].data_ptr(), dev["C"].data_ptr(), dev["D"].data_ptr(),
+                         dev["z"].data_ptr(), dev["delta_bias"].data_ptr(), True, y.data_ptr(),
+                         None, 0, stream.cuda_stream)
+        if rc != 0:
+            raise ssm.ScanError(rc, "ssm_selective_scan_fwd")
+
+    ms, pct = timed_steps(step, args, torch, stream)
+    fl, cy = alu_model(cfg)
+    achieved = fl * cfg.tokch / (ms * 1e-3) / 1e12
+    peak = alu_peak_tflops(cfg)
+    nbytes = cfg.algorithmic_bytes()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "selective-scan Gtoken\u00b7channel/s and achieved HBM GB/s vs peak, 1 MI355X",
+        "value": round(cfg.tokch / (ms * 1e-3) / 1e9, 3),
+        "unit": "Gtoken\u00b7channel/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": f"f32 arithmetic and complex state, {cfg.io} io", "data": "synthetic",
+        "config": {"workload": "selective scan with a complex diagonal A (complex A, B, C; "
+                               "real delta, x, z)",
+                   "batch": cfg.batch, "d_inner": cfg.dim, "seq_len": cfg.L, "d_state": cfg.N,
+                   "io_dtype": cfg.io, "gate": "silu(z)", "delta_softplus": cfg.softplus},
+        # the kernel is bound by VALU issue: the peak is that of its own instruction mix at full
+        # issue on 1024 SIMDs at 2.4 GHz (alu_model)
+        "roofline": {"bound": "alu", "achieved": round(achieved, 2), "peak": round(peak, 2),
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic_from_profile("complex_layer"),
+                     "derivation": (f"per 64 token*channels: {cfg.N} complex state updates x "
+                                    f"(13 fp32 ops x {VALU_CYCLES} cycles + exp2, sin, cos x "
+                                    f"{TRANS_CYCLES} cycles) + bias, softplus, delta*x, D skip "
+                                    f"and silu gate = {cy:.0f} SIMD cycles for {fl:.0f} flops; "
+                                    f"1024 SIMDs at 2.4 GHz")},
+        "hbm": {"algorithmic_bytes": nbytes, "achieved_GBs": round(gbs, 1),
+                "peak_GBs": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4)},
+        "step_ms": {"p10": round(pct(0.1), 5), "median": round(pct(0.5), 5),
+                    "p90": round(pct(0.9), 5)},
+        "launches_per_step": 1,
+        "kernel_source": kernel_source_hash(),
+    }
+    if args.cpu_budget > 0:
+        del dev, y
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget, scan=oracle.scan_inputs_complex)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -606,7 +674,7 @@ def main():
                     help="seconds of oracle work for the CPU baseline (0 skips it)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--workload", choices=("scan", "decode", "bwd", "bwd-heads", "heads",
-                                           "lsweep"), default="scan")
+                                           "lsweep", "complex"), default="scan")
     ap.add_argument("--algorithm", choices=("chunked", "recurrent"), default="chunked",
                     help="--workload heads: the form of the scan")
     ap.add_argument("--config", type=int, choices=(0, 1, 2, 3, 4), default=WORKLOAD,
@@ -652,6 +720,9 @@ def main():
         return
     if args.workload == "lsweep":
         run_lsweep(args, torch)
+        return
+    if args.workload == "complex":
+        run_complex(args, torch)
         return
 
     import ssmgen

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_ABI_VERSION 5
+#define SSM_SCAN_ABI_VERSION 6
 
 typedef enum {
   SSM_OK = 0,
@@ -76,9 +76,21 @@ typedef enum {
 typedef enum { SSM_DTYPE_F32 = 0, SSM_DTYPE_BF16 = 1 } ssm_dtype;
 
 typedef enum {
-  SSM_A_DIAG = 0, /* A is (dim, dstate): a diagonal A per channel, delta per channel */
-  SSM_A_HEAD = 1  /* A is one scalar per head; delta and delta_bias per head */
+  SSM_A_DIAG = 0,   /* A is (dim, dstate): a diagonal A per channel, delta per channel */
+  SSM_A_HEAD = 1,   /* A is one scalar per head; delta and delta_bias per head */
+  SSM_A_COMPLEX = 2 /* A is (dim, dstate) complex, stored as (dim, dstate, 2) fp32 pairs
+                       (real, imaginary); B and C are complex: each (batch, group) holds 2*dstate
+                       rows, the real parts at state rows 0..dstate-1 and the imaginary parts at
+                       rows dstate..2*dstate-1 (B_stride_state / C_stride_state between rows);
+                       the state is complex and y_t = Re(sum_n C_tn h_tn) + D x_t (times the
+                       gate). delta, delta_bias as in SSM_A_DIAG; headdim must be 1. The memo
+                       page's Figure 10 caption compares SSM parameterisations and stresses
+                       complex-valued parameters; the pages give no formula, so the recurrence
+                       above is taken over complex numbers. Forward scan only (see
+                       ssm_selective_scan_fwd_ext); dstate <= SSM_MAX_COMPLEX_DSTATE. */
 } ssm_a_mode;
+
+#define SSM_MAX_COMPLEX_DSTATE 32
 
 #define SSM_MAX_DSTATE 128
 
@@ -101,7 +113,7 @@ typedef struct ssm_scan_desc {
 } ssm_scan_desc;
 
 /* Fills `desc` with the contiguous layout of the given sizes (strides as listed above, L
- * innermost). Returns SSM_ERR_NULL_ARG for a NULL desc, else SSM_OK; sizes are checked by the
+ * innermost; with SSM_A_COMPLEX, B and C have 2 * dstate rows per group). Returns SSM_ERR_NULL_ARG for a NULL desc, else SSM_OK; sizes are checked by the
  * calls that use the descriptor. */
 int ssm_scan_desc_init_contiguous(ssm_scan_desc* desc, int64_t batch, int64_t dim, int64_t seqlen,
                                   int64_t dstate, int64_t ngroups, int64_t headdim,
@@ -163,14 +175,18 @@ typedef struct ssm_scan_ext {
 } ssm_scan_ext;
 
 /* ssm_selective_scan_fwd with the options above (`ext` may be NULL). With seqlen == 0, y is not
- * touched and h_final receives h0 (or zeros). The workspace size does not depend on `ext`. */
+ * touched and h_final receives h0 (or zeros). The workspace size does not depend on `ext`.
+ * a_mode SSM_A_COMPLEX takes the delta * B rule, no h0 or h_final and the recurrent algorithm
+ * (AUTO or RECURRENT), with dstate <= SSM_MAX_COMPLEX_DSTATE; it needs no workspace. Any other
+ * option with it returns SSM_ERR_UNSUPPORTED. */
 int ssm_selective_scan_fwd_ext(const ssm_scan_desc* desc, const void* x, const void* delta,
                                const float* A, const void* B, const void* C, const float* D,
                                const void* z, const float* delta_bias, int32_t delta_softplus,
                                void* y, const ssm_scan_ext* ext, void* workspace,
                                size_t workspace_bytes, void* stream);
 
-/* One recurrent step per sequence, for decoding one token at a time: the state carries the
+/* One recurrent step per sequence, for decoding one token at a time (a_mode DIAG or HEAD; COMPLEX
+ * returns SSM_ERR_UNSUPPORTED): the state carries the
  * whole history, so each step costs the same whatever the position (page "NL-345", §1
  * "Selection Mechanism" and §2 "Computation": the recurrent mode of a selective SSM).
  *   `desc` describes a scan with seqlen == 1 (SSM_ERR_BAD_SHAPE otherwise): x, delta, z, y are
@@ -203,7 +219,8 @@ int ssm_selective_scan_bwd_workspace_size(const ssm_scan_desc* desc, size_t* byt
  *              the batch (and over each head's channels in A_HEAD mode)
  *   dh0      : nullable, (batch, dim, dstate) fp32: the gradient of the initial state
  *   workspace: at least ssm_selective_scan_bwd_workspace_size bytes, 4-byte aligned
- * Every a_mode, io dtype and dstate (up to 128) is supported. Outputs must not overlap any input
+ * The a_modes DIAG and HEAD, every io dtype and dstate up to 128 are supported (COMPLEX returns
+ * SSM_ERR_UNSUPPORTED). Outputs must not overlap any input
  * or each other. Because dx, ddelta, dz, dB and dC are written with the strides of x, delta, z,
  * B and C, those strides must give disjoint rows (as y's must in the forward call; a stride-0
  * broadcast of B, say, returns SSM_ERR_BAD_STRIDE). Results are deterministic (fixed-order

@@ -7,8 +7,9 @@ task); this module only converts arrays to fp64 and calls it.
 
 Pinned by the CPU tests (closed-form geometric series, B = 0 skip path, brute-force
 semiseparable matrix, LTI convolution kernel, Theorem 1 gated-RNN form, linearity, causality,
-segment composition, head-mode broadcast, the A = 0 and large-step limits). Nothing here is
-parity-unpinned.
+segment composition, head-mode broadcast, the A = 0 and large-step limits; for the complex-A
+scan: the real reduction, a closed form in Python's cmath, a rotating phasor, the materialised
+semiseparable matrix and conjugation symmetry). Nothing here is parity-unpinned.
 """
 from __future__ import annotations
 
@@ -174,6 +175,22 @@ def selective_scan_complex(x, delta, A, B, C, D=None, z=None, delta_bias=None,
     if rc != 0:
         raise ValueError(f"ssm_oracle_scan_complex: bad sizes (rc {rc})")
     return y
+
+
+def scan_inputs_complex(inputs: dict, cfg=None, **kw):
+    """``selective_scan_complex`` on a dict of generated inputs in the library's layout: A as
+    (dim, N, 2) (real, imaginary) pairs, B and C as (batch, ngroups, 2N, L) with the real parts
+    in rows 0..N-1 and the imaginary parts in rows N..2N-1."""
+    if cfg is not None:
+        kw.setdefault("delta_softplus", cfg.softplus)
+    A = np.asarray(inputs["A"], dtype=np.float64)
+    A = A[..., 0] + 1j * A[..., 1]
+    N = A.shape[1]
+    B, C = as_f64(inputs["B"]), as_f64(inputs["C"])
+    B = B[:, :, :N] + 1j * B[:, :, N:]
+    C = C[:, :, :N] + 1j * C[:, :, N:]
+    return selective_scan_complex(inputs["x"], inputs["delta"], A, B, C, inputs.get("D"),
+                                  inputs.get("z"), inputs.get("delta_bias"), **kw)
 
 
 def scan_inputs_bwd(inputs: dict, dy, cfg=None, **kw) -> dict:

@@ -17,11 +17,12 @@ LIB_PATH = os.path.join(_PKG, "lib", "libssm_scan.so")
 
 SSM_OK = 0
 SSM_DTYPE_F32, SSM_DTYPE_BF16 = 0, 1
-SSM_A_DIAG, SSM_A_HEAD = 0, 1
+SSM_A_DIAG, SSM_A_HEAD, SSM_A_COMPLEX = 0, 1, 2
 SSM_DISC_DELTA_B, SSM_DISC_ZOH = 0, 1
 SSM_ALGO_AUTO, SSM_ALGO_RECURRENT, SSM_ALGO_CHUNKED = 0, 1, 2
 ALGORITHMS = {"auto": SSM_ALGO_AUTO, "recurrent": SSM_ALGO_RECURRENT, "chunked": SSM_ALGO_CHUNKED}
 SSM_MAX_DSTATE = 128
+SSM_MAX_COMPLEX_DSTATE = 32
 
 STATUS_NAMES = {
     0: "SSM_OK", -1: "SSM_ERR_NULL_ARG", -2: "SSM_ERR_BAD_SHAPE", -3: "SSM_ERR_BAD_DTYPE",
@@ -203,7 +204,12 @@ def _ptr(t) -> Optional[int]:
 
 def describe(x, delta, A, B, C, z=None, y=None) -> ScanDesc:
     """Descriptor of torch tensors: x (batch, dim, L), delta (batch, dim | nheads, L),
-    A (dim, N) or (nheads,), B/C (batch, ngroups, N, L), z and y like x."""
+    A (dim, N) or (nheads,), B/C (batch, ngroups, N, L), z and y like x.
+
+    A complex A, either a complex64 (dim, N) tensor or a float32 (dim, N, 2) tensor of
+    (real, imaginary) pairs, selects SSM_A_COMPLEX: B and C are then real tensors of shape
+    (batch, ngroups, 2N, L), the real parts in rows 0..N-1 and the imaginary parts in rows N..2N-1.
+    """
     import torch
     if x.dtype == torch.bfloat16:
         io = SSM_DTYPE_BF16
@@ -214,13 +220,23 @@ def describe(x, delta, A, B, C, z=None, y=None) -> ScanDesc:
     for name, t in (("delta", delta), ("B", B), ("C", C), ("z", z), ("y", y)):
         if t is not None and t.dtype != x.dtype:
             raise TypeError(f"{name} has dtype {t.dtype}, expected {x.dtype}")
+    if A.dtype == torch.complex64:
+        A = torch.view_as_real(A)
     if A.dtype != torch.float32:
-        raise TypeError("A must be float32")
+        raise TypeError("A must be float32 (or complex64)")
     if x.dim() != 3 or delta.dim() != 3 or B.dim() != 4 or C.dim() != 4:
         raise ValueError("expected x/delta (batch, rows, L) and B/C (batch, groups, N, L)")
     batch, dim, L = x.shape
     ngroups, N = B.shape[1], B.shape[2]
-    if A.dim() == 1:
+    bc_rows = N
+    if A.dim() == 3:
+        a_mode, headdim = SSM_A_COMPLEX, 1
+        if B.shape[2] % 2:
+            raise ValueError("complex A: B and C need 2N rows (real parts, then imaginary)")
+        N = B.shape[2] // 2
+        if tuple(A.shape) != (dim, N, 2):
+            raise ValueError(f"complex A must be (dim, N) = {(dim, N)}, got {tuple(A.shape[:2])}")
+    elif A.dim() == 1:
         a_mode = SSM_A_HEAD
         nheads = A.shape[0]
         if nheads == 0 or dim % nheads:
@@ -231,12 +247,13 @@ def describe(x, delta, A, B, C, z=None, y=None) -> ScanDesc:
         if tuple(A.shape) != (dim, N):
             raise ValueError(f"A must be (dim, N) = {(dim, N)}, got {tuple(A.shape)}")
     else:
-        raise ValueError("A must be (dim, N) or (nheads,)")
+        raise ValueError("A must be (dim, N), (nheads,) or complex (dim, N)")
     rows = dim // headdim
     if tuple(delta.shape) != (batch, rows, L):
         raise ValueError(f"delta must be {(batch, rows, L)}, got {tuple(delta.shape)}")
-    if tuple(B.shape) != (batch, ngroups, N, L) or tuple(C.shape) != (batch, ngroups, N, L):
-        raise ValueError("B and C must both be (batch, ngroups, N, L)")
+    if (tuple(B.shape) != (batch, ngroups, bc_rows, L)
+            or tuple(C.shape) != (batch, ngroups, bc_rows, L)):
+        raise ValueError(f"B and C must both be (batch, ngroups, {bc_rows}, L)")
     for name, t in (("x", x), ("delta", delta), ("B", B), ("C", C), ("z", z), ("y", y)):
         if t is not None and t.shape[-1] > 1 and t.stride(-1) != 1:
             raise ValueError(f"{name} must have unit stride along L")

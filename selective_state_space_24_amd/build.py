@@ -15,7 +15,7 @@ LIB = os.path.join(LIBDIR, "libssm_scan.so")
 SOURCES = ["scan_fwd_bf16_diag.hip", "scan_fwd_bf16_head.hip", "scan_fwd_f32_diag.hip",
            "scan_fwd_f32_head.hip", "scan_state.hip", "scan_decode.hip",
            "scan_bwd.hip", "scan_bwd_wide_bf16.hip", "scan_bwd_wide_f32.hip", "scan_ssd.hip",
-           "scan_noalloc.hip", "scan_api.cpp"]
+           "scan_noalloc.hip", "scan_complex.hip", "scan_api.cpp"]
 
 # Packed fp32 instructions are switched off for all device code.
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -72,15 +72,22 @@ bool rows_disjoint3(int64_t n0, int64_t n1, int64_t L, int64_t s0, int64_t s1) {
   return rows_disjoint(2, n, s, L);
 }
 
+// rows of B and C per (batch, group): dstate, or 2 dstate (real, then imaginary parts) with a
+// complex A
+int64_t bc_rows(const ssm_scan_desc* d) {
+  return d->a_mode == SSM_A_COMPLEX ? 2 * d->dstate : d->dstate;
+}
+
 int check_desc(const ssm_scan_desc* d) {
   if (!d) return SSM_ERR_NULL_ARG;
   if (d->io_dtype != SSM_DTYPE_F32 && d->io_dtype != SSM_DTYPE_BF16) return SSM_ERR_BAD_DTYPE;
-  if (d->a_mode != SSM_A_DIAG && d->a_mode != SSM_A_HEAD) return SSM_ERR_BAD_DTYPE;
+  if (d->a_mode != SSM_A_DIAG && d->a_mode != SSM_A_HEAD && d->a_mode != SSM_A_COMPLEX)
+    return SSM_ERR_BAD_DTYPE;
   if (d->batch < 0 || d->seqlen < 0 || d->dim < 1 || d->dstate < 1 || d->dstate > SSM_MAX_DSTATE ||
       d->ngroups < 1 || d->headdim < 1)
     return SSM_ERR_BAD_SHAPE;
   if (d->dim % d->ngroups || d->dim % d->headdim) return SSM_ERR_BAD_SHAPE;
-  if (d->a_mode == SSM_A_DIAG && d->headdim != 1) return SSM_ERR_BAD_SHAPE;
+  if (d->a_mode != SSM_A_HEAD && d->headdim != 1) return SSM_ERR_BAD_SHAPE;
   int64_t t;
   if (!mul_ok(d->batch, d->dim, &t) || !mul_ok(t, d->seqlen, &t) || !mul_ok(t, d->dstate, &t))
     return SSM_ERR_BAD_SHAPE;
@@ -99,9 +106,9 @@ int check_desc(const ssm_scan_desc* d) {
       extent3(d->batch, drows, d->seqlen, d->delta_stride_batch, d->delta_stride_dim) < 0 ||
       extent3(d->batch, d->dim, d->seqlen, d->z_stride_batch, d->z_stride_dim) < 0 ||
       extent3(d->batch, d->dim, d->seqlen, d->y_stride_batch, d->y_stride_dim) < 0 ||
-      extent4(d->batch, d->ngroups, d->dstate, d->seqlen, d->B_stride_batch, d->B_stride_group,
+      extent4(d->batch, d->ngroups, bc_rows(d), d->seqlen, d->B_stride_batch, d->B_stride_group,
               d->B_stride_state) < 0 ||
-      extent4(d->batch, d->ngroups, d->dstate, d->seqlen, d->C_stride_batch, d->C_stride_group,
+      extent4(d->batch, d->ngroups, bc_rows(d), d->seqlen, d->C_stride_batch, d->C_stride_group,
               d->C_stride_state) < 0)
     return SSM_ERR_BAD_SHAPE;
   return SSM_OK;
@@ -199,6 +206,78 @@ bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// The forward scan with a complex diagonal A (a_mode SSM_A_COMPLEX), after check_desc: the
+// delta * B rule, no initial or final state, the recurrent algorithm, dstate <= 32.
+int complex_fwd(const ssm_scan_desc& d, const void* x, const void* delta, const float* A,
+                const void* B, const void* C, const float* D, const void* z,
+                const float* delta_bias, int32_t delta_softplus, void* y, int32_t disc,
+                int32_t algo, const float* h0, const float* hfin, void* stream) {
+  if (disc != SSM_DISC_DELTA_B || algo == SSM_ALGO_CHUNKED || h0 || hfin ||
+      d.dstate > SSM_MAX_COMPLEX_DSTATE)
+    return SSM_ERR_UNSUPPORTED;
+  // the B and C of a workgroup's 64 channels come from one group
+  if (d.ngroups > 1 && (d.dim / d.ngroups) % ssm::kChannelsPerGroup != 0)
+    return SSM_ERR_UNSUPPORTED;
+  if (d.batch == 0 || d.seqlen == 0) return SSM_OK;
+  if (!x || !delta || !A || !B || !C || !y) return SSM_ERR_NULL_ARG;
+  const bool bf16 = d.io_dtype == SSM_DTYPE_BF16;
+  const size_t es = bf16 ? 2 : 4;
+  const void* io_ptrs[] = {x, delta, B, C, z, y};
+  for (const void* q : io_ptrs)
+    if (q && !aligned(q, es)) return SSM_ERR_MISALIGNED;
+  const void* f32_ptrs[] = {A, D, delta_bias};
+  for (const void* q : f32_ptrs)
+    if (q && !aligned(q, 4)) return SSM_ERR_MISALIGNED;
+  const size_t y_bytes =
+      (size_t)extent3(d.batch, d.dim, d.seqlen, d.y_stride_batch, d.y_stride_dim) * es;
+  const size_t in_bytes[] = {
+      (size_t)extent3(d.batch, d.dim, d.seqlen, d.x_stride_batch, d.x_stride_dim) * es,
+      (size_t)extent3(d.batch, d.dim, d.seqlen, d.delta_stride_batch, d.delta_stride_dim) * es,
+      (size_t)extent4(d.batch, d.ngroups, 2 * d.dstate, d.seqlen, d.B_stride_batch,
+                      d.B_stride_group, d.B_stride_state) * es,
+      (size_t)extent4(d.batch, d.ngroups, 2 * d.dstate, d.seqlen, d.C_stride_batch,
+                      d.C_stride_group, d.C_stride_state) * es,
+      z ? (size_t)extent3(d.batch, d.dim, d.seqlen, d.z_stride_batch, d.z_stride_dim) * es : 0,
+      (size_t)d.dim * d.dstate * 2 * 4,
+      D ? (size_t)d.dim * 4 : 0,
+      delta_bias ? (size_t)d.dim * 4 : 0};
+  const void* in_ptrs[] = {x, delta, B, C, z, A, D, delta_bias};
+  for (int i = 0; i < 8; ++i)
+    if (overlaps(y, y_bytes, in_ptrs[i], in_bytes[i])) return SSM_ERR_ALIAS;
+
+  ssm::ScanParams p;
+  memset(&p, 0, sizeof(p));
+  p.x = x; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.delta_bias = delta_bias;
+  p.y = y;
+  p.batch = d.batch; p.dim = d.dim; p.L = d.seqlen; p.N = d.dstate; p.ngroups = d.ngroups;
+  p.headdim = 1;
+  p.x_sb = d.x_stride_batch; p.x_sd = d.x_stride_dim;
+  p.dl_sb = d.delta_stride_batch; p.dl_sd = d.delta_stride_dim;
+  p.B_sb = d.B_stride_batch; p.B_sg = d.B_stride_group; p.B_sn = d.B_stride_state;
+  p.C_sb = d.C_stride_batch; p.C_sg = d.C_stride_group; p.C_sn = d.C_stride_state;
+  p.z_sb = d.z_stride_batch; p.z_sd = d.z_stride_dim;
+  p.y_sb = d.y_stride_batch; p.y_sd = d.y_stride_dim;
+  p.softplus = delta_softplus ? 1 : 0;
+  // 16-byte row access of x, delta, z, y: aligned bases, strides multiples of 16 bytes
+  const int64_t vec = 16 / (int64_t)es;
+  bool vec_ok = true;
+  const void* vptrs[] = {x, delta, z, y};
+  for (const void* q : vptrs)
+    if (q && !aligned(q, 16)) vec_ok = false;
+  for (int64_t st : {d.x_stride_batch, d.x_stride_dim, d.delta_stride_batch, d.delta_stride_dim,
+                     z ? d.z_stride_batch : 0, z ? d.z_stride_dim : 0, d.y_stride_batch,
+                     d.y_stride_dim})
+    if (st % vec) vec_ok = false;
+  p.vec_io = vec_ok ? 1 : 0;
+  bool bc_ok = aligned(B, 16) && aligned(C, 16);
+  for (int64_t st : {d.B_stride_batch, d.B_stride_group, d.B_stride_state, d.C_stride_batch,
+                     d.C_stride_group, d.C_stride_state})
+    if (st % vec) bc_ok = false;
+  p.bc_vec = bc_ok ? 1 : 0;
+  const hipError_t e = ssm::launch_complex(p, bf16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -232,7 +311,8 @@ int ssm_scan_desc_init_contiguous(ssm_scan_desc* d, int64_t batch, int64_t dim, 
   const int64_t rows = (a_mode == SSM_A_HEAD && headdim > 0) ? dim / headdim : dim;
   d->x_stride_dim = seqlen; d->x_stride_batch = dim * seqlen;
   d->delta_stride_dim = seqlen; d->delta_stride_batch = rows * seqlen;
-  d->B_stride_state = seqlen; d->B_stride_group = dstate * seqlen; d->B_stride_batch = ngroups * dstate * seqlen;
+  const int64_t bc = a_mode == SSM_A_COMPLEX ? 2 * dstate : dstate;  // B/C rows per group
+  d->B_stride_state = seqlen; d->B_stride_group = bc * seqlen; d->B_stride_batch = ngroups * bc * seqlen;
   d->C_stride_state = d->B_stride_state; d->C_stride_group = d->B_stride_group; d->C_stride_batch = d->B_stride_batch;
   d->z_stride_dim = seqlen; d->z_stride_batch = dim * seqlen;
   d->y_stride_dim = seqlen; d->y_stride_batch = dim * seqlen;
@@ -243,7 +323,8 @@ int ssm_selective_scan_workspace_size(const ssm_scan_desc* desc, size_t* bytes) 
   if (!bytes) return SSM_ERR_NULL_ARG;
   const int rc = check_desc(desc);
   if (rc != SSM_OK) return rc;
-  *bytes = workspace_bytes_for(desc, plan_segments(desc));
+  // the complex-A scan runs in one pass without workspace
+  *bytes = desc->a_mode == SSM_A_COMPLEX ? 0 : workspace_bytes_for(desc, plan_segments(desc));
   return SSM_OK;
 }
 
@@ -262,6 +343,9 @@ int ssm_selective_scan_fwd_ext(const ssm_scan_desc* desc, const void* x, const v
   const float* h0 = ext ? ext->h0 : nullptr;
   float* hfin = ext ? ext->h_final : nullptr;
   const ssm_scan_desc& d = *desc;
+  if (d.a_mode == SSM_A_COMPLEX)
+    return complex_fwd(d, x, delta, A, B, C, D, z, delta_bias, delta_softplus, y, disc, algo, h0,
+                       hfin, stream);
   if (d.batch == 0) return SSM_OK;  // nothing to compute or write
   if (d.seqlen == 0) {
     // no steps: the final state is the initial one (zero without h0)
@@ -396,6 +480,7 @@ int ssm_selective_state_update(const ssm_scan_desc* desc, float* state, const vo
   int rc = check_desc(desc);
   if (rc != SSM_OK) return rc;
   const ssm_scan_desc& d = *desc;
+  if (d.a_mode == SSM_A_COMPLEX) return SSM_ERR_UNSUPPORTED;
   if (d.seqlen != 1) return SSM_ERR_BAD_SHAPE;
   if (d.batch == 0) return SSM_OK;
   if (!state || !x || !delta || !A || !B || !C || !y) return SSM_ERR_NULL_ARG;
@@ -459,6 +544,7 @@ int ssm_selective_scan_bwd_workspace_size(const ssm_scan_desc* desc, size_t* byt
   if (!bytes) return SSM_ERR_NULL_ARG;
   const int rc = check_desc(desc);
   if (rc != SSM_OK) return rc;
+  if (desc->a_mode == SSM_A_COMPLEX) return SSM_ERR_UNSUPPORTED;
   *bytes = bwd_layout(desc).total;
   return SSM_OK;
 }
@@ -473,6 +559,7 @@ int ssm_selective_scan_bwd_ext(const ssm_scan_desc* desc, const void* x, const v
   int rc = check_desc(desc);
   if (rc != SSM_OK) return rc;
   const ssm_scan_desc& d = *desc;
+  if (d.a_mode == SSM_A_COMPLEX) return SSM_ERR_UNSUPPORTED;
   const int32_t disc = ext ? ext->discretization : SSM_DISC_DELTA_B;
   if (disc != SSM_DISC_DELTA_B && disc != SSM_DISC_ZOH) return SSM_ERR_BAD_DTYPE;
   const float* dhfin = ext ? ext->dh_final : nullptr;

@@ -22,7 +22,8 @@ _SO = os.path.join(_HERE, "libssmgen.so")
 NORMAL, UNIFORM, INV_SOFTPLUS_UNIFORM, NEG_ARANGE = 0, 1, 2, 3
 F64, F32, BF16 = 0, 1, 2
 
-TENSOR_IDS = {"x": 1, "delta": 2, "B": 3, "C": 4, "D": 5, "z": 6, "delta_bias": 7, "A": 8}
+TENSOR_IDS = {"x": 1, "delta": 2, "B": 3, "C": 4, "D": 5, "z": 6, "delta_bias": 7, "A": 8,
+              "A_imag": 9}
 SEED_BASE = 0x53534D5336323400
 
 
@@ -109,7 +110,9 @@ class ScanConfig:
     N: int            # state size per channel
     ngroups: int = 1  # B/C groups; channel d uses group d // (dim // ngroups)
     headdim: int = 1  # channels per head; >1 with a_mode == "head"
-    a_mode: str = "diag"  # "diag": A is (dim, N); "head": one scalar per head
+    a_mode: str = "diag"  # "diag": A is (dim, N); "head": one scalar per head; "complex": A is
+    #                       (dim, N) complex, stored (dim, N, 2), and B/C hold 2N rows per group
+    #                       (real parts, then imaginary parts)
     io: str = "bf16"  # dtype of x, delta, B, C, z and y
     gate: bool = True
     softplus: bool = True
@@ -134,13 +137,23 @@ class ScanConfig:
     def tokch(self) -> int:
         return self.batch * self.dim * self.L
 
+    @property
+    def bc_rows(self) -> int:
+        return 2 * self.N if self.a_mode == "complex" else self.N
+
     def shapes(self) -> Dict[str, Tuple[int, ...]]:
+        if self.a_mode == "head":
+            a_shape = (self.nheads,)
+        elif self.a_mode == "complex":
+            a_shape = (self.dim, self.N, 2)
+        else:
+            a_shape = (self.dim, self.N)
         s = {
             "x": (self.batch, self.dim, self.L),
             "delta": (self.batch, self.delta_rows, self.L),
-            "A": (self.nheads,) if self.a_mode == "head" else (self.dim, self.N),
-            "B": (self.batch, self.ngroups, self.N, self.L),
-            "C": (self.batch, self.ngroups, self.N, self.L),
+            "A": a_shape,
+            "B": (self.batch, self.ngroups, self.bc_rows, self.L),
+            "C": (self.batch, self.ngroups, self.bc_rows, self.L),
         }
         if self.has_D:
             s["D"] = (self.dim,)
@@ -161,7 +174,11 @@ class ScanConfig:
         if name == "delta_bias":
             return Dist(INV_SOFTPLUS_UNIFORM, 0.001, 0.1)
         if name == "A":
+            if self.a_mode == "complex":  # the real parts
+                return Dist(UNIFORM, -0.75, -0.25)
             return Dist(UNIFORM, -16.0, -1.0) if self.a_mode == "head" else Dist(NEG_ARANGE, self.N)
+        if name == "A_imag":  # jitter added to pi n
+            return Dist(UNIFORM, -0.5, 0.5)
         return Dist(NORMAL, 0.0, 1.0)
 
     def algorithmic_bytes(self) -> int:
@@ -203,7 +220,26 @@ DECODE_CONFIGS: Dict[str, ScanConfig] = {
 }
 
 
+# The complex-A scan at the Mamba-130M layer's shape (A, B and C complex; delta, x and z real).
+COMPLEX_CONFIG = ScanConfig(name="complex-A layer: batch 8, d_inner 1536, N 16, L 2048", batch=8,
+                            dim=1536, L=2048, N=16, a_mode="complex", seed=SEED_BASE + 18)
+
+
+def _complex_a(cfg: ScanConfig, d0: int, d1: int) -> np.ndarray:
+    """Rows [d0, d1) of a complex A as (rows, N, 2) float32 (real, imaginary) pairs: real parts
+    from the "A" stream, imaginary parts pi n (a linear ladder of frequencies over the states)
+    plus jitter from the "A_imag" stream."""
+    N, rows = cfg.N, d1 - d0
+    dr, di = cfg.dist_of("A"), cfg.dist_of("A_imag")
+    re = fill(cfg.seed, TENSOR_IDS["A"], dr.kind, dr.p0, dr.p1, rows * N, F32, d0 * N)
+    jit = fill(cfg.seed, TENSOR_IDS["A_imag"], di.kind, di.p0, di.p1, rows * N, F32, d0 * N)
+    im = (np.float32(np.pi) * np.arange(N, dtype=np.float32))[None, :] + jit.reshape(rows, N)
+    return np.stack([re.reshape(rows, N), im.astype(np.float32)], axis=-1)
+
+
 def make_tensor(cfg: ScanConfig, name: str, nthreads: Optional[int] = None) -> np.ndarray:
+    if name == "A" and cfg.a_mode == "complex":
+        return _complex_a(cfg, 0, cfg.dim)
     shp = cfg.shapes()[name]
     d = cfg.dist_of(name)
     arr = fill(cfg.seed, TENSOR_IDS[name], d.kind, d.p0, d.p1, int(np.prod(shp)),
@@ -220,7 +256,7 @@ def make_channel(cfg: ScanConfig, b: int, d: int) -> Dict[str, np.ndarray]:
     """Inputs of the single channel (b, d), regenerated from the streams without building the
     full tensors. Shapes are those of a batch-1, dim-1 problem (head mode: headdim 1, one head).
     """
-    L, N = cfg.L, cfg.N
+    L, N, R = cfg.L, cfg.N, cfg.bc_rows
     g = d // (cfg.dim // cfg.ngroups)
     row = d // cfg.headdim if cfg.a_mode == "head" else d
 
@@ -232,11 +268,13 @@ def make_channel(cfg: ScanConfig, b: int, d: int) -> Dict[str, np.ndarray]:
     out = {
         "x": part("x", (b * cfg.dim + d) * L, L, (1, 1, L)),
         "delta": part("delta", (b * cfg.delta_rows + row) * L, L, (1, 1, L)),
-        "B": part("B", (b * cfg.ngroups + g) * N * L, N * L, (1, 1, N, L)),
-        "C": part("C", (b * cfg.ngroups + g) * N * L, N * L, (1, 1, N, L)),
+        "B": part("B", (b * cfg.ngroups + g) * R * L, R * L, (1, 1, R, L)),
+        "C": part("C", (b * cfg.ngroups + g) * R * L, R * L, (1, 1, R, L)),
     }
     if cfg.a_mode == "head":
         out["A"] = part("A", row, 1, (1,))
+    elif cfg.a_mode == "complex":
+        out["A"] = _complex_a(cfg, d, d + 1)
     else:
         out["A"] = part("A", d * N, N, (1, N))
     if cfg.has_D:
@@ -255,6 +293,9 @@ def make_batch_entry(cfg: ScanConfig, b: int, nthreads: Optional[int] = None
     out = {}
     one = with_shape(cfg, batch=1)
     for name, shp in one.shapes().items():
+        if name == "A" and cfg.a_mode == "complex":
+            out[name] = _complex_a(cfg, 0, cfg.dim)
+            continue
         d = cfg.dist_of(name)
         count = int(np.prod(shp))
         start = b * count if name in ("x", "delta", "B", "C", "z") else 0
@@ -273,7 +314,7 @@ def make_channel_block(cfg: ScanConfig, b: int, d0: int, d1: int,
         raise ValueError("the channel block must lie inside one B/C group")
     if cfg.a_mode == "head" and (d0 % cfg.headdim or d1 % cfg.headdim):
         raise ValueError("the channel block must cover whole heads")
-    L, N, nch = cfg.L, cfg.N, d1 - d0
+    L, N, R, nch = cfg.L, cfg.N, cfg.bc_rows, d1 - d0
     g = d0 // gsize
     r0, r1 = (d0 // cfg.headdim, d1 // cfg.headdim) if cfg.a_mode == "head" else (d0, d1)
 
@@ -285,11 +326,13 @@ def make_channel_block(cfg: ScanConfig, b: int, d0: int, d1: int,
     out = {
         "x": part("x", (b * cfg.dim + d0) * L, nch * L, (1, nch, L)),
         "delta": part("delta", (b * cfg.delta_rows + r0) * L, (r1 - r0) * L, (1, r1 - r0, L)),
-        "B": part("B", (b * cfg.ngroups + g) * N * L, N * L, (1, 1, N, L)),
-        "C": part("C", (b * cfg.ngroups + g) * N * L, N * L, (1, 1, N, L)),
+        "B": part("B", (b * cfg.ngroups + g) * R * L, R * L, (1, 1, R, L)),
+        "C": part("C", (b * cfg.ngroups + g) * R * L, R * L, (1, 1, R, L)),
     }
     if cfg.a_mode == "head":
         out["A"] = part("A", r0, r1 - r0, (r1 - r0,))
+    elif cfg.a_mode == "complex":
+        out["A"] = _complex_a(cfg, d0, d1)
     else:
         out["A"] = part("A", d0 * N, nch * N, (nch, N))
     if cfg.has_D:

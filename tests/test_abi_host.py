@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert ssm.abi_version() == 5
+    assert ssm.abi_version() == 6
     for code in range(-10, 1):
         s = ssm.status_string(code)
         assert s and s != "unknown status"
@@ -85,6 +85,9 @@ def test_validation_errors_are_reported_before_launch():
     bad = ssm.desc_contiguous(2, 64, 128, 16)
     bad.a_mode = 3
     assert _fwd(bad) == -3
+    bad = ssm.desc_contiguous(2, 64, 128, 16, a_mode=ssm.SSM_A_COMPLEX)
+    bad.headdim = 2  # complex mode requires headdim 1
+    assert _fwd(bad) == -2
     bad = ssm.desc_contiguous(2, 64, 128, 16)
     bad.x_stride_dim = -1
     assert _fwd(bad) == -4
@@ -142,6 +145,39 @@ def test_extended_entry_point_validation():
                            ssm.ScanExt(0, 0, None, None), None, 0, None) == 0
     assert ssm.fwd_ext_raw(e, None, None, None, None, None, None, None, None, 1, None,
                            ssm.ScanExt(0, 0, H0, H0 + 64), None, 0, None) == -6
+
+
+def test_complex_mode_validation():
+    """a_mode SSM_A_COMPLEX: B and C extents cover 2N rows, the forward scan takes only the
+    delta * B rule without initial or final state, N <= 32, and needs no workspace; the decode
+    step and the backward pass reject it."""
+    c = ssm.SSM_A_COMPLEX
+    d = ssm.desc_contiguous(2, 64, 128, 16, a_mode=c)
+    assert d.B_stride_group == 32 * 128 and d.B_stride_batch == 32 * 128
+    assert ssm.workspace_size(d) == 0
+    H0 = FAKE + (12 << 30)
+    assert _fwd_ext(d, ssm.ScanExt(1, 0, None, None)) == -9          # zero-order hold
+    assert _fwd_ext(d, ssm.ScanExt(0, 2, None, None)) == -9          # chunked
+    assert _fwd_ext(d, ssm.ScanExt(0, 0, H0, None)) == -9            # initial state
+    assert _fwd_ext(d, ssm.ScanExt(0, 0, None, H0)) == -9            # final state
+    assert _fwd(ssm.desc_contiguous(2, 64, 128, 33, a_mode=c)) == -9  # N > 32
+    assert _fwd(ssm.desc_contiguous(1, 256, 128, 16, ngroups=8, a_mode=c)) == -9  # groups of 32
+    assert _fwd(d, x=None) == -1
+    assert _fwd(d, x=FAKE + 1) == -5
+    assert _fwd(d, y=FAKE + (3 << 30) + 64) == -6                    # y overlaps B
+    # B's 2N rows: y placed just past N rows of B still overlaps its imaginary parts
+    assert _fwd(d, y=FAKE + (3 << 30) + 16 * 128 * 2) == -6
+    # nothing to compute: no pointers needed
+    e = ssm.desc_contiguous(3, 64, 0, 16, a_mode=c)
+    assert ssm.fwd_raw(e, None, None, None, None, None, None, None, None, 1, None, None, 0,
+                       None) == 0
+    one = ssm.desc_contiguous(4, 64, 1, 16, a_mode=c)
+    S = FAKE + (16 << 30)
+    assert ssm.state_update_raw(one, S, FAKE, FAKE + (1 << 30), FAKE + (2 << 30),
+                                FAKE + (3 << 30), FAKE + (4 << 30), None, None, None, True,
+                                FAKE + (8 << 30), None) == -9
+    out = ctypes.c_size_t(0)
+    assert ssm.lib().ssm_selective_scan_bwd_workspace_size(ctypes.byref(d), ctypes.byref(out)) == -9
 
 
 def test_state_update_validation():

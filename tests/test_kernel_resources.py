@@ -87,6 +87,8 @@ HOT = [
      160 * 1024),
     ("decode_vec_kernelItLi16ELb0ELb1E", "decode step, bf16, N 16, gate", 0, 0),
     ("bwd_kernelItLi4ELb1E", "backward reverse kernel, bf16, N <= 16, gate", 0, 80 * 1024),
+    ("scan_complex_kernelItLi2ELi8ELb1E", "complex-A forward, bf16, N <= 16, gate", 0, 64 * 1024),
+    ("scan_complex_kernelIfLi4ELi8ELb1E", "complex-A forward, fp32, N <= 32, gate", 0, 64 * 1024),
     ("bwd_wide_kernelItLi16ELi8ELi4ELb1ELb0ELb1E",
      "backward reverse kernel, one A per head, N 128, gate", 57, 160 * 1024),
 ]
