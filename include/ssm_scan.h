@@ -256,8 +256,12 @@ int ssm_selective_scan_bwd_ext(const ssm_scan_desc* desc, const void* x, const v
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Size of the fixed device array that ssm_selective_scan_fwd_noalloc uses as its workspace:
- * 8 MiB, held on every GPU the library runs on until the process ends. Every segment plan with
- * dstate <= 32 fits it (the million-token scan needs 2.2 MB). */
+ * 8 MiB, held on every GPU the library runs on until the process ends. The per-segment
+ * summaries of every segment plan with dstate <= 32 fit it (2.2 MB for the million-token scan).
+ * A split sequence's workspace also holds states that let the pass correcting its later
+ * segments stop early (64 MiB for the million-token scan); where those do not fit, the array
+ * holds the summaries only and that pass runs every later segment to its end: the results are
+ * the same, only slower. */
 #define SSM_NOALLOC_SCRATCH_BYTES (8 << 20)
 
 /* ssm_selective_scan_fwd_ext for callers that cannot allocate device memory (code under HIP
@@ -266,8 +270,8 @@ int ssm_selective_scan_bwd_ext(const ssm_scan_desc* desc, const void* x, const v
  * owned by the library instead of a caller buffer. It allocates nothing and calls no
  * allocating routine. The caller still passes every input and output.
  *   Arguments, layouts and errors: those of ssm_selective_scan_fwd_ext (`ext` may be NULL).
- *   Returns SSM_ERR_SCRATCH_LIMIT, before touching the GPU, when
- *   ssm_selective_scan_workspace_size(desc) exceeds SSM_NOALLOC_SCRATCH_BYTES, and SSM_ERR_HIP
+ *   Returns SSM_ERR_SCRATCH_LIMIT, before touching the GPU, when even the summaries alone (see
+ *   SSM_NOALLOC_SCRATCH_BYTES) exceed SSM_NOALLOC_SCRATCH_BYTES, and SSM_ERR_HIP
  *   when the array's device address cannot be found. The first call on a device looks that
  *   address up (with the stream's device current) and keeps it.
  *   Every call on a GPU shares that GPU's array and leaves its contents behind; nothing in it

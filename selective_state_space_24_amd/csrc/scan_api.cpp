@@ -18,6 +18,8 @@ struct Plan {
   int64_t nseg;
   int64_t seg_len;
   bool state_split = false;  // bf16 io, 8 < dstate <= 16: the state-split kernel (see below)
+  bool wave = false;         // bf16 io, 8 < dstate <= 16: the kernel with independent wavefronts
+  bool fix = false;          // its split with a zero-start output pass and a correcting pass
 };
 
 bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
@@ -134,6 +136,7 @@ Plan plan_segments(const ssm_scan_desc* d) {
       p.state_split = true;
       return p;
     }
+    p.wave = true;
     // otherwise segments: beyond what fills the chip once they would start a second round of
     // workgroups that leaves most CUs idle, so the count is rounded down
     want = kTargetWaves / waves;
@@ -147,13 +150,28 @@ Plan plan_segments(const ssm_scan_desc* d) {
   p.seg_len = seg_tiles * tile;
   p.nseg = (d->seqlen + p.seg_len - 1) / p.seg_len;
   if (p.nseg <= 1) p = Plan{1, d->seqlen};
+  // long segments: zero-start output pass and correcting pass (see scan_fwd_wave_kernel)
+  p.fix = p.wave && p.nseg > 1 && p.seg_len >= ssm::kFixMinSegment;
   return p;
 }
 
-size_t workspace_bytes_for(const ssm_scan_desc* d, const Plan& p) {
+// States the split output pass of the independent-wavefront kernel stores per segment for the
+// correcting pass: one per kFixCheck steps, at most kFixMaxChecks (0 when `checks` is off).
+int64_t fix_checks(const Plan& p, bool checks) {
+  if (!checks || !p.fix) return 0;
+  return std::min<int64_t>(p.seg_len / ssm::kFixCheck, ssm::kFixMaxChecks);
+}
+
+// Workspace of a split sequence: hend (batch, dim, nseg, N) fp32, then dsum (batch, dim, nseg)
+// fp32, then (the correcting scheme) the stored states (batch, dim, nseg, nchk, 16) fp32, from
+// the next 16-byte boundary (12 bytes of slack allow for a 4-byte-aligned base).
+size_t workspace_bytes_for(const ssm_scan_desc* d, const Plan& p, bool checks = true) {
   if (p.nseg <= 1) return 0;
-  // hend (batch, dim, nseg, N) fp32, then dsum (batch, dim, nseg) fp32
-  return (size_t)d->batch * (size_t)d->dim * (size_t)p.nseg * (size_t)(d->dstate + 1) * sizeof(float);
+  const size_t bdn = (size_t)d->batch * (size_t)d->dim * (size_t)p.nseg;
+  size_t bytes = bdn * (size_t)(d->dstate + 1) * sizeof(float);
+  const int64_t nchk = fix_checks(p, checks);
+  if (nchk > 0) bytes += 12 + bdn * (size_t)nchk * 16 * sizeof(float);
+  return bytes;
 }
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -323,16 +341,23 @@ int ssm_selective_scan_workspace_size(const ssm_scan_desc* desc, size_t* bytes) 
   if (!bytes) return SSM_ERR_NULL_ARG;
   const int rc = check_desc(desc);
   if (rc != SSM_OK) return rc;
-  // the complex-A scan runs in one pass without workspace
-  *bytes = desc->a_mode == SSM_A_COMPLEX ? 0 : workspace_bytes_for(desc, plan_segments(desc));
+  *bytes = ssm::fwd_workspace_bytes(desc, true);
   return SSM_OK;
 }
 
-int ssm_selective_scan_fwd_ext(const ssm_scan_desc* desc, const void* x, const void* delta,
-                               const float* A, const void* B, const void* C, const float* D,
-                               const void* z, const float* delta_bias, int32_t delta_softplus,
-                               void* y, const ssm_scan_ext* ext, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace ssm {
+
+size_t fwd_workspace_bytes(const ssm_scan_desc* desc, bool checks) {
+  // the complex-A scan runs in one pass without workspace
+  return desc->a_mode == SSM_A_COMPLEX ? 0 : workspace_bytes_for(desc, plan_segments(desc), checks);
+}
+
+int fwd_ext(const ssm_scan_desc* desc, const void* x, const void* delta, const float* A,
+            const void* B, const void* C, const float* D, const void* z, const float* delta_bias,
+            int32_t delta_softplus, void* y, const ssm_scan_ext* ext, void* workspace,
+            size_t workspace_bytes, void* stream, bool checks) {
   int rc = check_desc(desc);
   if (rc != SSM_OK) return rc;
   const int32_t disc = ext ? ext->discretization : SSM_DISC_DELTA_B;
@@ -414,6 +439,7 @@ int ssm_selective_scan_fwd_ext(const ssm_scan_desc* desc, const void* x, const v
   p.seg_len = plan.seg_len;
   p.nseg = (int32_t)plan.nseg;
   p.state_split = plan.state_split ? 1 : 0;
+  p.fix_split = plan.fix ? 1 : 0;
   p.softplus = delta_softplus ? 1 : 0;
   p.zoh = disc == SSM_DISC_ZOH ? 1 : 0;
   // 16-byte vector access of x/delta/z/y rows: 16-byte aligned bases, strides multiple of 16 B
@@ -445,7 +471,7 @@ int ssm_selective_scan_fwd_ext(const ssm_scan_desc* desc, const void* x, const v
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
   }
 
-  const size_t need = workspace_bytes_for(desc, plan);
+  const size_t need = workspace_bytes_for(desc, plan, checks);
   if (need > 0 && (!workspace || workspace_bytes < need)) return SSM_ERR_WORKSPACE;
   if (need > 0 && !aligned(workspace, 4)) return SSM_ERR_MISALIGNED;
   if (need > 0) {
@@ -455,14 +481,31 @@ int ssm_selective_scan_fwd_ext(const ssm_scan_desc* desc, const void* x, const v
     if (hfin && overlaps(workspace, need, hfin, state_bytes)) return SSM_ERR_ALIAS;
   }
   if (plan.nseg > 1) {
+    const size_t bdn = (size_t)d.batch * d.dim * plan.nseg;
     p.hend = static_cast<float*>(workspace);
-    p.dsum = p.hend + (size_t)d.batch * d.dim * plan.nseg * d.dstate;
+    p.dsum = p.hend + bdn * d.dstate;
+    p.nchk = fix_checks(plan, checks);
+    if (p.nchk > 0)
+      p.hchk = reinterpret_cast<float*>(((uintptr_t)(p.dsum + bdn) + 15) & ~(uintptr_t)15);
   }
 
   hipError_t e;
   if (bf16) e = head ? ssm::launch_bf16_head(p, hs) : ssm::launch_bf16_diag(p, hs);
   else e = head ? ssm::launch_f32_head(p, hs) : ssm::launch_f32_diag(p, hs);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+}  // namespace ssm
+
+extern "C" {
+
+int ssm_selective_scan_fwd_ext(const ssm_scan_desc* desc, const void* x, const void* delta,
+                               const float* A, const void* B, const void* C, const float* D,
+                               const void* z, const float* delta_bias, int32_t delta_softplus,
+                               void* y, const ssm_scan_ext* ext, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return ssm::fwd_ext(desc, x, delta, A, B, C, D, z, delta_bias, delta_softplus, y, ext,
+                      workspace, workspace_bytes, stream, true);
 }
 
 int ssm_selective_scan_fwd(const ssm_scan_desc* desc, const void* x, const void* delta,

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ssm_scan.h"
+
 namespace ssm {
 
 // Channels handled by one workgroup: one channel per lane of a 64-wide wavefront.
@@ -14,6 +16,10 @@ constexpr int kLT = 2 * kTB;  // time steps per load tile (128 bytes of bf16 per
                               // along L start at multiples of it
 constexpr int kCkptStep = 8;  // steps between the states the backward checkpoint pass stores
 constexpr int kHeadDeltaChunk = 1024;  // steps per partial sum of the head-mode bias gradient
+constexpr int kFixCheck = 1024;  // steps between the states a split output pass stores for the
+                                 // pass that corrects its later segments (checked against there)
+constexpr int kFixMaxChecks = 32;  // stored states per segment at most (the first 32K steps)
+constexpr int64_t kFixMinSegment = 32768;  // shortest segment that takes that scheme
 
 constexpr int64_t kCUs = 256;           // compute units of an MI355X
 constexpr int64_t kTargetWaves = 2048;  // about two resident wavefronts per SIMD (256 CUs)
@@ -54,6 +60,11 @@ struct ScanParams {
   // hend[((b * dim + d) * nseg + s) * N + n] and dsum[(b * dim + d) * nseg + s]
   float* hend;
   float* dsum;
+  // the independent-wavefront kernel's split: its output pass's zero-start state after every
+  // kFixCheck steps of each segment, all 16 padded states, hchk[(((b * dim + d) * nseg + s) *
+  // nchk + k) * 16 + n] (16-byte aligned; nullable when nchk == 0)
+  float* hchk;
+  int64_t nchk;
 
   int64_t batch, dim, L, N, ngroups, headdim;
   int64_t x_sb, x_sd, dl_sb, dl_sd, B_sb, B_sg, B_sn, C_sb, C_sg, C_sn, z_sb, z_sd, y_sb, y_sd;
@@ -70,6 +81,9 @@ struct ScanParams {
   int32_t state_split;       // bf16 io, 8 < N <= 16: run scan_fwd_kernel (eight wavefronts of two
                              // states) in one pass rather than the kernel with independent
                              // wavefronts (chosen by the segment planner)
+  int32_t fix_split;         // the kernel with independent wavefronts, split along L: zero-start
+                             // output pass, then the correcting pass (rather than a summary pass
+                             // first; chosen by the segment planner)
 };
 
 // One launcher per (io dtype, A mode); each is compiled in its own translation unit.
@@ -130,5 +144,15 @@ hipError_t launch_state_copy(const float* src, float* dst, int64_t n, hipStream_
 // pairs, B and C with 2N rows per group (real parts, then imaginary), N <= 32, delta * B rule,
 // no initial or final state (checked by the caller).
 hipError_t launch_complex(const ScanParams& p, bool bf16, hipStream_t stream);
+
+// The forward entry point behind ssm_selective_scan_fwd_ext. `checks` off leaves out the states
+// that a split sequence's output pass stores for the correcting pass (a smaller workspace; the
+// correcting pass then runs every later segment to its end, with the same results).
+// fwd_workspace_bytes is the workspace either way, for a descriptor that check_desc accepts.
+size_t fwd_workspace_bytes(const ssm_scan_desc* desc, bool checks);
+int fwd_ext(const ssm_scan_desc* desc, const void* x, const void* delta, const float* A,
+            const void* B, const void* C, const float* D, const void* z, const float* delta_bias,
+            int32_t delta_softplus, void* y, const ssm_scan_ext* ext, void* workspace,
+            size_t workspace_bytes, void* stream, bool checks);
 
 }  // namespace ssm

@@ -4,8 +4,8 @@
 // wavefront owns 16 channels x all states and runs without workgroup barriers. scan_fwd_kernel,
 // described here, serves every other case (fp32 io, N <= 8 or N > 16, and bf16 shapes whose
 // 128-channel workgroups are too few to fill the chip while its 64-channel ones are not: the
-// segment planner's state_split choice) and also runs some segment summaries and the backward
-// pass's checkpoints.
+// segment planner's state_split choice) and also runs the backward pass's checkpoints for the
+// shapes it serves. The two split a sequence along L in different ways (see each kernel).
 //
 // Work decomposition of scan_fwd_kernel: one workgroup = 64 channels of one batch entry x one
 // segment of L, in NW wavefronts.
@@ -745,11 +745,32 @@ constexpr int kWaveGroupChannels = kWaveChannels * kWaveGroupWaves;
 constexpr int kWaveDuStride = 2 * kTB + 4;  // floats per channel row of (delta, u)
 constexpr int kWaveRowStride = kTB + 4;     // floats per state row of B / C, per lane row of partials
 
-// MODE: kWaveOut computes y; kWaveSummary is the segment summary pass (the state at the
-// segment's end from a zero start, and the segment's sum of delta); kWaveCkpt is the backward
-// pass's checkpoint pass (the state before every kCkptStep-th step). The last two have no
-// readout and no y.
-constexpr int kWaveOut = 0, kWaveSummary = 1, kWaveCkpt = 2;
+// MODE: a sequence split into segments along L runs one of two schemes, chosen by the planner
+// from the segment length.
+//  Summary first (segments shorter than kFixMinSegment):
+//   kWaveSummary the summary pass of segments 0 .. nseg-2: each segment's end state from a zero
+//                start and its sum of delta (no readout, no y).
+//   kWaveOut     computes y; segment s > 0 starts from the summaries of segments < s composed,
+//                h <- exp(A * sum delta) h + h_end. A sequence that is not split runs this alone.
+//  Zero start, then correction (segments of kFixMinSegment steps or more):
+//   kWaveOutSum  the output pass of every segment at once: segment 0 from the initial state, the
+//                others from a zero state. Each also writes its summary (its end state and its
+//                sum of delta) and stores its state after every kFixCheck steps.
+//   kWaveFix     the second pass, for segments 1, 2, ...: it composes the
+//                summaries of the earlier segments into the segment's true initial state and
+//                runs the recurrence from there, rewriting y. Its trajectory and the output
+//                pass's zero-start one differ by the decayed initial state. At every kFixCheck
+//                steps it compares its state with the one the output pass stored there: once
+//                every state of the wavefront is bitwise equal, the output pass's y from there on
+//                is exactly the true one, so the wavefront stops. A state that does not decay
+//                (A = 0) makes it run to the segment's end.
+//  kWaveCkpt     the backward pass's checkpoint pass (the state before every kCkptStep-th step;
+//                no readout and no y).
+// The first scheme pays for a summary pass over most of the sequence; the second for rerunning
+// each segment from its start until the decay has washed out the difference of the initial
+// states, which the stored states detect. For the workloads' step sizes that takes a few
+// thousand steps, so the second wins once segments are long.
+constexpr int kWaveOut = 0, kWaveSummary = 1, kWaveCkpt = 2, kWaveOutSum = 3, kWaveFix = 4;
 
 template <typename IO, bool HEAD, bool GATE, bool ZOH, int MODE = kWaveOut>
 __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
@@ -759,7 +780,8 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
                          const float* __restrict__ Dm, const float* __restrict__ bias_p,
                          float* __restrict__ hend, float* __restrict__ dsum,
                          const ScanParams p) {
-  constexpr bool NOREAD = MODE != kWaveOut;
+  constexpr bool NOREAD = MODE == kWaveSummary || MODE == kWaveCkpt;
+  constexpr bool FIX = MODE == kWaveFix;
   static_assert(!(NOREAD && GATE), "the summary and checkpoint passes have no gate");
   static_assert(MODE != kWaveCkpt || (kCkptStep == 8 && kTB % kCkptStep == 0),
                 "checkpoints fall on every other 4-step block");
@@ -787,7 +809,7 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
   __syncthreads();
   if (d0 >= p.dim) return;  // a wavefront past the last channel (its partner keeps going)
 
-  const int seg = blockIdx.y;
+  const int seg = FIX ? blockIdx.y + 1 : blockIdx.y;
   const int64_t t_begin = (int64_t)seg * p.seg_len;
   const int64_t t_end = min(p.L, t_begin + p.seg_len);
   const bool softplus = p.softplus != 0;
@@ -808,8 +830,9 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
       ap[j] = (live && 4 * q + j < p.N) ? Am[d * p.N + 4 * q + j] * kLog2e : 0.0f;
   }
   float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  double dsum_total = 0.0;  // summary pass: the segment's sum of delta
-  if (MODE != kWaveSummary && p.h0 && live) {
+  double dsum_total = 0.0;  // kWaveSummary: the segment's sum of delta
+  if ((MODE == kWaveOut || MODE == kWaveCkpt || (MODE == kWaveOutSum && seg == 0)) && p.h0 &&
+      live) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       if (4 * q + j < p.N) h[j] = p.h0[(b * p.dim + d) * p.N + 4 * q + j];
@@ -818,6 +841,24 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
     // compose the summaries of segments 0 .. seg-1: h <- exp(A * sum delta) h + h_end
     const int64_t base = (b * p.dim + d) * p.nseg;
     for (int s = 0; s < seg; ++s) {
+      const float ds = dsum[base + s];
+      const float* he = hend + (base + s) * p.N;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a = HEAD ? ap[0] : ap[j];
+        if (4 * q + j < p.N) h[j] = __builtin_amdgcn_exp2f(a * ds) * h[j] + he[4 * q + j];
+      }
+    }
+  }
+  if (FIX && live) {
+    // the true state at the segment's start: segment 0's end state (it ran from the true
+    // initial state), then h <- exp(A * sum delta) h + h_end for segments 1 .. seg-1, whose
+    // summaries are from a zero start
+    const int64_t base = (b * p.dim + d) * p.nseg;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (4 * q + j < p.N) h[j] = hend[base * p.N + 4 * q + j];
+    for (int s = 1; s < seg; ++s) {
       const float ds = dsum[base + s];
       const float* he = hend + (base + s) * p.N;
 #pragma unroll
@@ -878,8 +919,13 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
     }
   };
 
-  // delta and u = delta * x of piece i into the channel rows; B and C into the state rows
-  auto put_du = [&](int i, const float (&xv)[V], const float (&dv)[V]) __attribute__((always_inline)) {
+  // kWaveOutSum: this lane's part of its row's sum of delta over the segment (the row's other
+  // pieces are on the three neighbouring lanes)
+  static_assert(MODE != kWaveOutSum || (CPL == 1 && PPR == 4), "one piece per lane, four per row");
+  double dsum_lane = 0.0;
+  // delta and u = delta * x of piece i into the channel rows; B and C into the state rows. nv:
+  // the piece's valid steps
+  auto put_du = [&](int i, const float (&xv)[V], const float (&dv)[V], int nv) __attribute__((always_inline)) {
     float o[2 * V];
     if (softplus) {
 #pragma unroll
@@ -887,6 +933,13 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
     } else {
 #pragma unroll
       for (int e = 0; e < V; ++e) o[2 * e] = dv[e] + pb[i];
+    }
+    if constexpr (MODE == kWaveOutSum) {
+      float s = 0.0f;
+#pragma unroll
+      for (int e = 0; e < V; ++e)
+        if (e < nv) s += o[2 * e];
+      dsum_lane += (double)s;
     }
 #pragma unroll
     for (int e = 0; e < V; ++e) o[2 * e + 1] = o[2 * e] * xv[e];
@@ -921,7 +974,7 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
       unpack16<IO>(r.d[hf][i], dv);
       unpack16<IO>(r.b[hf][i], bv);
       if constexpr (!NOREAD) unpack16<IO>(r.c[hf][i], cv);
-      put_du(i, xv, dv);
+      put_du(i, xv, dv, V);
       put_bc(i, bv, cv);
     }
   };
@@ -940,7 +993,7 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
       load_chunk<IO, false>(br[i], t0 + pt[i], bvalid[i] ? cnt : 0, false, bv);
       if constexpr (!NOREAD)
         load_chunk<IO, false>(cr[i], t0 + pt[i], bvalid[i] ? cnt : 0, false, cv);
-      put_du(i, xk[i], dv);
+      put_du(i, xk[i], dv, cnt);
       if (cnt < V) {
         float* row = &du[prow[i] * kWaveDuStride + 2 * pt[i]];
         for (int e = cnt; e < V; ++e) { row[2 * e] = 0.0f; row[2 * e + 1] = 0.0f; }
@@ -1116,8 +1169,17 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
   // ---- full load tiles, two per iteration so that the two register sets alternate without
   // copies (a copy would wait for the loads in flight). The fetch after the last tile re-reads
   // that tile (in bounds, unused): unconditional loads keep the compiler's wait counts exact.
+  // kWaveOutSum stores its state after every kFixCheck steps of the segment (all 16 padded
+  // states, 16 bytes per lane); kWaveFix compares its own there and stops once every state of
+  // the wavefront is bitwise equal to the stored one
+  constexpr int kChkTiles = kFixCheck / kLT;
+  static_assert(kChkTiles % 2 == 0, "checks fall after the second tile of a pair");
+  f32x4* const chk_lane = (MODE == kWaveOutSum || FIX) && p.hchk
+      ? reinterpret_cast<f32x4*>(p.hchk) + ((b * p.dim + min(d, p.dim - 1)) * p.nseg + seg) * p.nchk * 4 + q
+      : nullptr;
   const bool fast_ok = p.vec_io != 0 && p.bc_vec != 0;
   const int64_t n_full = fast_ok ? (t_end - t_begin) / kLT : 0;
+  bool done = false;  // kWaveFix: converged
   if (n_full > 0) {
     Raw ra, rb;
     fetch(ra, t_begin);
@@ -1126,7 +1188,29 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
       tile_full(ra, rb, t0, i + 1 < n_full ? t0 + kLT : t0);
       if (i + 1 >= n_full) break;
       tile_full(rb, ra, t0 + kLT, i + 2 < n_full ? t0 + 2 * kLT : t0 + kLT);
+      if ((MODE == kWaveOutSum || FIX) && (i + 2) % kChkTiles == 0) {
+        const int64_t k = (i + 2) / kChkTiles - 1;
+        if (k < p.nchk) {
+          f32x4* const cp = chk_lane + k * 4;
+          if constexpr (MODE == kWaveOutSum) {
+            if (live) *cp = f32x4{h[0], h[1], h[2], h[3]};
+          } else {
+            const f32x4 z = *cp;
+            const bool same = !live || (__float_as_uint(h[0]) == __float_as_uint(z[0]) &&
+                                        __float_as_uint(h[1]) == __float_as_uint(z[1]) &&
+                                        __float_as_uint(h[2]) == __float_as_uint(z[2]) &&
+                                        __float_as_uint(h[3]) == __float_as_uint(z[3]));
+            if (__all(same)) { done = true; break; }
+          }
+        }
+      }
     }
+  }
+  if (FIX && done) {
+    // the next tile's loads are still in flight: let them land before the wavefront ends
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_setprio(0);
+    return;
   }
   // ---- the rest, one half tile at a time
   for (int64_t t0 = t_begin + n_full * kLT; t0 < t_end; t0 += kTB) {
@@ -1149,6 +1233,20 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
         if (4 * q + j < p.N) hend[base * p.N + 4 * q + j] = h[j];
       if (q == 0) dsum[base] = (float)dsum_total;
     }
+  }
+  if constexpr (MODE == kWaveOutSum) {
+    // the segment's summary: its end state and its sum of delta (each row's sum from its four
+    // lanes; IEEE addition commutes, so every lane of the row holds the same sum)
+    if (live) {
+      const int64_t base = (b * p.dim + d) * p.nseg + seg;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (4 * q + j < p.N) hend[base * p.N + 4 * q + j] = h[j];
+    }
+    double s = dsum_lane;
+    s += __shfl_xor(s, 1, 64);
+    s += __shfl_xor(s, 2, 64);
+    if ((lane & 3) == 0 && plive[0]) dsum[(b * p.dim + d0 + prow[0]) * p.nseg + seg] = (float)s;
   }
   if constexpr (NOREAD) return;
   if (p.hfin && live && seg == p.nseg - 1) {
@@ -1191,12 +1289,16 @@ hipError_t launch_cfg(const ScanParams& p, hipStream_t stream) {
                            dim3((unsigned)groups, 1), block8, 0, stream, SCAN_ARGS(p));
       return hipGetLastError();
     } else {
-      // 8 < N <= 16: the kernel with independent wavefronts for the output. The summaries take it
-      // too when they fill about three quarters of the chip (1536 wavefronts, 192 CUs); fewer
+      // 8 < N <= 16: the kernel with independent wavefronts. A sequence split into long
+      // segments runs its output pass over every segment at once (segments after the first
+      // from a zero state, each writing its summary), then the pass that reruns each later
+      // segment from its true initial state until the two trajectories agree bitwise
+      // (kWaveFix). Shorter segments take the summary pass first. Its summaries take this kernel
+      // when they fill about three quarters of the chip (1536 wavefronts, 192 CUs); fewer
       // summary workgroups run faster spread over more CUs in the barrier-synchronised form.
       const unsigned wg = (unsigned)(p.batch * ((p.dim + kWaveGroupChannels - 1) / kWaveGroupChannels));
       const dim3 wblock(64 * kWaveGroupWaves);
-      if (p.nseg > 1) {
+      if (p.nseg > 1 && !p.fix_split) {
         if ((int64_t)wg * (p.nseg - 1) * kWaveGroupWaves >= 1536)
           hipLaunchKernelGGL((scan_fwd_wave_kernel<IO, HEAD, false, ZOH, kWaveSummary>),
                              dim3(wg, (unsigned)(p.nseg - 1)), wblock, 0, stream, SCAN_ARGS(p));
@@ -1206,6 +1308,23 @@ hipError_t launch_cfg(const ScanParams& p, hipStream_t stream) {
                              SCAN_ARGS(p));
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+      } else if (p.nseg > 1) {
+        const dim3 ogrid(wg, (unsigned)p.nseg), fgrid(wg, (unsigned)(p.nseg - 1));
+        if (p.z)
+          hipLaunchKernelGGL((scan_fwd_wave_kernel<IO, HEAD, true, ZOH, kWaveOutSum>), ogrid,
+                             wblock, 0, stream, SCAN_ARGS(p));
+        else
+          hipLaunchKernelGGL((scan_fwd_wave_kernel<IO, HEAD, false, ZOH, kWaveOutSum>), ogrid,
+                             wblock, 0, stream, SCAN_ARGS(p));
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        if (p.z)
+          hipLaunchKernelGGL((scan_fwd_wave_kernel<IO, HEAD, true, ZOH, kWaveFix>), fgrid, wblock,
+                             0, stream, SCAN_ARGS(p));
+        else
+          hipLaunchKernelGGL((scan_fwd_wave_kernel<IO, HEAD, false, ZOH, kWaveFix>), fgrid,
+                             wblock, 0, stream, SCAN_ARGS(p));
+        return hipGetLastError();
       }
       const dim3 wgrid(wg, (unsigned)p.nseg);
       if (p.z)

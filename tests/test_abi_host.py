@@ -264,8 +264,14 @@ def test_disjoint_rows_accepts_any_dimension_order():
 
 def test_workspace_size_depends_only_on_shape():
     assert ssm.workspace_size(ssm.desc_contiguous(8, 4096, 4096, 16)) == 0
+    # the million-token scan: 16 segments; per (channel, segment) the summary (16 states and the
+    # sum of delta, fp32), then 12 bytes of alignment slack, then the 32 states of 16 floats that
+    # the output pass stores for the correcting pass (one per 1024 steps of a 65536-step segment)
     c3 = ssm.workspace_size(ssm.desc_contiguous(1, 2048, 1 << 20, 16))
-    assert c3 > 0 and c3 % (2048 * 17 * 4) == 0
+    assert c3 == 2048 * 16 * 17 * 4 + 12 + 2048 * 16 * 32 * 16 * 4
+    # fp32 io takes the four-wavefront kernel, whose split needs the summaries only
+    f32 = ssm.workspace_size(ssm.desc_contiguous(1, 2048, 1 << 20, 16, io_dtype=ssm.SSM_DTYPE_F32))
+    assert f32 > 0 and f32 % (2048 * 17 * 4) == 0
     assert ssm.workspace_size(ssm.desc_contiguous(0, 64, 10, 16)) == 0
     assert ssm.workspace_size(ssm.desc_contiguous(3, 64, 0, 16)) == 0
 
@@ -305,6 +311,9 @@ def test_noalloc_rejects_problems_beyond_its_scratch_on_the_host():
     assert ssm.fwd_noalloc_raw(d, *args) == -10
     bad = ssm.desc_contiguous(1, 64, 128, 200)      # argument errors come first
     assert ssm.fwd_noalloc_raw(bad, *args) == -2
-    # every segment plan with dstate <= 32 fits
-    for (b, dim, L, N) in [(1, 2048, 1 << 20, 16), (1, 64, 1 << 22, 32), (3, 64, 1 << 20, 32)]:
+    # the summaries of every segment plan with dstate <= 32 fit (the million-token scan's stored
+    # states, 64 MiB, do not: that call runs with the summaries only)
+    for (b, dim, L, N) in [(1, 64, 1 << 22, 32), (3, 64, 1 << 20, 32)]:
         assert ssm.workspace_size(ssm.desc_contiguous(b, dim, L, N)) <= ssm.NOALLOC_SCRATCH_BYTES
+    c3 = ssm.workspace_size(ssm.desc_contiguous(1, 2048, 1 << 20, 16))
+    assert c3 > ssm.NOALLOC_SCRATCH_BYTES >= 2048 * 16 * 17 * 4

@@ -2,8 +2,8 @@
 (CPU only: no kernel runs).
 
 Several kernels depend on the compiler keeping their working set in registers: the
-independent-wavefront forward kernel (the Mamba-1.4B layer), its segment-summary mode (the
-million-token config), the state-split kernel (the Mamba-130M layer), the chunked MFMA kernel,
+independent-wavefront forward kernel (the Mamba-1.4B layer), its split modes (the million-token
+config), the state-split kernel (the Mamba-130M layer), the chunked MFMA kernel,
 the decode kernels. A compiler or source change that makes them spill shows up here as scratch
 use, before any timing does. Kernels with a known, small spill are held to it.
 
@@ -78,7 +78,11 @@ HOT = [
     ("scan_fwd_wave_kernelItLb0ELb1ELb0ELi0E",
      "independent-wavefront forward, bf16, gate (Mamba-1.4B layer)", 0, 160 * 1024),
     ("scan_fwd_wave_kernelItLb0ELb0ELb0ELi1E",
-     "its segment-summary mode (million-token config)", 0, 160 * 1024),
+     "its segment-summary mode (splits into shorter segments)", 0, 160 * 1024),
+    ("scan_fwd_wave_kernelItLb0ELb1ELb0ELi3E",
+     "its zero-start output pass of a split, gate (million-token config)", 0, 160 * 1024),
+    ("scan_fwd_wave_kernelItLb0ELb1ELb0ELi4E",
+     "its correcting pass of a split, gate (million-token config)", 0, 160 * 1024),
     ("scan_fwd_wave_kernelItLb0ELb0ELb0ELi2E",
      "its checkpoint mode (backward of the Mamba-1.4B layer)", 11, 160 * 1024),
     ("scan_fwd_kernelItLi2ELi8ELb0ELb0ELb1ELb0ELb0E",
