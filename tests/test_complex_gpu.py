@@ -156,23 +156,25 @@ def test_complex_strided_and_misaligned():
     assert err <= TOL["bf16"]
 
 
-def test_complex_sampled_channels_layer_size():
-    """A Mamba-130M-sized layer (batch 8, 1536 channels, L 2048, N 16, bf16, gate) in one call;
-    channels spread over the tensor checked against the oracle one by one."""
-    cfg = _cfg(8, 1536, 2048, 16, io="bf16", seed=15)
-    inputs = ssmgen.make_inputs(cfg)
-    y = y_to_f64(_run(cfg, device_inputs(inputs)))
-    rng = np.random.default_rng(5)
-    picks = {(0, 0), (7, 1535)} | {(int(rng.integers(8)), int(rng.integers(1536)))
-                                   for _ in range(14)}
+@pytest.mark.timeout(600)
+def test_complex_layer_size_every_element():
+    """The bench workload, a Mamba-130M-sized layer (batch 8, 1536 channels, L 2048, N 16,
+    bf16, gate), in one call as bench.py --workload complex runs it; every output against the
+    oracle, which runs one batch entry at a time on inputs regenerated from the streams."""
+    cfg = ssmgen.COMPLEX_CONFIG
+    dev = {}
+    for name in cfg.shapes():
+        dev.update(device_inputs({name: ssmgen.make_tensor(cfg, name)}))
+    y = y_to_f64(_run(cfg, dev))
+    del dev
+    one = ssmgen.with_shape(cfg, batch=1)
     worst = 0.0
-    for b, d in sorted(picks):
-        ch = ssmgen.make_channel(cfg, b, d)
-        one = ssmgen.with_shape(cfg, batch=1, dim=1)
-        yref = oracle.scan_inputs_complex(ch, one, nthreads=1)[0, 0]
-        worst = max(worst, oracle.rel_err(y[b, d], yref))
-    _say(f"[complex] layer-size sample: worst rel err {worst:.3e}")
-    assert worst <= TOL["bf16"]
+    for b in range(cfg.batch):
+        yref = oracle.scan_inputs_complex(ssmgen.make_batch_entry(cfg, b), one)
+        err = oracle.rel_err(y[b:b + 1], yref)
+        worst = max(worst, err)
+        assert err <= TOL["bf16"], (b, err)
+    _say(f"[complex] layer size: worst rel err {worst:.3e} over {y.size} outputs")
 
 
 def test_complex_empty_and_rejections():
