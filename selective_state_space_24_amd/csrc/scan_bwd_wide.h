@@ -33,6 +33,7 @@ constexpr int kT = 16;          // steps per tile (one load of the per-step inpu
 constexpr int kInS = kT + 1;    // entries per channel row of the per-step LDS arrays
 constexpr int kSumS = 64 + 4;   // floats per column of the lane-sum scratch
 constexpr int kHeadChunk = kHeadDeltaChunk;  // steps per workgroup of the head-mode delta reduction
+constexpr int kDbcS = kT + 1;   // floats per (tensor, state) row of the tile's dB / dC partials
 static_assert(kT % kCkptStep == 0, "a tile holds whole checkpoint intervals");
 }  // namespace wide
 
@@ -70,10 +71,20 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_wide_kernel(const BwdParams q)
 
   __shared__ __align__(16) f32x4 s_in[kChannelsPerGroup * kInS];  // delta, u = delta x, gy, x
   __shared__ float s_gz[GATE ? kChannelsPerGroup * kInS : 1];     // dy silu'(z)
-  __shared__ __align__(16) float s_B[NP * kT];
-  __shared__ __align__(16) float s_C[NP * kT];
+  // B and C step-major: a wavefront's NS states of one step are NS consecutive floats, read as
+  // NS / 4 16-byte words at one (wave-uniform) address each
+  __shared__ __align__(16) float s_B[kT * NP];
+  __shared__ __align__(16) float s_C[kT * NP];
   __shared__ float s_red[3 * NW * kChannelsPerGroup * RED];        // per-channel partial sums
   __shared__ __align__(16) float s_sum[NW * NV * kSumS];           // dB / dC lane sums
+  // the tile's dC, dB partials (tensor, state, step), written out whole when the tile is done;
+  // where that buffer would take the workgroup past 80 KB of LDS (two workgroups per CU with
+  // four wavefronts), each step's sums are stored as they are made instead
+  constexpr int kLdsRest = (int)(kChannelsPerGroup * kInS * sizeof(f32x4)) +
+                           (GATE ? kChannelsPerGroup * kInS * 4 : 4) + 2 * NP * kT * 4 +
+                           3 * NW * kChannelsPerGroup * RED * 4 + NW * NV * kSumS * 4;
+  constexpr bool kStageDbc = NW == 8 || kLdsRest + 2 * NP * kDbcS * 4 <= 80 * 1024;
+  __shared__ float s_dbc[kStageDbc ? 2 * NP * kDbcS : 1];
 
   const ScanParams& p = q.f;
   const int tid = threadIdx.x;
@@ -159,8 +170,8 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_wide_kernel(const BwdParams q)
     for (int i = tid; i < NP * kT; i += NT) {
       const int n = i / kT, t = i % kT;
       const bool on = n < p.N && t < len;
-      s_B[i] = on ? to_f32(Bg[n * p.B_sn + t0 + t]) : 0.0f;
-      s_C[i] = on ? to_f32(Cg[n * p.C_sn + t0 + t]) : 0.0f;
+      s_B[t * NP + n] = on ? to_f32(Bg[n * p.B_sn + t0 + t]) : 0.0f;
+      s_C[t * NP + n] = on ? to_f32(Cg[n * p.C_sn + t0 + t]) : 0.0f;
     }
     __syncthreads();
 
@@ -173,9 +184,20 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_wide_kernel(const BwdParams q)
       const int64_t ci = tile * (kT / kCkptStep) + k;
       const float* const ck = p.ckpt + ((b * p.ntiles + ci) * p.N + n0) * p.dim + (live ? d : 0);
 
+      // the wavefront's NS values of B or C at tile step t
+      auto states_at = [&](const float* s, int t, float (&v)[NS]) __attribute__((always_inline)) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(s + t * NP + n0);
+#pragma unroll
+        for (int k = 0; k < NS / 4; ++k) {
+          const f32x4 w4 = src[k];
+          v[4 * k] = w4.x; v[4 * k + 1] = w4.y; v[4 * k + 2] = w4.z; v[4 * k + 3] = w4.w;
+        }
+      };
       // one forward step of the recurrence at tile step t: h <- dA h + B_bar x
       auto fwd_step = [&](float (&hv)[NS], int t) __attribute__((always_inline)) {
         const f32x4 in = s_in[lane * kInS + t];
+        float Bt[NS];
+        states_at(s_B, t, Bt);
         float dAh = 1.0f, gH = 1.0f;
         if constexpr (HEAD) {
           dAh = __builtin_amdgcn_exp2f(in.x * ap[0]);
@@ -183,7 +205,7 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_wide_kernel(const BwdParams q)
         }
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-          float dA, ub = in.y * s_B[(n0 + j) * kT + t];
+          float dA, ub = in.y * Bt[j];
           if constexpr (HEAD) {
             dA = dAh;
             if constexpr (ZOH) ub *= gH;
@@ -215,8 +237,10 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_wide_kernel(const BwdParams q)
           fwd_step(hh[i], tm + i);
           float acc = 0.0f;
           if constexpr (GATE) {
+            float Ct[NS];
+            states_at(s_C, tm + i, Ct);
 #pragma unroll
-            for (int j = 0; j < NS; ++j) acc = fmaf(s_C[(n0 + j) * kT + tm + i], hh[i][j], acc);
+            for (int j = 0; j < NS; ++j) acc = fmaf(Ct[j], hh[i][j], acc);
           }
           yp[i] = acc;
         }
@@ -235,10 +259,13 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_wide_kernel(const BwdParams q)
             if constexpr (ZOH) gH = zoh_ratio(dAh, dl * ap[0]);
           }
           float gd = 0.0f, sb = 0.0f, sbA = 0.0f, s1 = 0.0f;
+          float Bt[NS], Ct[NS];
+          states_at(s_B, t, Bt);
+          states_at(s_C, t, Ct);
 #pragma unroll
           for (int j = 0; j < NS; ++j) {
-            const float Bv = s_B[(n0 + j) * kT + t];
-            const float Cv = s_C[(n0 + j) * kT + t];
+            const float Bv = Bt[j];
+            const float Cv = Ct[j];
             gh[j] = fmaf(gy, Cv, gh[j]);
             red[j * kSumS] = gy * hh[i][j];  // dC
             const float hp = i == 0 ? hs[j] : hh[i - 1][j];
@@ -304,11 +331,17 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_wide_kernel(const BwdParams q)
             float sum = (acc4.x + acc4.y) + (acc4.z + acc4.w);
 #pragma unroll
             for (int off = NV; off < 64; off <<= 1) sum = xor_sum(sum, off);
-            const int j = col % NS;
-            const int64_t tt = t0 + t;
-            if (lane < NV && n0 + j < p.N && tt < L) {
-              float* dst = col < NS ? q.dC_part : q.dB_part;
-              dst[((b * p.groups_per_batch + wg) * p.N + n0 + j) * L + tt] = sum;
+            if constexpr (kStageDbc) {
+              // into the tile buffer (rows of padding states and steps past L are never written
+              // out)
+              if (lane < NV) s_dbc[((col < NS ? 0 : NP) + n0 + col % NS) * kDbcS + t] = sum;
+            } else {
+              const int j = col % NS;
+              const int64_t tt = t0 + t;
+              if (lane < NV && n0 + j < p.N && tt < L) {
+                float* dst = col < NS ? q.dC_part : q.dB_part;
+                dst[((b * p.groups_per_batch + wg) * p.N + n0 + j) * L + tt] = sum;
+              }
             }
           }
           wave_lds_sync();
@@ -369,8 +402,26 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_wide_kernel(const BwdParams q)
         __syncthreads();  // s_red is reused by the next block
       }
     }
-    // the next tile's prologue overwrites s_in, s_B, s_C: every wavefront is past its reads
-    // (the last block ended with a barrier)
+    // the tile's dC, dB partials: whole rows of its steps (16-byte stores where the rows allow
+    // them). Every step's sums are in s_dbc (the last block ended with a barrier).
+    if constexpr (kStageDbc) {
+      constexpr int Q4 = kT / 4;
+      for (int item = tid; item < 2 * NP * Q4; item += NT) {
+        const int row = item / Q4, t4 = 4 * (item % Q4);
+        const int n = row % NP;
+        if (n >= p.N || t4 >= len) continue;
+        float* dst = (row < NP ? q.dC_part : q.dB_part) +
+                     ((b * p.groups_per_batch + wg) * p.N + n) * L + t0 + t4;
+        const float* src = s_dbc + row * kDbcS + t4;
+        if (q.part_vec && t4 + 4 <= len) {
+          *reinterpret_cast<f32x4*>(dst) = f32x4{src[0], src[1], src[2], src[3]};
+        } else {
+          for (int e = 0; e < 4 && t4 + e < len; ++e) dst[e] = src[e];
+        }
+      }
+    }
+    // the next tile's prologue overwrites s_in, s_B, s_C and its steps s_dbc: every wavefront is
+    // past its reads (the barrier that begins the next tile's steps)
   }
 
   // ---- per-workgroup partials of the batch-summed gradients, and dh0
