@@ -16,8 +16,8 @@
 //      per-(t, n) sums over channels (dB, dC) are added over the lanes of each wavefront in
 //      wave-private LDS, giving one partial per workgroup. Outputs wait in LDS until the tile is
 //      done (dx, ddelta, dz in the slots of the consumed inputs, the dB/dC partials in a tile
-//      buffer) and leave in whole 16-byte pieces; for bf16 the next tile's inputs are loaded
-//      while the tile runs;
+//      buffer), then in registers, and leave in whole 16-byte pieces while the next tile runs;
+//      for bf16 the next tile's inputs are loaded while the tile runs;
 //   3. reduce kernels add the partials: dB, dC over the workgroups of a batch entry's group,
 //      dA, dD, dbias over the batch, in a fixed order (results are deterministic).
 // The LDS use (under 80 KB) lets two workgroups share a CU. Arithmetic: fp32. This kernel takes
@@ -112,12 +112,15 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
 
   // ---- a tile's per-step inputs: raw 16-byte chunks (x, delta, dy, z) of this thread's prologue
   // items and its B, C elements; then converted into LDS (padding steps are zero). With the
-  // prefetch, an odd tile's chunks are loaded together with those of the even tile before it
-  // (kept in raw2): the two share each 128-byte line of a bf16 row, which is then read whole.
+  // prefetch, an odd tile's chunks are loaded together with those of the even tile before it:
+  // the two share each 128-byte line of a bf16 row, which is then read whole. An odd tile's
+  // chunks are held in raw_odd, an even tile's in raw_even; loads go straight into them and
+  // nothing copies them, since a copy of a register a load is still writing waits for that
+  // load.
   struct Items {
     u32x4 c[IPT][4];  // per item: x, delta, dy, z
   };
-  Items raw, raw2;
+  Items raw_odd, raw_even;
   IO rb[BCI], rc[BCI];
   auto load_items = [&](int64_t tile) __attribute__((always_inline)) {
     const int64_t t0 = tile * kBT;
@@ -141,12 +144,14 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
   auto issue = [&](int64_t tile, bool pair) __attribute__((always_inline)) {
     const int64_t t0 = tile * kBT;
     const int lt_len = (int)min<int64_t>(kBT, L - t0);
-    if (PREFETCH && pair && (tile & 1) == 0) {
-      raw = raw2;  // loaded with tile + 1
-    } else {
-      raw = load_items(tile);
-      if (PREFETCH && pair && tile > 0) raw2 = load_items(tile - 1);
-    }
+    if (!PREFETCH) {
+      raw_even = load_items(tile);
+    } else if (tile & 1) {
+      raw_odd = load_items(tile);
+      if (pair) raw_even = load_items(tile - 1);
+    } else if (!pair) {
+      raw_even = load_items(tile);  // an even tile with no odd one after it
+    }  // (else an even tile loaded with the odd one after it)
 #pragma unroll
     for (int k = 0; k < BCI; ++k) {
       const int i = tid + k * NT;
@@ -156,6 +161,14 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
       rc[k] = on ? Cg[n * p.C_sn + t0 + t] : IO(0);
     }
   };
+  // the delta bias of each prologue item's channel, read once: inside the tile loop the compiler
+  // would read it again every tile (the loop's stores might alias it) and wait for it
+  float item_bias[IPT];
+#pragma unroll
+  for (int it = 0; it < IPT; ++it) {
+    const int64_t dd = d0 + (tid + it * NT) / CPT;
+    item_bias[it] = (dd < p.dim && p.delta_bias) ? p.delta_bias[dd] : 0.0f;
+  }
   auto fill = [&](int64_t tile) __attribute__((always_inline)) {
     const int64_t t0 = tile * kBT;
     const int lt_len = (int)min<int64_t>(kBT, L - t0);
@@ -165,12 +178,23 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
       const int r = item / CPT, tl = (item % CPT) * V;
       const int64_t dd = d0 + r;
       const int cnt = dd < p.dim ? max(0, min(V, lt_len - tl)) : 0;
-      const float bias = (dd < p.dim && p.delta_bias) ? p.delta_bias[dd] : 0.0f;
+      const float bias = item_bias[it];
+      // this tile's chunks (both sets are complete here: the other one was loaded with them or
+      // before them)
+      const bool odd = PREFETCH && (tile & 1);
+      u32x4 cw[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        // a select of the two values (of two lvalues it would select an address, and the
+        // chunks would go to memory)
+        const u32x4 vo = raw_odd.c[it][c], ve = raw_even.c[it][c];
+        cw[c] = odd ? vo : ve;
+      }
       float xv[V], dv_raw[V], gv[V], zv[V];
-      unpack16<IO>(raw.c[it][0], xv);
-      unpack16<IO>(raw.c[it][1], dv_raw);
-      unpack16<IO>(raw.c[it][2], gv);
-      if constexpr (GATE) unpack16<IO>(raw.c[it][3], zv);
+      unpack16<IO>(cw[0], xv);
+      unpack16<IO>(cw[1], dv_raw);
+      unpack16<IO>(cw[2], gv);
+      if constexpr (GATE) unpack16<IO>(cw[3], zv);
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         float dl = 0.0f, gy = 0.0f, xx = 0.0f, gzf = 0.0f;
@@ -200,23 +224,94 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
   };
 
   const int64_t ntile = (L + kBT - 1) / kBT;
-  // tile pairs (2m, 2m + 1) share their 128-byte lines; the last tile is alone if it is even
-  issue(ntile - 1, (ntile - 1) & 1);
-  for (int64_t tile = ntile - 1; tile >= 0; --tile) {
+  // the checkpoints of a tile's sub-tiles (channel-contiguous). A sub-tile entirely past L has
+  // none: its steps are padding, and it starts from 0.
+  auto load_ck = [&](int64_t tile, int k, float (&hv)[NS]) __attribute__((always_inline)) {
+    const float* ck = p.ckpt + ((b * p.ntiles + tile * kSubs) * p.N + n0) * p.dim + (live ? d : 0);
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+      hv[j] = (live && n0 + j < p.N && tile * kBT + k * kSub < L) ? ck[(k * p.N + j) * p.dim] : 0.0f;
+  };
+
+  // A tile's outputs leave from registers while the next tile runs: its dx, ddelta, dz (one
+  // 16-byte word each per prologue item) and its dB, dC partials (one 4-float piece per thread).
+  // The stores are issued after the next tile's inputs have arrived, and every load a wait
+  // is needed for soon is issued before them: a wait for a load also waits for every store
+  // issued before it, so this keeps the stores' latency out of the waits.
+  constexpr int PIECES = 2 * NP * kBT / 4;
+  static_assert(PIECES <= NT && PIECES % 64 == 0, "at most one partial piece per thread");
+  u32x4 out_w[IPT][3];
+  f32x4 out_part = {0.0f, 0.0f, 0.0f, 0.0f};
+  // both partial arrays' addresses as values, selected per lane below (a select between the
+  // two argument fields would load the chosen one from the argument segment, and wait for it)
+  const uint64_t dC_base = reinterpret_cast<uint64_t>(q.dC_part);
+  const uint64_t dB_base = reinterpret_cast<uint64_t>(q.dB_part);
+  auto gather_outputs = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+      const int item = tid + it * NT;
+      const int r = item / CPT, tl = (item % CPT) * V;
+      float vx[V], vd[V], vz[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const f32x4 o = s_in[r * kInStride + tl + e];
+        vx[e] = o.x;
+        vd[e] = o.y;
+        vz[e] = o.z;
+      }
+      out_w[it][0] = pack16<IO>(vx);
+      out_w[it][1] = pack16<IO>(vd);
+      out_w[it][2] = pack16<IO>(vz);
+    }
+    if (tid < PIECES) {
+      const int tensor = tid / (NP * kBT / 4), n = (tid / (kBT / 4)) % NP, tq = (tid % (kBT / 4)) * 4;
+      out_part = *reinterpret_cast<const f32x4*>(s_dbc + (tensor * NP + n) * kBT + tq);
+    }
+  };
+  auto put_outputs = [&](int64_t tile) __attribute__((always_inline)) {
     const int64_t t0 = tile * kBT;
     const int lt_len = (int)min<int64_t>(kBT, L - t0);
-    fill(tile);
-    // the checkpoints of the tile's sub-tiles (channel-contiguous); the last sub-tile's is
-    // read now and each earlier one while the sub-tile after it runs. A sub-tile entirely past
-    // L has none: its steps are padding, and it starts from 0.
-    const float* ck = p.ckpt + ((b * p.ntiles + tile * kSubs) * p.N + n0) * p.dim + (live ? d : 0);
-    auto load_ck = [&](int k, float (&hv)[NS]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < NS; ++j)
-        hv[j] = (live && n0 + j < p.N && t0 + k * kSub < L) ? ck[(k * p.N + j) * p.dim] : 0.0f;
-    };
-    float hnext[NS];
-    load_ck(kSubs - 1, hnext);
+    for (int it = 0; it < IPT; ++it) {
+      const int item = tid + it * NT;
+      const int r = item / CPT, tl = (item % CPT) * V;
+      const int64_t dd = d0 + r;
+      const int cnt = dd < p.dim ? max(0, min(V, lt_len - tl)) : 0;
+      if (cnt > 0) {
+        const bool full = q.vec_out != 0;
+        store_raw16<IO>(static_cast<IO*>(q.dx) + b * p.x_sb + dd * p.x_sd, t0 + tl, cnt, full,
+                        out_w[it][0]);
+        store_raw16<IO>(static_cast<IO*>(q.ddelta) + b * p.dl_sb + dd * p.dl_sd, t0 + tl, cnt,
+                        full, out_w[it][1]);
+        if constexpr (GATE)
+          store_raw16<IO>(static_cast<IO*>(q.dz) + b * p.z_sb + dd * p.z_sd, t0 + tl, cnt, full,
+                          out_w[it][2]);
+      }
+    }
+    if (tid < PIECES) {
+      const int tensor = tid / (NP * kBT / 4), n = (tid / (kBT / 4)) % NP, tq = (tid % (kBT / 4)) * 4;
+      const int cnt = n < p.N ? max(0, min(4, lt_len - tq)) : 0;
+      float* dst = reinterpret_cast<float*>(tensor == 0 ? dC_base : dB_base) +
+                   ((b * p.groups_per_batch + wg) * p.N + n) * L + t0 + tq;
+      if (q.part_vec && cnt == 4) {
+        *reinterpret_cast<f32x4*>(dst) = out_part;
+      } else {
+        const float pv[4] = {out_part.x, out_part.y, out_part.z, out_part.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (e < cnt) dst[e] = pv[e];
+      }
+    }
+  };
+
+  // tile pairs (2m, 2m + 1) share their 128-byte lines; the last tile is alone if it is even
+  issue(ntile - 1, (ntile - 1) & 1);
+  // the start state of the tile's last sub-tile, read one sub-tile ahead like the others
+  float hnext[NS];
+  load_ck(ntile - 1, kSubs - 1, hnext);
+  for (int64_t tile = ntile - 1; tile >= 0; --tile) {
+    fill(tile);
+    if (tile + 1 < ntile) put_outputs(tile + 1);
     __syncthreads();
     if (PREFETCH && tile > 0) issue(tile - 1, true);
 
@@ -232,7 +327,9 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
       float hsk[NS];
 #pragma unroll
       for (int j = 0; j < NS; ++j) hsk[j] = hnext[j];
-      if (k > 0) load_ck(k - 1, hnext);
+      // the next sub-tile's start state: this tile's, or the last one of the tile before
+      if (k > 0) load_ck(tile, k - 1, hnext);
+      else if (tile > 0) load_ck(tile - 1, kSubs - 1, hnext);
       // recompute the sub-tile's states (after each step), their decays and the readout partials
       float hh[kSub][NS], dAk[kSub][NS];
 #pragma unroll
@@ -320,47 +417,12 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
       __syncthreads();  // s_red is reused by the next sub-tile
     }
 
-    // ---- the tile's outputs: dx, ddelta, dz from the s_in slots, 16 bytes per store, by the
-    // thread whose prologue item covers the same slots (no barrier needed before its next
-    // prologue writes them); the dB, dC partials from s_dbc
-#pragma unroll
-    for (int it = 0; it < IPT; ++it) {
-      const int item = tid + it * NT;
-      const int r = item / CPT, tl = (item % CPT) * V;
-      const int64_t dd = d0 + r;
-      const int cnt = dd < p.dim ? max(0, min(V, lt_len - tl)) : 0;
-      if (cnt > 0) {
-        float vx[V], vd[V], vz[V];
-#pragma unroll
-        for (int e = 0; e < V; ++e) {
-          const f32x4 o = s_in[r * kInStride + tl + e];
-          vx[e] = o.x;
-          vd[e] = o.y;
-          vz[e] = o.z;
-        }
-        const bool full = q.vec_out && cnt == V;
-        store_chunk<IO>(static_cast<IO*>(q.dx) + b * p.x_sb + dd * p.x_sd, t0 + tl, cnt, full, vx);
-        store_chunk<IO>(static_cast<IO*>(q.ddelta) + b * p.dl_sb + dd * p.dl_sd, t0 + tl, cnt,
-                        full, vd);
-        if constexpr (GATE)
-          store_chunk<IO>(static_cast<IO*>(q.dz) + b * p.z_sb + dd * p.z_sd, t0 + tl, cnt, full, vz);
-      }
-    }
-    static_assert((2 * NP * kBT / 4) % 64 == 0, "4-float pieces of the partials per wavefront");
-    for (int pc = tid; pc < 2 * NP * kBT / 4; pc += NT) {
-      const int tensor = pc / (NP * kBT / 4), n = (pc / (kBT / 4)) % NP, tq = (pc % (kBT / 4)) * 4;
-      const int cnt = n < p.N ? max(0, min(4, lt_len - tq)) : 0;
-      float* dst = (tensor == 0 ? q.dC_part : q.dB_part) +
-                   ((b * p.groups_per_batch + wg) * p.N + n) * L + t0 + tq;
-      const float* src = s_dbc + (tensor * NP + n) * kBT + tq;
-      if (q.part_vec && cnt == 4) {
-        *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(src);
-      } else {
-        for (int e = 0; e < cnt; ++e) dst[e] = src[e];
-      }
-    }
+    // the tile's outputs into registers (each thread reads the s_in slots of its own prologue
+    // item, which only it overwrites next; s_dbc is written again after the next barrier)
+    gather_outputs();
     if (!PREFETCH && tile > 0) issue(tile - 1, false);
   }
+  put_outputs(0);
 
   // ---- per-workgroup partials of the batch-summed gradients, and dh0
   if (live) {

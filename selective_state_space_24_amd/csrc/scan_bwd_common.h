@@ -110,4 +110,40 @@ __device__ __forceinline__ u32x4 load_raw16(const IO* __restrict__ row, int64_t 
   return u32x4{ws[0], ws[1], ws[2], ws[3]};
 }
 
+// kVec io values as one 16-byte word (bf16 rounded to nearest even, as store_chunk does)
+template <typename IO>
+__device__ __forceinline__ u32x4 pack16(const float (&v)[IoTraits<IO>::kVec]) {
+  uint32_t ws[4];
+  if constexpr (IoTraits<IO>::kVec == 8) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ws[k] = pack_bf16x2(v[2 * k], v[2 * k + 1]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ws[k] = __float_as_uint(v[k]);
+  }
+  return u32x4{ws[0], ws[1], ws[2], ws[3]};
+}
+
+// stores a word made by pack16 at row[t ..): whole (write-once hint) when vec_ok and all kVec
+// elements are valid, else its first cnt elements one by one
+template <typename IO>
+__device__ __forceinline__ void store_raw16(IO* __restrict__ row, int64_t t, int cnt, bool vec_ok,
+                                            const u32x4 w) {
+  constexpr int V = IoTraits<IO>::kVec;
+  if (vec_ok && cnt == V) {
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(row + t));
+    return;
+  }
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int e = 0; e < V; ++e) {
+    if (e >= cnt) continue;
+    if constexpr (V == 8) {
+      row[t + e] = (IO)((ws[e / 2] >> (16 * (e & 1))) & 0xffffu);
+    } else {
+      row[t + e] = __uint_as_float(ws[e]);
+    }
+  }
+}
+
 }  // namespace ssm
