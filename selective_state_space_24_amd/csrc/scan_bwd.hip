@@ -310,6 +310,7 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
   float hnext[NS];
   load_ck(ntile - 1, kSubs - 1, hnext);
   for (int64_t tile = ntile - 1; tile >= 0; --tile) {
+    const int lt_len = (int)min<int64_t>(kBT, L - tile * kBT);
     fill(tile);
     if (tile + 1 < ntile) put_outputs(tile + 1);
     __syncthreads();
@@ -408,7 +409,9 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
           const float vx = fmaf(in.z, eD, gxsum);
           const float vd = gds * (p.softplus ? sigmoid_from_softplus(in.x) : 1.0f);
           dD_acc = fmaf(in.z, in.w, dD_acc);
-          dbias_acc += vd;
+          // (a padding step past L adds nothing: its vd is not zero when a final-state
+          // gradient flows through it and delta takes no softplus)
+          if (t < lt_len) dbias_acc += vd;
           // the step's inputs are dead now (this thread read them last): the slot holds the
           // outputs until the tile is written out
           s_in[er * kInStride + t] = f32x4{vx, vd, vz, 0.0f};

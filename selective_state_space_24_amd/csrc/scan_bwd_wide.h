@@ -85,6 +85,9 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_wide_kernel(const BwdParams q)
                            3 * NW * kChannelsPerGroup * RED * 4 + NW * NV * kSumS * 4;
   constexpr bool kStageDbc = NW == 8 || kLdsRest + 2 * NP * kDbcS * 4 <= 80 * 1024;
   __shared__ float s_dbc[kStageDbc ? 2 * NP * kDbcS : 1];
+  // head mode: each channel's ddelta (summed over the wavefronts) at the block's steps, for the
+  // sums over runs of channels
+  __shared__ float s_hd[HEAD ? kChannelsPerGroup * RED : 1];
 
   const ScanParams& p = q.f;
   const int tid = threadIdx.x;
@@ -123,9 +126,15 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_wide_kernel(const BwdParams q)
 #pragma unroll
   for (int j = 0; j < (HEAD ? 1 : NS); ++j) da[j] = 0.0f;
 
-  float dD_acc[IPE], dbias_acc[IPE];
+  float dD_acc[IPE], dbias_acc[IPE], eD_item[IPE];
 #pragma unroll
-  for (int r = 0; r < IPE; ++r) dD_acc[r] = dbias_acc[r] = 0.0f;
+  for (int r = 0; r < IPE; ++r) {
+    dD_acc[r] = dbias_acc[r] = 0.0f;
+    // D of the epilogue item's channel, read once (inside the loops it would be read, and
+    // waited for, every block: the loops' stores might alias it)
+    const int64_t ed = d0 + (tid + r * NT) / SUB;
+    eD_item[r] = (ed < p.dim && p.D) ? p.D[min(ed, p.dim - 1)] : 0.0f;
+  }
 
   float* const red = s_sum + w * NV * kSumS + lane;  // this lane's column entries
   const int rows_per_wg = kChannelsPerGroup / (HEAD ? (int)q.span : 1);
@@ -364,42 +373,43 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_wide_kernel(const BwdParams q)
             gxs += s_red[((2 * NW + ww) * kChannelsPerGroup + er) * RED + i];
           }
           const f32x4 in = s_in[er * kInS + t];
-          const float eD = (ed < p.dim && p.D) ? p.D[ed] : 0.0f;
+          const float eD = eD_item[r];
           const float vx = fmaf(in.z, eD, gxs);
           dD_acc[r] = fmaf(in.z, in.w, dD_acc[r]);
-          if (ed < p.dim && tt < L) {
-            store_elem(static_cast<IO*>(q.dx) + b * p.x_sb + ed * p.x_sd + tt, vx);
-            if constexpr (GATE) {
-              const float y0 = fmaf(eD, in.w, ys);
-              store_elem(static_cast<IO*>(q.dz) + b * p.z_sb + ed * p.z_sd + tt,
-                         s_gz[er * kInS + t] * y0);
-            }
+          float vz = 0.0f, vd = 0.0f;
+          if constexpr (GATE) vz = s_gz[er * kInS + t] * fmaf(eD, in.w, ys);
+          if constexpr (HEAD) {
+            s_hd[er * RED + i] = gds;
+          } else {
+            vd = gds * (p.softplus ? sigmoid_from_softplus(in.x) : 1.0f);
+            // (a padding step past L adds nothing: its vd is not zero when a final-state
+            // gradient flows through it and delta takes no softplus)
+            if (ed < p.dim && tt < L) dbias_acc[r] += vd;
           }
-          if constexpr (!HEAD) {
-            const float vd = gds * (p.softplus ? sigmoid_from_softplus(in.x) : 1.0f);
-            dbias_acc[r] += vd;
-            if (ed < p.dim && tt < L)
-              store_elem(static_cast<IO*>(q.ddelta) + b * p.dl_sb + ed * p.dl_sd + tt, vd);
-          }
+          // the step's inputs are dead now (later blocks take earlier steps): the slot holds
+          // the outputs until the tile is written out
+          s_in[er * kInS + t] = f32x4{vx, vd, vz, 0.0f};
         }
+        __syncthreads();  // s_red is reused by the next block; s_hd is complete
         if constexpr (HEAD) {
           // ddelta before the activation, summed over each run of `span` channels (all in one
-          // head); the head's rows are added by bwd_head_delta
-          const int span = (int)q.span;
-          for (int item = tid; item < rows_per_wg * SUB; item += NT) {
+          // head; the head's rows are added by bwd_head_delta). A wavefront takes 64 / span
+          // (run, step) items at once, a lane per channel, and adds each run's lanes by lane
+          // exchanges in a fixed order.
+          const int span = (int)q.span;  // a power of two, at most 64
+          const int per = 64 / span;
+          const int nitems = rows_per_wg * SUB;
+          const int g = lane / span, c = lane % span;
+          for (int base = w * per; base < nitems; base += NW * per) {
+            const int item = base + g;
             const int rr = item / SUB, i = item % SUB;
+            float v = item < nitems ? s_hd[(rr * span + c) * RED + i] : 0.0f;
+            for (int off = 1; off < span; off <<= 1) v = xor_sum(v, off);
             const int64_t tt = t0 + tm + i;
-            float gsum = 0.0f;
-            for (int c = 0; c < span; ++c) {
-#pragma unroll
-              for (int ww = 0; ww < NW; ++ww)
-                gsum += s_red[((1 * NW + ww) * kChannelsPerGroup + rr * span + c) * RED + i];
-            }
-            if (d0 + (int64_t)rr * span < p.dim && tt < L)
-              q.ddl_part[(b * (p.dim / span) + d0 / span + rr) * L + tt] = gsum;
+            if (c == 0 && item < nitems && d0 + (int64_t)rr * span < p.dim && tt < L)
+              q.ddl_part[(b * (p.dim / span) + d0 / span + rr) * L + tt] = v;
           }
         }
-        __syncthreads();  // s_red is reused by the next block
       }
     }
     // the tile's dC, dB partials: whole rows of its steps (16-byte stores where the rows allow
@@ -419,6 +429,29 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_wide_kernel(const BwdParams q)
           for (int e = 0; e < 4 && t4 + e < len; ++e) dst[e] = src[e];
         }
       }
+    }
+    // dx, dz (and ddelta per channel) of the tile from the s_in slots, 16 bytes per store, by
+    // the thread whose prologue item covers the same slots (its next prologue writes them)
+    for (int item = tid; item < ITEMS; item += NT) {
+      const int r = item / CPT, tl = (item % CPT) * V;
+      const int64_t dd = d0 + r;
+      const int cnt = dd < p.dim ? max(0, min(V, len - tl)) : 0;
+      if (cnt == 0) continue;
+      float vx[V], vd[V], vz[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const f32x4 o = s_in[r * kInS + tl + e];
+        vx[e] = o.x;
+        vd[e] = o.y;
+        vz[e] = o.z;
+      }
+      const bool full = q.vec_out != 0;
+      store_chunk<IO>(static_cast<IO*>(q.dx) + b * p.x_sb + dd * p.x_sd, t0 + tl, cnt, full, vx);
+      if constexpr (GATE)
+        store_chunk<IO>(static_cast<IO*>(q.dz) + b * p.z_sb + dd * p.z_sd, t0 + tl, cnt, full, vz);
+      if constexpr (!HEAD)
+        store_chunk<IO>(static_cast<IO*>(q.ddelta) + b * p.dl_sb + dd * p.dl_sd, t0 + tl, cnt,
+                        full, vd);
     }
     // the next tile's prologue overwrites s_in, s_B, s_C and its steps s_dbc: every wavefront is
     // past its reads (the barrier that begins the next tile's steps)

@@ -124,6 +124,23 @@ def test_backward_head_mode_zoh_and_wide_states(case):
     _compare(cfg, inputs, _dy(cfg, L), hinit, zoh=zoh, dhf=dhfin)
 
 
+@pytest.mark.parametrize("N,zoh", [(16, False), (32, False), (16, True)],
+                         ids=["four-state-kernel", "wide-kernel", "wide-kernel-zoh"])
+def test_final_state_gradient_without_softplus(N, zoh):
+    """delta taken as given (no softplus), with a bias and a final-state gradient, and L = 100,
+    which is not a multiple of either kernel's tile. The padding steps of the last tile are run
+    in reverse first, while the gradient is the final-state one; their ddelta term is not zero
+    without the softplus factor, and must not reach the bias gradient."""
+    dists = {"delta": ssmgen.Dist(ssmgen.UNIFORM, 0.0, 0.2),
+             "delta_bias": ssmgen.Dist(ssmgen.UNIFORM, 0.001, 0.01)}
+    cfg = ssmgen.ScanConfig(name="bwd-nosp-dhf", batch=2, dim=64, L=100, N=N, io="f32", gate=True,
+                            softplus=False, has_D=True, has_bias=True, seed=4711 + N, dists=dists)
+    _say(f"[bwd] no softplus, final-state gradient, N={N}, zoh={zoh}")
+    inputs = ssmgen.make_inputs(cfg)
+    dhfin = np.random.default_rng(N).standard_normal((2, 64, N)).astype(np.float32)
+    _compare(cfg, inputs, _dy(cfg, cfg.L), zoh=zoh, dhf=dhfin)
+
+
 @pytest.mark.parametrize("ci", [0, 1])
 def test_backward_configs(ci):
     cfg = ssmgen.CONFIGS[ci]
