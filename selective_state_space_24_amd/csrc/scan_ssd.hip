@@ -121,6 +121,26 @@ __device__ __forceinline__ u32x4 mask8(const u32x4 w, int nv) {
   return r;
 }
 
+// v moved across lanes by the DPP control CTRL in the rows of ROW_MASK; a lane outside those rows,
+// or whose source lane lies outside its row, gets 0
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_or_zero(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+// Inclusive prefix sum over the 64 lanes, in registers: shifts right by 1, 2, 4 and 8 lanes
+// within each row of 16 lanes (row_shr), then the last lane of rows 0 and 2 is added to rows 1
+// and 3 (row_bcast:15), and the last lane of row 1, by then the sum of lanes 0..31, to rows 2
+// and 3 (row_bcast:31). Six dependent VALU instructions instead of six LDS round trips.
+__device__ __forceinline__ float wave_inclusive_sum(float v) {
+  v += dpp_or_zero<0x111, 0xf>(v);
+  v += dpp_or_zero<0x112, 0xf>(v);
+  v += dpp_or_zero<0x114, 0xf>(v);
+  v += dpp_or_zero<0x118, 0xf>(v);
+  v += dpp_or_zero<0x142, 0xa>(v);
+  v += dpp_or_zero<0x143, 0xc>(v);
+  return v;
+}
+
 // Per-chunk step arrays in LDS, kQ floats each: s2 = s_t log2 e, w = w_t, es = e^{s_t},
 // cw = e^{s_Q - s_t} w_t.
 struct StepArrays {
@@ -308,13 +328,8 @@ __global__ void __launch_bounds__(kThreads, 1)
       // 1e-3 even when single steps decay by far more (large delta times large |A|)
       a2 = fmaxf(a2, -160.0f);
       // inclusive prefix sum over the 64 steps of the chunk
-      float s2 = a2;
-#pragma unroll
-      for (int k = 1; k < 64; k <<= 1) {
-        const float o = __shfl_up(s2, k, 64);
-        if (lane >= k) s2 += o;
-      }
-      const float sQ = __shfl(s2, 63, 64);
+      const float s2 = wave_inclusive_sum(a2);
+      const float sQ = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s2), 63));
       StepArrays& A = sa[par];
       A.s2[lane] = s2;
       A.w[lane] = w;
