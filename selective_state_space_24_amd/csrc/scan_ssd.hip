@@ -20,9 +20,10 @@
 // Work decomposition: one workgroup = one batch entry x 64 channels of one head (P = 64), four
 // wavefronts, the whole sequence in order. Wavefront w owns channels p in [16w, 16w + 16) and all
 // N states of H for them (N/16 accumulator tiles). Per chunk:
-//   1. G^T[j][t] = sum_n B[n][j] C[n][t] for the 10 causal 16x16 tiles (split over the
-//      wavefronts), masked, scaled by e^{s_t - s_j} w_j and stored as bf16 hi and lo parts in
-//      LDS (Lmat[t][j]).
+//   1. G^T[j][t] = sum_n B[n][j] C[n][t] for the 10 causal 16x16 tiles, masked, scaled by
+//      e^{s_t - s_j} w_j and stored as bf16 hi and lo parts in LDS (Lmat[t][j]). The tiles are
+//      split over the wavefronts so that a wavefront's tiles share one operand, which it reads
+//      from LDS once: (0,0) (0,1) (0,2); (0,3) (1,3) (2,3); (1,1) (1,2); (2,2) (3,3).
 //   2. Y = (e^{s_t} (C^T H)) + Lmat x for the wavefront's channels; H enters as the B operand
 //      straight from its accumulators (the k-slot order of the operand is chosen to match the
 //      accumulator layout, and C^T is read in the same order).
@@ -42,6 +43,8 @@
 // A[c][8g .. 8g+8), B operand holds B[8g .. 8g+8)[c], the accumulator holds D[4g .. 4g+4)[c].
 // Output rows of the Y tiles are permuted so that lane (g, c) ends up with the 16 consecutive
 // steps [16g, 16g+16) of channel 16w + c: x, z and y then move 32 contiguous bytes per lane.
+#include <type_traits>
+
 #include "scan_kernels.h"
 
 namespace ssm {
@@ -306,9 +309,10 @@ __global__ void __launch_bounds__(kThreads, 1)
     const uint32_t base = (uint32_t)(uintptr_t)(par ? (lds_u8*)stage1 : (lds_u8*)stage0);
     if (wave == 3 && lane < 8) dma16(dlrow + word_at(ch * kQ + 8 * lane, L), base + kOffD);
   };
-  // step arrays of chunk ch (wavefront 3), after its loads have landed
+  // step arrays of chunk ch (wavefront 2, which has the fewest G^T operands to read), after
+  // its loads have landed
   auto steps = [&](int64_t ch, const int par) __attribute__((always_inline)) {
-    if (wave == 3) {
+    if (wave == 2) {
       const int64_t t = ch * kQ + lane;
       const bool valid = t < L;
       const lds_u8* buf = par ? (const lds_u8*)stage1 : (const lds_u8*)stage0;
@@ -338,10 +342,7 @@ __global__ void __launch_bounds__(kThreads, 1)
     }
   };
 
-  // G^T tile k of the 10 causal tiles (jt <= tt), in the order (0,0) (0,1) (0,2) (0,3) (1,1)
-  // (1,2) (1,3) (2,2) (2,3) (3,3): masked, decay-weighted, split and stored into Lmat.
-  auto tile_jt = [](int k) { return k < 4 ? 0 : (k < 7 ? 1 : (k < 9 ? 2 : 3)); };
-  auto tile_tt = [](int k, int jt) { return jt + k - (jt == 0 ? 0 : (jt == 1 ? 4 : (jt == 2 ? 7 : 9))); };
+  // G^T tile (jt, tt) (jt <= tt): masked, decay-weighted, split and stored into Lmat.
   auto store_lmat = [&](const StepArrays& A, int jt, int tt, const f32x4 acc)
       __attribute__((always_inline)) {
     // acc[q] = G^T[j = 16jt + 4g + q][t = 16tt + c]
@@ -370,6 +371,42 @@ __global__ void __launch_bounds__(kThreads, 1)
     const u32x2 hi = ldtr(tile, off_st(n + 4, slot) + 8 * (tr_r & 1));
     return u32x4{lo[0], lo[1], hi[0], hi[1]};
   };
+
+  // G^T tiles that share one operand: with SB the B block S and the C blocks O0, O1, O2, i.e.
+  // tiles (S, O_i); otherwise the C block S and the B blocks O_i, tiles (O_i, S). CNT tiles
+  // (the first CNT of the O_i). Every argument is a std::integral_constant.
+  auto shared_tiles = [&](const StepArrays& A, const lds_u8* bt, const lds_u8* ct, auto sb,
+                          auto s_blk, auto cnt, auto o0, auto o1, auto o2)
+      __attribute__((always_inline)) {
+    constexpr bool SB = decltype(sb)::value;
+    constexpr int S = decltype(s_blk)::value, CNT = decltype(cnt)::value;
+    constexpr int O[3] = {decltype(o0)::value, decltype(o1)::value, decltype(o2)::value};
+    u32x4 sh[NK], ot[CNT][NK];
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      sh[kk] = g_operand(SB ? bt : ct, S, kk);
+#pragma unroll
+      for (int i = 0; i < CNT; ++i) ot[i][kk] = g_operand(SB ? ct : bt, O[i], kk);
+    }
+    f32x4 g[CNT];
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) g[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+#pragma unroll
+      for (int i = 0; i < CNT; ++i)
+        g[i] = SB ? mma(sh[kk], ot[i][kk], g[i]) : mma(ot[i][kk], sh[kk], g[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) store_lmat(A, SB ? S : O[i], SB ? O[i] : S, g[i]);
+  };
+  using ic0 = std::integral_constant<int, 0>;
+  using ic1 = std::integral_constant<int, 1>;
+  using ic2 = std::integral_constant<int, 2>;
+  using ic3 = std::integral_constant<int, 3>;
+  using kB = std::integral_constant<bool, true>;
+  using kC = std::integral_constant<bool, false>;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
 
   // chunk ch, par = ch & 1 (a constant at both calls)
   auto chunk = [&](int64_t ch, const int par) __attribute__((always_inline)) {
@@ -412,38 +449,16 @@ __global__ void __launch_bounds__(kThreads, 1)
       sync_lds();
     }
 
-    // 1. Lmat: tiles wave and wave + 4 for every wavefront, wave + 8 for wavefronts 0 and 1
-    {
-      const int jt0 = tile_jt(wave), tt0 = tile_tt(wave, jt0);
-      const int jt1 = tile_jt(wave + 4), tt1 = tile_tt(wave + 4, jt1);
-      u32x4 a0[NK], b0[NK], a1[NK], b1[NK];
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
-        a0[kk] = g_operand(bt, jt0, kk);
-        b0[kk] = g_operand(ct, tt0, kk);
-        a1[kk] = g_operand(bt, jt1, kk);
-        b1[kk] = g_operand(ct, tt1, kk);
-      }
-      f32x4 g0 = {0.f, 0.f, 0.f, 0.f}, g1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
-        g0 = mma(a0[kk], b0[kk], g0);
-        g1 = mma(a1[kk], b1[kk], g1);
-      }
-      store_lmat(A, jt0, tt0, g0);
-      store_lmat(A, jt1, tt1, g1);
-      if (wave < 2) {
-        const int jt2 = tile_jt(wave + 8), tt2 = tile_tt(wave + 8, jt2);
-#pragma unroll
-        for (int kk = 0; kk < NK; ++kk) {
-          a0[kk] = g_operand(bt, jt2, kk);
-          b0[kk] = g_operand(ct, tt2, kk);
-        }
-        f32x4 g2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < NK; ++kk) g2 = mma(a0[kk], b0[kk], g2);
-        store_lmat(A, jt2, tt2, g2);
-      }
+    // 1. Lmat: the wavefront's G^T tiles (see the header comment)
+    if (wv == 0) {
+      shared_tiles(A, bt, ct, kB{}, ic0{}, ic3{}, ic0{}, ic1{}, ic2{});
+    } else if (wv == 1) {
+      shared_tiles(A, bt, ct, kC{}, ic3{}, ic3{}, ic0{}, ic1{}, ic2{});
+    } else if (wv == 2) {
+      shared_tiles(A, bt, ct, kB{}, ic1{}, ic2{}, ic1{}, ic2{}, ic0{});
+    } else {
+      shared_tiles(A, bt, ct, kB{}, ic2{}, ic1{}, ic2{}, ic0{}, ic0{});
+      shared_tiles(A, bt, ct, kB{}, ic3{}, ic1{}, ic3{}, ic0{}, ic0{});
     }
     sync_lds();
 
@@ -569,6 +584,7 @@ __global__ void __launch_bounds__(kThreads, 1)
   issue_delta(0, 0);
   if (nchunks > 1) issue_delta(1, 1);
   wait_vmem_all();
+  __syncthreads();  // wavefront 3's delta loads have landed
   steps(0, 0);
   __syncthreads();
   for (int64_t ch = 0; ch < nchunks; ch += 2) {
