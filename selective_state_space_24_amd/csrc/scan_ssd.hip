@@ -449,16 +449,33 @@ __global__ void __launch_bounds__(kThreads, 1)
       sync_lds();
     }
 
-    // 1. Lmat: the wavefront's G^T tiles (see the header comment)
+    // 1. Lmat: the wavefront's G^T tiles (see the header comment). The bf16 hi and lo parts of
+    //    H that step 2 takes are made in the same block, where they overlap the tiles' products.
+    //    k-slots of step kk: states 32kk + 4g + (0..3), then 32kk + 16 + 4g + (0..3)
+    u32x4 hb[NK], hl[NK];
+    auto split_h = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        const u32x2 h01 = split2(H[2 * kk][0], H[2 * kk][1]), h23 = split2(H[2 * kk][2], H[2 * kk][3]);
+        const u32x2 h45 = split2(H[2 * kk + 1][0], H[2 * kk + 1][1]);
+        const u32x2 h67 = split2(H[2 * kk + 1][2], H[2 * kk + 1][3]);
+        hb[kk] = u32x4{h01[0], h23[0], h45[0], h67[0]};
+        hl[kk] = u32x4{h01[1], h23[1], h45[1], h67[1]};
+      }
+    };
     if (wv == 0) {
       shared_tiles(A, bt, ct, kB{}, ic0{}, ic3{}, ic0{}, ic1{}, ic2{});
+      split_h();
     } else if (wv == 1) {
       shared_tiles(A, bt, ct, kC{}, ic3{}, ic3{}, ic0{}, ic1{}, ic2{});
+      split_h();
     } else if (wv == 2) {
       shared_tiles(A, bt, ct, kB{}, ic1{}, ic2{}, ic1{}, ic2{}, ic0{});
+      split_h();
     } else {
       shared_tiles(A, bt, ct, kB{}, ic2{}, ic1{}, ic2{}, ic0{}, ic0{});
       shared_tiles(A, bt, ct, kB{}, ic3{}, ic1{}, ic3{}, ic0{}, ic0{});
+      split_h();
     }
     sync_lds();
 
@@ -471,12 +488,6 @@ __global__ void __launch_bounds__(kThreads, 1)
       for (int i = 0; i < 4; ++i) Y[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        // k-slots: states 32kk + 4g + (0..3), then 32kk + 16 + 4g + (0..3)
-        const u32x2 h01 = split2(H[2 * kk][0], H[2 * kk][1]), h23 = split2(H[2 * kk][2], H[2 * kk][3]);
-        const u32x2 h45 = split2(H[2 * kk + 1][0], H[2 * kk + 1][1]);
-        const u32x2 h67 = split2(H[2 * kk + 1][2], H[2 * kk + 1][3]);
-        const u32x4 hb = {h01[0], h23[0], h45[0], h67[0]};
-        const u32x4 hl = {h01[1], h23[1], h45[1], h67[1]};
         const int n = 32 * kk + 4 * g + tr_q;
         u32x4 ca[4];
 #pragma unroll
@@ -487,9 +498,9 @@ __global__ void __launch_bounds__(kThreads, 1)
           ca[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Y[i] = mma(ca[i], hb, Y[i]);
+        for (int i = 0; i < 4; ++i) Y[i] = mma(ca[i], hb[kk], Y[i]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Y[i] = mma(ca[i], hl, Y[i]);
+        for (int i = 0; i < 4; ++i) Y[i] = mma(ca[i], hl[kk], Y[i]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) Y[i] *= *reinterpret_cast<const f32x4*>(&A.es[16 * g + 4 * i]);
