@@ -17,7 +17,7 @@ constexpr int64_t kMaxSegments = 65535;       // grid.y limit
 struct Plan {
   int64_t nseg;
   int64_t seg_len;
-  bool state_split = false;  // bf16 io, 8 < dstate <= 16: the state-split kernel (see below)
+  bool narrow_groups = false;  // bf16 io, 8 < dstate <= 16: 64-channel workgroups (see below)
   bool wave = false;         // bf16 io, 8 < dstate <= 16: the kernel with independent wavefronts
   bool fix = false;          // its split with a zero-start output pass and a correcting pass
 };
@@ -127,13 +127,13 @@ Plan plan_segments(const ssm_scan_desc* d) {
   int64_t want = (kTargetWaves + waves - 1) / waves;
   if (d->io_dtype == SSM_DTYPE_BF16 && d->dstate > 8 && d->dstate <= 16) {
     // bf16 io with 8 < N <= 16 runs the kernel with independent wavefronts, one 8-wavefront
-    // workgroup (128 channels) per CU, except where state_split_one_pass holds: then the
-    // barrier-synchronised kernel whose wavefronts split the states needs no summary pass, and
-    // its 64-channel workgroups spread over more CUs (measured 165 us with eight wavefronts of
-    // two states, 183 us with four of four, against 192-204 us split along L, at batch 8,
-    // d_inner 1536, L 2048, and likewise at 8 x 2048 and 4 x 4096 channels)
-    if (ssm::state_split_one_pass(groups)) {
-      p.state_split = true;
+    // workgroup (128 channels) per CU, except where narrow_one_pass holds: then 64-channel
+    // workgroups of four wavefronts spread over more CUs and need no summary pass (measured
+    // 163 us per-step median; the barrier-synchronised kernel with eight wavefronts of two
+    // states 167 us, with four of four 183 us, against 192-204 us split along L, at batch 8,
+    // d_inner 1536, L 2048)
+    if (ssm::narrow_one_pass(groups)) {
+      p.narrow_groups = true;
       return p;
     }
     p.wave = true;
@@ -438,7 +438,7 @@ int fwd_ext(const ssm_scan_desc* desc, const void* x, const void* delta, const f
   p.groups_per_batch = (d.dim + ssm::kChannelsPerGroup - 1) / ssm::kChannelsPerGroup;
   p.seg_len = plan.seg_len;
   p.nseg = (int32_t)plan.nseg;
-  p.state_split = plan.state_split ? 1 : 0;
+  p.narrow_groups = plan.narrow_groups ? 1 : 0;
   p.fix_split = plan.fix ? 1 : 0;
   p.softplus = delta_softplus ? 1 : 0;
   p.zoh = disc == SSM_DISC_ZOH ? 1 : 0;

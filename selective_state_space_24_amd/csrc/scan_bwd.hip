@@ -543,7 +543,7 @@ static hipError_t bwd_cfg(const BwdParams& q, hipStream_t stream) {
   const ScanParams& p = q.f;
   const int64_t groups = p.batch * p.groups_per_batch;
   // 1. checkpoints (bf16 io with 8 < N <= 16: the kernel with independent wavefronts, except
-  // where the forward's planner takes the state-split kernel, state_split_one_pass: then the
+  // where the forward's planner takes 64-channel workgroups, narrow_one_pass: then the
   // barrier-synchronised kernel's four wavefronts of four states)
   auto four_wave_ckpt = [&]() {
     hipLaunchKernelGGL((scan_fwd_kernel<IO, NS, kWavesPerGroup, false, false, false, false, true>),
@@ -554,7 +554,7 @@ static hipError_t bwd_cfg(const BwdParams& q, hipStream_t stream) {
                        p.delta_bias, nullptr, nullptr, p);
   };
   if constexpr (NS == 4 && WaveIo<IO>::value) {
-    if (!state_split_one_pass(groups)) {
+    if (!narrow_one_pass(groups)) {
       const unsigned wg = (unsigned)(p.batch * ((p.dim + kWaveGroupChannels - 1) / kWaveGroupChannels));
       hipLaunchKernelGGL((scan_fwd_wave_kernel<IO, false, false, false, kWaveCkpt>), dim3(wg, 1),
                          dim3(64 * kWaveGroupWaves), 0, stream, static_cast<const IO*>(p.x),

@@ -33,10 +33,11 @@ inline bool groups_fill_chip(int64_t groups) {
 
 // bf16 io with 8 < N <= 16 normally runs the kernel with independent wavefronts (128-channel,
 // 8-wavefront workgroups, one per CU). With 64-channel groups for three quarters of the CUs or
-// more, but too few 128-channel workgroups to fill the chip, the barrier-synchronised kernel
-// whose wavefronts split the states (64-channel workgroups) runs the whole sequence in one pass
-// instead. The forward planner and the backward checkpoint pass both take this choice from here.
-inline bool state_split_one_pass(int64_t groups) {
+// more, but too few 128-channel workgroups to fill the chip, the whole sequence runs in one pass
+// in 64-channel workgroups instead: four independent wavefronts in the forward pass, the
+// barrier-synchronised kernel's four wavefronts of four states in the backward's checkpoint
+// pass. The forward planner and the backward both take this choice from here.
+inline bool narrow_one_pass(int64_t groups) {
   return groups * 4 >= kCUs * 3 && !groups_fill_chip(groups);
 }
 
@@ -78,9 +79,9 @@ struct ScanParams {
   int32_t zoh;               // zero-order-hold B discretisation instead of delta * B
   int32_t state_vec;         // decode: the state allows 16-byte access (N % 4 == 0, aligned)
   int32_t a_vec;             // decode: rows of A allow 16-byte access
-  int32_t state_split;       // bf16 io, 8 < N <= 16: run scan_fwd_kernel (eight wavefronts of two
-                             // states) in one pass rather than the kernel with independent
-                             // wavefronts (chosen by the segment planner)
+  int32_t narrow_groups;     // bf16 io, 8 < N <= 16: run the kernel with independent wavefronts
+                             // in 64-channel workgroups of four, in one pass (chosen by the
+                             // segment planner)
   int32_t fix_split;         // the kernel with independent wavefronts, split along L: zero-start
                              // output pass, then the correcting pass (rather than a summary pass
                              // first; chosen by the segment planner)

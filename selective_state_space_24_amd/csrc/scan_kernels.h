@@ -2,10 +2,8 @@
 //
 // Two kernels. scan_fwd_wave_kernel (further down) serves bf16 io with 8 < N <= 16: every
 // wavefront owns 16 channels x all states and runs without workgroup barriers. scan_fwd_kernel,
-// described here, serves every other case (fp32 io, N <= 8 or N > 16, and bf16 shapes whose
-// 128-channel workgroups are too few to fill the chip while its 64-channel ones are not: the
-// segment planner's state_split choice) and also runs the backward pass's checkpoints for the
-// shapes it serves. The two split a sequence along L in different ways (see each kernel).
+// described here, serves every other case (fp32 io, N <= 8 or N > 16) and also runs the
+// backward pass's checkpoints for the shapes it serves. The two split a sequence along L in different ways (see each kernel).
 //
 // Work decomposition of scan_fwd_kernel: one workgroup = 64 channels of one batch entry x one
 // segment of L, in NW wavefronts.
@@ -735,10 +733,13 @@ __global__ void __launch_bounds__(64 * NW, (NS <= 4 && NW <= 4) ? 2 : 1)
 // two wavefronts on a SIMD overlap each other's phases freely. The arithmetic per state update
 // and its order are those of scan_fwd_kernel, so both kernels give bit-identical results.
 //
-// A workgroup holds kWaveGroupWaves (8) wavefronts = 128 channels, one workgroup per CU: the two
-// wavefronts that share a SIMD (w and w ^ 4) belong to the same workgroup and use the same
-// batch entry's B and C. They publish their progress in LDS after every half tile and the one
-// that is behind takes the higher issue priority, so neither finishes long after the other.
+// A workgroup holds WGW wavefronts. Normally WGW = kWaveGroupWaves (8), 128 channels, one
+// workgroup per CU: the two wavefronts that share a SIMD (w and w ^ 4) belong to the same
+// workgroup and use the same batch entry's B and C. They publish their progress in LDS after
+// every half tile and the one that is behind takes the higher issue priority, so neither
+// finishes long after the other. Shapes with too few 128-channel groups to fill the chip but
+// enough 64-channel ones (the planner's narrow_groups choice) run WGW = 4: 64-channel
+// workgroups, one wavefront per SIMD, no pacing.
 constexpr int kWaveChannels = 16;
 constexpr int kWaveGroupWaves = 8;
 constexpr int kWaveGroupChannels = kWaveChannels * kWaveGroupWaves;
@@ -772,8 +773,8 @@ constexpr int kWaveRowStride = kTB + 4;     // floats per state row of B / C, pe
 // thousand steps, so the second wins once segments are long.
 constexpr int kWaveOut = 0, kWaveSummary = 1, kWaveCkpt = 2, kWaveOutSum = 3, kWaveFix = 4;
 
-template <typename IO, bool HEAD, bool GATE, bool ZOH, int MODE = kWaveOut>
-__global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
+template <typename IO, bool HEAD, bool GATE, bool ZOH, int MODE = kWaveOut, int WGW = kWaveGroupWaves>
+__global__ void __launch_bounds__(64 * WGW, 1)
     scan_fwd_wave_kernel(const IO* __restrict__ X, const IO* __restrict__ DL,
                          const IO* __restrict__ Bm, const IO* __restrict__ Cm,
                          const IO* __restrict__ Z, IO* __restrict__ Y, const float* __restrict__ Am,
@@ -790,10 +791,11 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
   constexpr int CPL = kWaveChannels * PPR / 64;  // pieces per lane per half (x, delta, z, y, B, C)
   static_assert(CPL * 64 == kWaveChannels * PPR, "every lane owns whole pieces");
   static_assert(kWaveChannels == 16, "B / C pieces cover exactly the 16 padded states");
-  __shared__ __align__(16) float s_du[kWaveGroupWaves][kWaveChannels * kWaveDuStride];
-  __shared__ __align__(16) float s_bc[kWaveGroupWaves][2 * 16 * kWaveRowStride];
-  __shared__ __align__(16) float s_part[kWaveGroupWaves][64 * kWaveRowStride];
-  __shared__ int s_prog[kWaveGroupWaves];
+  static_assert(WGW == kWaveGroupWaves || WGW == 4, "eight wavefronts, or four without pacing");
+  __shared__ __align__(16) float s_du[WGW][kWaveChannels * kWaveDuStride];
+  __shared__ __align__(16) float s_bc[WGW][2 * 16 * kWaveRowStride];
+  __shared__ __align__(16) float s_part[WGW][64 * kWaveRowStride];
+  __shared__ int s_prog[WGW];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -802,9 +804,10 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
   float* const sC = s_bc[w] + 16 * kWaveRowStride;
   float* const part = s_part[w];
   const int c = lane & 15, q = lane >> 4;
-  const int64_t gpb = (p.dim + kWaveGroupChannels - 1) / kWaveGroupChannels;
+  constexpr int kGroupChannels = kWaveChannels * WGW;
+  const int64_t gpb = (p.dim + kGroupChannels - 1) / kGroupChannels;
   const int64_t b = blockIdx.x / gpb;
-  const int64_t d0 = (blockIdx.x % gpb) * kWaveGroupChannels + w * kWaveChannels;
+  const int64_t d0 = (blockIdx.x % gpb) * kGroupChannels + w * kWaveChannels;
   if (lane == 0) s_prog[w] = 0;
   __syncthreads();
   if (d0 >= p.dim) return;  // a wavefront past the last channel (its partner keeps going)
@@ -1136,6 +1139,7 @@ __global__ void __launch_bounds__(64 * kWaveGroupWaves, 1)
   // progress of this wavefront in half tiles; the partner on the same SIMD is w ^ 4
   int halves_done = 0;
   auto pace = [&]() __attribute__((always_inline)) {
+    if constexpr (WGW != kWaveGroupWaves) return;  // four wavefronts: one per SIMD, no partner
     ++halves_done;
     *(volatile int*)&s_prog[w] = halves_done;
     const int other = __builtin_amdgcn_readfirstlane(*(volatile int*)&s_prog[w ^ 4]);
@@ -1276,17 +1280,19 @@ hipError_t launch_cfg(const ScanParams& p, hipStream_t stream) {
   const dim3 block(64 * NW);
   const int64_t groups = p.batch * p.groups_per_batch;
   if constexpr (NS == 4 && WaveIo<IO>::value) {
-    if (p.state_split) {
+    if (p.narrow_groups) {
       // the planner's one-pass choice for 64-channel groups too few for the chip's 128-channel
-      // workgroups: eight wavefronts of two states each, two per SIMD of the workgroup's CU
-      // (165 us against 183 us for four of four at batch 8, d_inner 1536, L 2048)
-      const dim3 block8(64 * 8);
+      // workgroups: workgroups of four wavefronts, 64 channels, one wavefront per SIMD (163 us
+      // against 167 us for the barrier-synchronised kernel with eight wavefronts of two states,
+      // per-step medians at batch 8, d_inner 1536, L 2048)
+      const dim3 block4(64 * 4);
+      const unsigned wg4 = (unsigned)(p.batch * ((p.dim + 63) / 64));
       if (p.z)
-        hipLaunchKernelGGL((scan_fwd_kernel<IO, 2, 8, HEAD, false, true, ZOH>),
-                           dim3((unsigned)groups, 1), block8, 0, stream, SCAN_ARGS(p));
+        hipLaunchKernelGGL((scan_fwd_wave_kernel<IO, HEAD, true, ZOH, kWaveOut, 4>),
+                           dim3(wg4, 1), block4, 0, stream, SCAN_ARGS(p));
       else
-        hipLaunchKernelGGL((scan_fwd_kernel<IO, 2, 8, HEAD, false, false, ZOH>),
-                           dim3((unsigned)groups, 1), block8, 0, stream, SCAN_ARGS(p));
+        hipLaunchKernelGGL((scan_fwd_wave_kernel<IO, HEAD, false, ZOH, kWaveOut, 4>),
+                           dim3(wg4, 1), block4, 0, stream, SCAN_ARGS(p));
       return hipGetLastError();
     } else {
       // 8 < N <= 16: the kernel with independent wavefronts. A sequence split into long
@@ -1362,7 +1368,7 @@ hipError_t launch_disc(const ScanParams& p, hipStream_t stream) {
 // States per wavefront for dstate N: N / 4 rounded up to a power of two.
 template <typename IO, bool HEAD>
 hipError_t launch_n(const ScanParams& p, hipStream_t stream) {
-  static_assert(kWavesPerGroup == 4, "the state split below assumes four wavefronts");
+  static_assert(kWavesPerGroup == 4, "the split of the states below assumes four wavefronts");
   const int64_t N = p.N;
   if (N <= 4) return launch_disc<IO, 1, 4, HEAD>(p, stream);
   if (N <= 8) return launch_disc<IO, 2, 4, HEAD>(p, stream);

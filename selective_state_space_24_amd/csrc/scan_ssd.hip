@@ -354,7 +354,7 @@ __global__ void __launch_bounds__(kThreads, 1)
     float v[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      v[q] = (j0 + q <= t) ? acc[q] * __builtin_amdgcn_exp2f(st - sj[q]) * wj[q] : 0.0f;
+      v[q] = (jt < tt || j0 + q <= t) ? acc[q] * __builtin_amdgcn_exp2f(st - sj[q]) * wj[q] : 0.0f;
     const u32x2 s01 = split2(v[0], v[1]), s23 = split2(v[2], v[3]);
     const int o = off_lm(t, 2 * jt + (g >> 1)) + 8 * (g & 1);
     sts8(lm, o, u32x2{s01[0], s23[0]});

@@ -3,7 +3,7 @@
 
 Several kernels depend on the compiler keeping their working set in registers: the
 independent-wavefront forward kernel (the Mamba-1.4B layer), its split modes (the million-token
-config), the state-split kernel (the Mamba-130M layer), the chunked MFMA kernel,
+config), its four-wavefront workgroups (the Mamba-130M layer), the chunked MFMA kernel,
 the decode kernels. A compiler or source change that makes them spill shows up here as scratch
 use, before any timing does. Kernels with a known, small spill are held to it.
 
@@ -75,18 +75,19 @@ def _one(kernels, fragment):
 
 # (mangled-name fragment, what it is, largest spill allowed in VGPRs, largest LDS in bytes)
 HOT = [
-    ("scan_fwd_wave_kernelItLb0ELb1ELb0ELi0E",
+    ("scan_fwd_wave_kernelItLb0ELb1ELb0ELi0ELi8E",
      "independent-wavefront forward, bf16, gate (Mamba-1.4B layer)", 0, 160 * 1024),
-    ("scan_fwd_wave_kernelItLb0ELb0ELb0ELi1E",
+    ("scan_fwd_wave_kernelItLb0ELb0ELb0ELi1ELi8E",
      "its segment-summary mode (splits into shorter segments)", 0, 160 * 1024),
-    ("scan_fwd_wave_kernelItLb0ELb1ELb0ELi3E",
+    ("scan_fwd_wave_kernelItLb0ELb1ELb0ELi3ELi8E",
      "its zero-start output pass of a split, gate (million-token config)", 0, 160 * 1024),
-    ("scan_fwd_wave_kernelItLb0ELb1ELb0ELi4E",
+    ("scan_fwd_wave_kernelItLb0ELb1ELb0ELi4ELi8E",
      "its correcting pass of a split, gate (million-token config)", 0, 160 * 1024),
-    ("scan_fwd_wave_kernelItLb0ELb0ELb0ELi2E",
+    ("scan_fwd_wave_kernelItLb0ELb0ELb0ELi2ELi8E",
      "its checkpoint mode (backward of the Mamba-1.4B layer)", 11, 160 * 1024),
-    ("scan_fwd_kernelItLi2ELi8ELb0ELb0ELb1ELb0ELb0E",
-     "state-split forward, eight wavefronts of two states (Mamba-130M layer)", 0, 160 * 1024),
+    ("scan_fwd_wave_kernelItLb0ELb1ELb0ELi0ELi4E",
+     "independent-wavefront forward in four-wavefront workgroups, gate (Mamba-130M layer)", 0,
+     160 * 1024),
     ("ssd_fwd_kernelILi128ELb1E", "chunked MFMA form, N 128, gate (scalar-decay heads)", 0,
      160 * 1024),
     ("decode_vec_kernelItLi16ELb0ELb1E", "decode step, bf16, N 16, gate", 0, 0),
@@ -109,7 +110,7 @@ def test_hot_kernel_registers(kernels, frag, what, max_spill, max_lds):
 
 
 def test_lds_budgets_allow_the_planned_occupancy(kernels):
-    """The occupancy the kernels are designed for: two state-split / backward workgroups per CU
+    """The occupancy the kernels are designed for: two backward workgroups per CU
     would need at most 80 KB each; the kernels that run one per CU fit 160 KB."""
     assert _one(kernels, "bwd_kernelItLi4ELb1E")["lds"] <= 80 * 1024  # two per CU
     for frag, *_ in HOT:
