@@ -69,7 +69,11 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
   __shared__ __align__(16) float s_B[kBT * NP];  // step-major: a wavefront's NS states of a step
   __shared__ __align__(16) float s_C[kBT * NP];  // are one aligned vector
   __shared__ __align__(16) float s_red[3 * NW * kChannelsPerGroup * kRedStride];
-  __shared__ __align__(16) float s_dbc[2 * NP * kBT];  // the tile's dC, dB partials, (tensor, n, t)
+  // the tile's dC, dB partials, (tensor, n, t): rows of kDbcRow floats, the dB rows 16 floats
+  // further on, so that the eight sums a wavefront stores per step (four states of each tensor)
+  // fall in eight different LDS banks
+  constexpr int kDbcRow = kBT + 4, kDbcTensor = NP * kDbcRow + 16;
+  __shared__ __align__(16) float s_dbc[2 * kDbcTensor];
 
   const ScanParams& p = q.f;
   const int tid = threadIdx.x;
@@ -96,8 +100,10 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
 #pragma unroll
   for (int j = 0; j < NS; ++j) ap[j] = ((live && n0 + j < p.N) ? p.A[d * p.N + n0 + j] : 0.0f) * kLog2e;
 
-  // the epilogue's item: channel er, steps [2 * eq, 2 * eq + 2) of each sub-tile
-  const int er = tid >> 2, eq = tid & 3;
+  // the epilogue's item: channel er (the lane), steps [2 * eq, 2 * eq + 2) of each sub-tile (eq
+  // the wavefront), so that a wavefront's reads of the per-channel partials and of the step
+  // slots run along the channels, whose LDS rows are padded to different banks
+  const int er = tid & 63, eq = tid >> 6;
   const int64_t ed = d0 + er;
   const bool elive = ed < p.dim;
   const float eD = (elive && p.D) ? p.D[ed] : 0.0f;
@@ -265,7 +271,7 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
     }
     if (tid < PIECES) {
       const int tensor = tid / (NP * kBT / 4), n = (tid / (kBT / 4)) % NP, tq = (tid % (kBT / 4)) * 4;
-      out_part = *reinterpret_cast<const f32x4*>(s_dbc + (tensor * NP + n) * kBT + tq);
+      out_part = *reinterpret_cast<const f32x4*>(s_dbc + tensor * kDbcTensor + n * kDbcRow + tq);
     }
   };
   auto put_outputs = [&](int64_t tile) __attribute__((always_inline)) {
@@ -384,7 +390,7 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
         const float tot = lane_sums<M>(dbc);
         if ((lane & (G - 1)) == 0) {
           const int v = lane / G;
-          s_dbc[((v / NS) * NP + n0 + v % NS) * kBT + t] = tot;
+          s_dbc[(v / NS) * kDbcTensor + (n0 + v % NS) * kDbcRow + t] = tot;
         }
       }
       __syncthreads();
@@ -436,13 +442,15 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
       if (q.dh0) q.dh0[(b * p.dim + d) * p.N + n0 + j] = gh[j];
     }
   }
-  dD_acc += __shfl_xor(dD_acc, 1);
-  dD_acc += __shfl_xor(dD_acc, 2);
-  dbias_acc += __shfl_xor(dbias_acc, 1);
-  dbias_acc += __shfl_xor(dbias_acc, 2);
+  // the channel's four step groups, one per wavefront, added as (0 + 1) + (2 + 3)
+  __syncthreads();  // every wavefront is past its last reads of s_red
+  s_red[eq * 64 + er] = dD_acc;
+  s_red[(4 + eq) * 64 + er] = dbias_acc;
+  __syncthreads();
   if (elive && eq == 0) {
-    q.dD_part[b * p.dim + ed] = dD_acc;
-    q.dbias_part[b * p.dim + ed] = dbias_acc;
+    q.dD_part[b * p.dim + ed] = (s_red[er] + s_red[64 + er]) + (s_red[128 + er] + s_red[192 + er]);
+    q.dbias_part[b * p.dim + ed] =
+        (s_red[256 + er] + s_red[320 + er]) + (s_red[384 + er] + s_red[448 + er]);
   }
 }
 
