@@ -31,7 +31,14 @@ constexpr int kBT = kTB;            // steps per backward tile (one load of the 
 constexpr int kSub = 8;             // steps per sub-tile (their states are held in registers)
 constexpr int kSubs = kBT / kSub;   // sub-tiles per tile
 static_assert(kSub == kCkptStep, "every sub-tile starts at a checkpoint");
-constexpr int kInStride = kBT + 1;  // entries per channel row of the per-step LDS arrays
+// The per-step LDS entries of a channel row: step t sits at in_col(t) = t + 2 (t / 8), two spare
+// entries after every 8 steps, in rows of an odd kInStride entries. A wavefront that reads one
+// step of 64 rows (lane = row) then hits 8 different 16-byte bank groups in every 8 lanes, and so
+// does one that writes 16-byte chunks of 16 rows, four lanes to a row (a chunk of 8 steps starts
+// 10 entries after the one before it).
+constexpr int kInStride = kBT + 7;
+static_assert(kInStride % 2 == 1 && kInStride >= kBT + 2 * (kBT / 8 - 1), "row layout");
+__device__ __forceinline__ constexpr int in_col(int t) { return t + 2 * (t >> 3); }
 constexpr int kRedStride = kSub + 1;
 
 // NS consecutive floats of LDS at p (aligned to NS floats) as one read
@@ -216,7 +223,7 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
             gy = gv[e] * zz * sg;
           }
         }
-        s_in[r * kInStride + tl + e] = f32x4{dl, gzf, gy, xx};
+        s_in[r * kInStride + in_col(tl + e)] = f32x4{dl, gzf, gy, xx};
       }
     }
 #pragma unroll
@@ -260,7 +267,7 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
       float vx[V], vd[V], vz[V];
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        const f32x4 o = s_in[r * kInStride + tl + e];
+        const f32x4 o = s_in[r * kInStride + in_col(tl + e)];
         vx[e] = o.x;
         vd[e] = o.y;
         vz[e] = o.z;
@@ -341,7 +348,7 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
       float hh[kSub][NS], dAk[kSub][NS];
 #pragma unroll
       for (int i = 0; i < kSub; ++i) {
-        const f32x4 in = s_in[lane * kInStride + tb + i];
+        const f32x4 in = s_in[lane * kInStride + in_col(tb + i)];
         const float u = in.x * in.w;
         float Bv[NS], Cv[NS];
         lds_states<NS>(s_B + (tb + i) * NP + n0, Bv);
@@ -360,7 +367,7 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
 #pragma unroll
       for (int i = kSub - 1; i >= 0; --i) {
         const int t = tb + i;
-        const f32x4 in = s_in[lane * kInStride + t];
+        const f32x4 in = s_in[lane * kInStride + in_col(t)];
         const float dl = in.x, gy = in.z, xx = in.w;
         const float u = dl * xx;
         // ddelta and dx need sum_j gh_j (h_prev,j dA_j a_j + B_j x) and sum_j gh_j delta B_j:
@@ -409,7 +416,7 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
             gds += pr[(ww * 3 + 1) * kChannelsPerGroup * kRedStride];
             gxsum += pr[(ww * 3 + 2) * kChannelsPerGroup * kRedStride];
           }
-          const f32x4 in = s_in[er * kInStride + t];
+          const f32x4 in = s_in[er * kInStride + in_col(t)];
           const float y = fmaf(eD, in.w, ys);
           const float vz = in.y * y;
           const float vx = fmaf(in.z, eD, gxsum);
@@ -420,7 +427,7 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
           if (t < lt_len) dbias_acc += vd;
           // the step's inputs are dead now (this thread read them last): the slot holds the
           // outputs until the tile is written out
-          s_in[er * kInStride + t] = f32x4{vx, vd, vz, 0.0f};
+          s_in[er * kInStride + in_col(t)] = f32x4{vx, vd, vz, 0.0f};
         }
       }
       __syncthreads();  // s_red is reused by the next sub-tile
