@@ -73,8 +73,12 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
   static_assert(ITEMS % NT == 0, "prologue items must divide evenly");
 
   __shared__ __align__(16) f32x4 s_in[kChannelsPerGroup * kInStride];  // delta, gz, gy, x
-  __shared__ __align__(16) float s_B[kBT * NP];  // step-major: a wavefront's NS states of a step
-  __shared__ __align__(16) float s_C[kBT * NP];  // are one aligned vector
+  // B and C step-major: a wavefront's NS states of a step are one aligned vector. Steps are
+  // kBCRow floats apart, an odd multiple of 4, so that the fill's stores along the steps of a
+  // state spread over 8 bank groups
+  constexpr int kBCRow = NP % 8 == 0 ? NP + 4 : NP;
+  __shared__ __align__(16) float s_B[kBT * kBCRow];
+  __shared__ __align__(16) float s_C[kBT * kBCRow];
   __shared__ __align__(16) float s_red[3 * NW * kChannelsPerGroup * kRedStride];
   // the tile's dC, dB partials, (tensor, n, t): rows of kDbcRow floats, the dB rows 16 floats
   // further on, so that the eight sums a wavefront stores per step (four states of each tensor)
@@ -230,8 +234,8 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
     for (int k = 0; k < BCI; ++k) {
       const int i = tid + k * NT;
       if (i < NP * kBT) {
-        s_B[(i % kBT) * NP + i / kBT] = to_f32(rb[k]);
-        s_C[(i % kBT) * NP + i / kBT] = to_f32(rc[k]);
+        s_B[(i % kBT) * kBCRow + i / kBT] = to_f32(rb[k]);
+        s_C[(i % kBT) * kBCRow + i / kBT] = to_f32(rc[k]);
       }
     }
   };
@@ -351,8 +355,8 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
         const f32x4 in = s_in[lane * kInStride + in_col(tb + i)];
         const float u = in.x * in.w;
         float Bv[NS], Cv[NS];
-        lds_states<NS>(s_B + (tb + i) * NP + n0, Bv);
-        lds_states<NS>(s_C + (tb + i) * NP + n0, Cv);
+        lds_states<NS>(s_B + (tb + i) * kBCRow + n0, Bv);
+        lds_states<NS>(s_C + (tb + i) * kBCRow + n0, Cv);
         float acc = 0.0f;
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
@@ -376,8 +380,8 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdParams q) {
         float gd = 0.0f, sb = 0.0f;
         float dbc[M];  // this lane's (channel's) terms of dC_j, dB_j at step t
         float Bv[NS], Cv[NS];
-        lds_states<NS>(s_B + t * NP + n0, Bv);
-        lds_states<NS>(s_C + t * NP + n0, Cv);
+        lds_states<NS>(s_B + t * kBCRow + n0, Bv);
+        lds_states<NS>(s_C + t * kBCRow + n0, Cv);
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
           gh[j] = fmaf(gy, Cv[j], gh[j]);

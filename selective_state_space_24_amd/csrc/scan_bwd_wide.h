@@ -73,15 +73,18 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_wide_kernel(const BwdParams q)
   __shared__ float s_gz[GATE ? kChannelsPerGroup * kInS : 1];     // dy silu'(z)
   // B and C step-major: a wavefront's NS states of one step are NS consecutive floats, read as
   // NS / 4 16-byte words at one (wave-uniform) address each
-  __shared__ __align__(16) float s_B[kT * NP];
-  __shared__ __align__(16) float s_C[kT * NP];
+  // (steps kBCRow floats apart, an odd multiple of 4: the fill's stores along the steps of a
+  // state spread over 8 bank groups)
+  constexpr int kBCRow = NP % 8 == 0 ? NP + 4 : NP;
+  __shared__ __align__(16) float s_B[kT * kBCRow];
+  __shared__ __align__(16) float s_C[kT * kBCRow];
   __shared__ float s_red[3 * NW * kChannelsPerGroup * RED];        // per-channel partial sums
   __shared__ __align__(16) float s_sum[NW * NV * kSumS];           // dB / dC lane sums
   // the tile's dC, dB partials (tensor, state, step), written out whole when the tile is done;
   // where that buffer would take the workgroup past 80 KB of LDS (two workgroups per CU with
   // four wavefronts), each step's sums are stored as they are made instead
   constexpr int kLdsRest = (int)(kChannelsPerGroup * kInS * sizeof(f32x4)) +
-                           (GATE ? kChannelsPerGroup * kInS * 4 : 4) + 2 * NP * kT * 4 +
+                           (GATE ? kChannelsPerGroup * kInS * 4 : 4) + 2 * kBCRow * kT * 4 +
                            3 * NW * kChannelsPerGroup * RED * 4 + NW * NV * kSumS * 4;
   constexpr bool kStageDbc = NW == 8 || kLdsRest + 2 * NP * kDbcS * 4 <= 80 * 1024;
   __shared__ float s_dbc[kStageDbc ? 2 * NP * kDbcS : 1];
@@ -179,8 +182,8 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_wide_kernel(const BwdParams q)
     for (int i = tid; i < NP * kT; i += NT) {
       const int n = i / kT, t = i % kT;
       const bool on = n < p.N && t < len;
-      s_B[t * NP + n] = on ? to_f32(Bg[n * p.B_sn + t0 + t]) : 0.0f;
-      s_C[t * NP + n] = on ? to_f32(Cg[n * p.C_sn + t0 + t]) : 0.0f;
+      s_B[t * kBCRow + n] = on ? to_f32(Bg[n * p.B_sn + t0 + t]) : 0.0f;
+      s_C[t * kBCRow + n] = on ? to_f32(Cg[n * p.C_sn + t0 + t]) : 0.0f;
     }
     __syncthreads();
 
@@ -195,7 +198,7 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_wide_kernel(const BwdParams q)
 
       // the wavefront's NS values of B or C at tile step t
       auto states_at = [&](const float* s, int t, float (&v)[NS]) __attribute__((always_inline)) {
-        const f32x4* src = reinterpret_cast<const f32x4*>(s + t * NP + n0);
+        const f32x4* src = reinterpret_cast<const f32x4*>(s + t * kBCRow + n0);
 #pragma unroll
         for (int k = 0; k < NS / 4; ++k) {
           const f32x4 w4 = src[k];
