@@ -285,6 +285,15 @@ int ssm_selective_scan_fwd_noalloc(const ssm_scan_desc* desc, const void* x, con
 /* SSM_SCAN_ABI_VERSION of the built library. */
 int ssm_abi_version(void);
 
+/* Diagnostic of a hardware assumption, no part of the scan: launches `nworkgroups` workgroups of
+ * eight wavefronts, the shape of the forward kernel with independent wavefronts, and writes to
+ * out[8 g + w] (device memory of 8 * nworkgroups int32, caller-owned) the SIMD (0..3 of its
+ * compute unit) that wavefront w of workgroup g ran on. That kernel paces wavefronts w and w ^ 4
+ * of a workgroup against each other on the assumption that they share a SIMD; a test checks it.
+ * Returns SSM_ERR_NULL_ARG for a null `out` and SSM_ERR_BAD_SHAPE for a negative count (nothing
+ * is launched), else SSM_OK or SSM_ERR_HIP (launch failure). Runs asynchronously on `stream`. */
+int ssm_wave_simd_ids(int32_t* out, int32_t nworkgroups, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -104,6 +104,8 @@ def lib():
         h.ssm_status_string.argtypes = [ctypes.c_int]
         h.ssm_status_string.restype = ctypes.c_char_p
         h.ssm_abi_version.argtypes = []
+        h.ssm_wave_simd_ids.restype = ctypes.c_int
+        h.ssm_wave_simd_ids.argtypes = [vp, i32, vp]
         h.ssm_abi_version.restype = ctypes.c_int
         _lib = h
     return _lib
@@ -111,6 +113,12 @@ def lib():
 
 def status_string(status: int) -> str:
     return lib().ssm_status_string(int(status)).decode()
+
+
+def wave_simd_ids_raw(out, nworkgroups: int, stream) -> int:
+    """ssm_wave_simd_ids: the SIMD of each wavefront of `nworkgroups` 8-wavefront workgroups into
+    the device int32 buffer at address `out` (8 per workgroup); returns the status."""
+    return int(lib().ssm_wave_simd_ids(out, int(nworkgroups), stream))
 
 
 def abi_version() -> int:

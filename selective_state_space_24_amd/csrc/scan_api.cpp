@@ -302,6 +302,13 @@ extern "C" {
 
 int ssm_abi_version(void) { return SSM_SCAN_ABI_VERSION; }
 
+int ssm_wave_simd_ids(int32_t* out, int32_t nworkgroups, void* stream) {
+  if (!out) return SSM_ERR_NULL_ARG;
+  if (nworkgroups < 0) return SSM_ERR_BAD_SHAPE;
+  const hipError_t e = ssm::launch_wave_simd(out, nworkgroups, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 const char* ssm_status_string(int status) {
   switch (status) {
     case SSM_OK: return "ok";

@@ -141,6 +141,7 @@ hipError_t launch_ssd(const ScanParams& p, hipStream_t stream);
 
 // dst[0, n) = src[0, n), or zeros when src is null
 hipError_t launch_state_copy(const float* src, float* dst, int64_t n, hipStream_t stream);
+hipError_t launch_wave_simd(int32_t* out, int32_t nworkgroups, hipStream_t stream);
 // The forward scan with a complex diagonal A (a_mode SSM_A_COMPLEX): A as (dim, N, 2) fp32
 // pairs, B and C with 2N rows per group (real parts, then imaginary), N <= 32, delta * B rule,
 // no initial or final state (checked by the caller).
