@@ -284,7 +284,8 @@ def run_bwd(args, torch, heads=False):
         "value": round(cfg.tokch / (ms * 1e-3) / 1e9, 3),
         "unit": "Gtoken\u00b7channel/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": f"f32 arithmetic and state, {cfg.io} io", "data": "synthetic",
         "config": {"workload": ("scalar-decay heads selective scan backward (all input "
                                 "gradients; one A per head, 64 heads x 64)" if heads else
                                 "Mamba-1.4B layer selective scan backward (all input gradients)"),
@@ -392,7 +393,8 @@ def run_heads(args, torch):
         "unit": "Gtoken\u00b7channel/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16 matrix products, fp32 accumulation and state" if chunked else "f32",
+        "dtype": ("bf16 matrix products, fp32 accumulation and state, bf16 io" if chunked
+                  else f"f32 arithmetic and state, {cfg.io} io"),
         "data": "synthetic",
         "config": {"workload": "scalar-decay heads selective scan (one A per head, B/C shared "
                                "by all heads)" + (", chunked matrix form" if chunked else
@@ -456,8 +458,8 @@ def run_decode(args, torch):
         "value": round(cfg.batch / (ms * 1e-3), 1),
         "unit": "tokens/s (one token per sequence per step, one layer)",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-        "data": "synthetic",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": f"f32 arithmetic and state, {cfg.io} io", "data": "synthetic",
         "config": {"workload": "Mamba-1.4B layer decode step", "batch": cfg.batch,
                    "d_inner": cfg.dim, "d_state": cfg.N, "io_dtype": cfg.io,
                    "state": "fp32, updated in place", "gate": "silu(z)"},
